@@ -1,0 +1,104 @@
+"""CPU fp64 oracle for paged grouped-query attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never imports,
+links or calls it, and it shares no code with the HIP kernels: the C source
+next to this file is compiled by ``gcc`` on its own.
+
+``paged_attn`` is masked softmax attention written out as its definition
+(see the header of ``paged_attn_oracle.c`` for the formula and the pages it
+follows).  ``quant_attn`` (in ``quant.py``) emulates the int8 QK / fp8 PV
+quantised variant step by step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRCS = [os.path.join(_HERE, "paged_attn_oracle.c"), os.path.join(_HERE, "quant_oracle.c")]
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP)."""
+    srcs = [s for s in _SRCS if os.path.exists(s)]
+    stale = force or not os.path.exists(_LIB_PATH) or any(
+        os.path.getmtime(s) > os.path.getmtime(_LIB_PATH) for s in srcs)
+    if stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", tmp] + srcs + ["-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        p, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_paged_attn.restype = ctypes.c_int
+        lib.oracle_paged_attn.argtypes = [
+            p, p, p, i64, i64, p, i64, i64, i64, i64, p, i64, p, p,
+            i32, i32, i32, i32, i32, f64, i32, p, i64, i32]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        if hasattr(lib, "oracle_quant_attn"):
+            lib.oracle_quant_attn.restype = ctypes.c_int
+            lib.oracle_quant_attn.argtypes = [
+                p, p, p, p, i32, i32, i32, i32, f64, i32, i32, p, i32]
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bool,
+               row_mask=None, chunk_keys: int = 0, nthreads: int = 0, return_lse: bool = False):
+    """fp64 masked softmax attention over a paged KV cache.
+
+    q         : bf16 [T, Hq, D] CPU tensor (D contiguous, other strides free)
+    kv_pool   : bf16 [NP, P, Hkv, 2, D] CPU tensor view (index 3: 0 = K, 1 = V)
+    block_table, seq_lens, cu_q : int32 CPU tensors
+    Returns fp64 numpy [T, Hq, D] (rows not covered by cu_q are zero), and
+    the natural-log lse [T, Hq] when ``return_lse``.
+    """
+    lib = _load()
+    assert q.dtype == torch.bfloat16 and kv_pool.dtype == torch.bfloat16
+    assert q.device.type == "cpu" and kv_pool.device.type == "cpu"
+    assert q.dim() == 3 and q.stride(2) == 1
+    assert kv_pool.dim() == 5 and kv_pool.stride(4) == 1 and kv_pool.shape[3] == 2
+    T, hq, d = q.shape
+    _, P, hkv, _, d2 = kv_pool.shape
+    assert d2 == d
+    bt = block_table.to(torch.int32).contiguous()
+    sl = seq_lens.to(torch.int32).contiguous()
+    cq = cu_q.to(torch.int32).contiguous()
+    n_seqs = sl.numel()
+    out = np.zeros((T, hq, d), dtype=np.float64)
+    lse = np.full((T, hq), -np.inf, dtype=np.float64)
+    rm = None
+    if row_mask is not None:
+        rm = np.ascontiguousarray(np.asarray(row_mask, dtype=np.uint8))
+        assert rm.shape == (T,)
+    st = kv_pool.stride()
+    rc = lib.oracle_paged_attn(
+        out.ctypes.data, lse.ctypes.data, _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv_pool), st[0], st[1], st[2], st[3], _ptr(bt), bt.stride(0), _ptr(sl), _ptr(cq),
+        n_seqs, hq, hkv, d, P, float(scale), int(bool(causal)),
+        rm.ctypes.data if rm is not None else None, int(chunk_keys), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_paged_attn failed with status %d" % rc)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,215 @@
+/*
+ * Oracle for paged grouped-query attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 CPU reference of what the GPU path computes.  Only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * this library; the product path never links, imports or calls it.  It shares
+ * no code, header, table or helper with the HIP kernels.
+ *
+ * Sources (web pages, cited by title and section):
+ *  - kern-kernels examples/decode.json (TRT-LLM-gen decode manifest):
+ *      buffers q / out / kv / table / seq / cuq give the paged layout
+ *      [pages, layer, slot, kv_head, {K,V}, head_dim]; programs.decode passes
+ *      K and V as two byte offsets into the same kv buffer.
+ *  - Mojo SM100MHA2Q API docs: "scaled dot-product attention over a KV cache",
+ *      MaskType "causal or unmasked", group / fuse_gqa (several q heads share
+ *      one KV head), ValidLengthType (ragged lengths), PartitionType (split-K).
+ *  - metrale blueprint graph.json, node l3.attn.attend: paged decode
+ *      attention with f32 scores, softmax and accumulation; node
+ *      l3.attn.kv_write runs first, so the cache already holds the step's
+ *      own tokens.
+ *
+ * What is computed (masked softmax attention, written out as its definition):
+ *   for each sequence b, query token i (row t = cu_q[b] + i), q head h:
+ *     n = cu_q[b+1] - cu_q[b], L = seq_lens[b], pos = L - n + i
+ *     visible keys j in [0, vis), vis = causal ? clamp(pos + 1, 0, L) : L
+ *     g = h / G (contiguous groups of G = Hq / Hkv q heads per KV head)
+ *     K_j, V_j = pool rows of page block_table[b][j / P], slot j % P, head g
+ *     s_j = scale * <q_t,h , K_j>
+ *     out[t, h, :] = sum_j softmax(s)_j V_j,   lse = log sum_j exp(s_j)
+ *   Rows with no visible key give out = 0 and lse = -inf.
+ * Every bf16 input is widened exactly to fp64; nothing is rounded on output.
+ *
+ * Readings taken where the pages are silent (each one is listed in the
+ * design notes): seq_lens counts the step's own tokens; causal alignment is
+ * bottom-right (queries sit at the tail of the sequence); q head h uses KV
+ * head h / G.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_bits_to_f64(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    const uint16_t *q;
+    int64_t q_stride_token, q_stride_head;
+    const uint16_t *pool;
+    int64_t s_page, s_slot, s_head, s_kv;
+    const int32_t *block_table;
+    int64_t bt_stride;
+    int hq, hkv, d, page_size;
+    double scale;
+} oracle_ctx;
+
+/* Address of element 0 of key/value row j of sequence b, KV head g. */
+static const uint16_t *kv_row(const oracle_ctx *c, int b, int64_t j, int g, int which)
+{
+    int64_t page = c->block_table[(int64_t)b * c->bt_stride + j / c->page_size];
+    int64_t slot = j % c->page_size;
+    return c->pool + page * c->s_page + slot * c->s_slot + (int64_t)g * c->s_head
+           + (int64_t)which * c->s_kv;
+}
+
+/*
+ * Attention of one (query token t of sequence b, q head h) over keys [j0, j1).
+ * Returns the partial triple (m, l, o[]) with o unnormalised:
+ *   m = max_j s_j, l = sum_j exp(s_j - m), o = sum_j exp(s_j - m) V_j.
+ * An empty range gives m = -inf, l = 0, o = 0.
+ */
+static void attend_range(const oracle_ctx *c, int b, int64_t t, int h, int64_t j0, int64_t j1,
+                         double *scores, double *m_out, double *l_out, double *o)
+{
+    const int d = c->d;
+    const int g = h / (c->hq / c->hkv);
+    const uint16_t *qrow = c->q + t * c->q_stride_token + (int64_t)h * c->q_stride_head;
+    for (int e = 0; e < d; ++e) o[e] = 0.0;
+    if (j1 <= j0) {
+        *m_out = -INFINITY;
+        *l_out = 0.0;
+        return;
+    }
+    double m = -INFINITY;
+    for (int64_t j = j0; j < j1; ++j) {
+        const uint16_t *k = kv_row(c, b, j, g, 0);
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += bf16_bits_to_f64(qrow[e]) * bf16_bits_to_f64(k[e]);
+        double s = c->scale * dot;
+        scores[j - j0] = s;
+        if (s > m) m = s;
+    }
+    double l = 0.0;
+    for (int64_t j = j0; j < j1; ++j) {
+        double w = exp(scores[j - j0] - m);
+        l += w;
+        const uint16_t *v = kv_row(c, b, j, g, 1);
+        for (int e = 0; e < d; ++e) o[e] += w * bf16_bits_to_f64(v[e]);
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+/* Number of keys visible to query i of a sequence with n queries and L keys. */
+static int64_t visible_keys(int64_t L, int64_t n, int64_t i, int causal)
+{
+    if (!causal) return L;
+    int64_t vis = L - n + i + 1;
+    if (vis < 0) vis = 0;
+    if (vis > L) vis = L;
+    return vis;
+}
+
+/*
+ * out  : fp64 [num_tokens, hq, d] (rows outside [0, cu_q[n_seqs]) untouched)
+ * lse  : fp64 [num_tokens, hq] natural-log log-sum-exp, or NULL
+ * row_mask : optional uint8 [num_tokens]; when given only rows with a nonzero
+ *            entry are computed (sampled checks at large sizes)
+ * n_chunks : 0 = single pass; otherwise the visible key range of every row is
+ *            cut into chunks at the boundaries given by chunk_keys (keys per
+ *            chunk, > 0) and the partial triples are merged by the
+ *            log-sum-exp rule -- the split-KV reading, used for the
+ *            "split + combine equals one pass" invariant.
+ */
+int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_stride_token,
+                      int64_t q_stride_head, const uint16_t *pool, int64_t s_page, int64_t s_slot,
+                      int64_t s_head, int64_t s_kv, const int32_t *block_table, int64_t bt_stride,
+                      const int32_t *seq_lens, const int32_t *cu_q, int n_seqs, int hq, int hkv,
+                      int d, int page_size, double scale, int causal, const uint8_t *row_mask,
+                      int64_t chunk_keys, int nthreads)
+{
+    if (hkv <= 0 || hq % hkv != 0 || d <= 0 || page_size <= 0 || n_seqs < 0) return -1;
+    oracle_ctx c = {q, q_stride_token, q_stride_head, pool, s_page, s_slot, s_head, s_kv,
+                    block_table, bt_stride, hq, hkv, d, page_size, scale};
+    int64_t max_l = 0;
+    for (int b = 0; b < n_seqs; ++b)
+        if (seq_lens[b] > max_l) max_l = seq_lens[b];
+    const int64_t total = cu_q[n_seqs];
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int status = 0;
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)(max_l > 0 ? max_l : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        double *part = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!scores || !acc || !part) {
+#pragma omp atomic write
+            status = -2;
+        } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t t = 0; t < total; ++t) {
+                for (int h = 0; h < hq; ++h) {
+                    if (row_mask && !row_mask[t]) continue;
+                    int b = 0;
+                    while (b + 1 <= n_seqs && cu_q[b + 1] <= t) ++b;
+                    const int64_t n = cu_q[b + 1] - cu_q[b];
+                    const int64_t i = t - cu_q[b];
+                    const int64_t L = seq_lens[b];
+                    const int64_t vis = visible_keys(L, n, i, causal);
+                    double *dst = out + (t * hq + h) * (int64_t)d;
+                    double m = -INFINITY, l = 0.0;
+                    if (chunk_keys <= 0) {
+                        attend_range(&c, b, t, h, 0, vis, scores, &m, &l, acc);
+                    } else {
+                        /* merge partial triples chunk by chunk (log-sum-exp rule) */
+                        for (int e = 0; e < d; ++e) acc[e] = 0.0;
+                        for (int64_t j0 = 0; j0 < vis; j0 += chunk_keys) {
+                            int64_t j1 = j0 + chunk_keys < vis ? j0 + chunk_keys : vis;
+                            double ms, ls;
+                            attend_range(&c, b, t, h, j0, j1, scores, &ms, &ls, part);
+                            double mn = ms > m ? ms : m;
+                            double a_old = (m == -INFINITY) ? 0.0 : exp(m - mn);
+                            double a_new = (ms == -INFINITY) ? 0.0 : exp(ms - mn);
+                            l = l * a_old + ls * a_new;
+                            for (int e = 0; e < d; ++e) acc[e] = acc[e] * a_old + part[e] * a_new;
+                            m = mn;
+                        }
+                    }
+                    if (l > 0.0) {
+                        for (int e = 0; e < d; ++e) dst[e] = acc[e] / l;
+                        if (lse) lse[t * hq + h] = m + log(l);
+                    } else {
+                        for (int e = 0; e < d; ++e) dst[e] = 0.0;
+                        if (lse) lse[t * hq + h] = -INFINITY;
+                    }
+                }
+            }
+        }
+        free(scores);
+        free(acc);
+        free(part);
+    }
+    return status;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
