@@ -1,0 +1,250 @@
+"""Benchmark of the paged GQA attention hot path on one MI355X.
+
+One "step" is one full forward pass (all kernels of the path: split-KV decode
+partials + log-sum-exp combine, or the prefill kernel) over one batch of
+synthetic, seeded input already resident in HBM.
+
+Default workload: the decode batch (64 sequences x 1 query token, 32 q / 8 KV
+heads, head_dim 128, page 64, KV lengths uniform in [1024, 8192], causal),
+reported as achieved HBM GB/s of algorithmic bytes (K and V read once per KV
+head, plus Q and the output).  Secondary lines (long-context decode, chunked
+prefill, DiT non-causal) are reported alongside, prefill ones in TFLOP/s of
+algorithmic FLOPs (4 * D per visible (query, q head, key) triple).
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+METRIC = "decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% bf16 MFMA peak)"
+
+DESCR = {
+    "decode_batch": "decode batch: 64 seqs x 1 query token, 32 q / 8 KV heads (GQA 4), head_dim 128, "
+                    "page 64, KV lengths U[1024, 8192], shuffled shared page pool, causal",
+    "long_decode": "long-context decode: 128 seqs x 1 token, 16 q / 2 KV heads (GQA 8), head_dim 256, "
+                   "page 64, context 32768, 1% outlier K rows x4, causal",
+    "chunked_prefill": "chunked prefill: 8 seqs, new tokens U[512, 4096] after cached context U[0, 8192], "
+                       "24 q / 4 KV heads, head_dim 256, page 64, causal",
+    "dit_self_attn": "DiT self-attention: 1 seq x 37810 tokens, 56 heads (MHA), head_dim 128, "
+                     "non-causal, per-channel K offset N(0, 2)",
+    "tiny_mixed": "tiny mixed: 2 seqs x 32 queries, 24 q / 4 KV heads, head_dim 256, 22-page pool, causal",
+}
+BOUND = {"decode_batch": "hbm", "long_decode": "hbm", "chunked_prefill": "mfma",
+         "dit_self_attn": "mfma", "tiny_mixed": "hbm"}
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def visible_pairs(case) -> int:
+    """Sum over (sequence, query) of visible keys."""
+    tot = 0
+    for n, L in zip(case.q_lens, case.kv_lens):
+        if not case.causal:
+            tot += n * L
+        else:
+            for i in range(n):
+                tot += max(0, min(L, L - n + i + 1))
+    return tot
+
+
+def algorithmic_bytes(case) -> int:
+    """K and V of every visible key once per KV head, Q read once, out written once."""
+    d, hq, hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
+    kv = sum(case.kv_lens) * hkv * 2 * d * 2
+    T = sum(case.q_lens)
+    return kv + 2 * T * hq * d * 2
+
+
+def algorithmic_flops(case) -> int:
+    return 4 * case.head_dim * case.num_q_heads * visible_pairs(case)
+
+
+def run_workload(name, steps, warmup, pps=0, path=0):
+    import paged_kv_gqa_fwd_amd as pa
+    log("[bench] generating %s" % name)
+    case = workloads.WORKLOADS[name](device="cuda")
+    out = torch.empty_like(case.q)
+    args = (case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, max(case.max_q, 1),
+            case.scale, case.causal)
+    dims = pa.make_dims(case.q, case.kv, case.block_table, out)
+    plan = pa.make_plan(dims, case.n_seqs, max(case.max_q, 1), path, pps)
+    for _ in range(warmup):
+        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
+    torch.cuda.synchronize()
+    pa.kernel_timing_read()                      # discard anything recorded before
+    pa.kernel_timing_enable(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
+    t1.record()
+    torch.cuda.synchronize()
+    pa.kernel_timing_enable(False)
+    step_ms = t0.elapsed_time(t1) / steps
+    main_ms, main_n, comb_ms, comb_n = pa.kernel_timing_read()
+    res = {
+        "workload": name, "case": case, "ms_per_step": step_ms,
+        "main_kernel_ms": main_ms / max(main_n, 1), "combine_kernel_ms": comb_ms / max(comb_n, 1) if comb_n else 0.0,
+        "path": "split_decode+combine" if plan.path == pa.PATH_SPLIT_DECODE else "prefill",
+        "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
+        "bytes": algorithmic_bytes(case), "flops": algorithmic_flops(case),
+    }
+    return res
+
+
+def summarize(res):
+    name = res["workload"]
+    if BOUND[name] == "hbm":
+        val = res["bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+        kern = res["bytes"] / (res["main_kernel_ms"] * 1e-3) / 1e9
+        return {"workload": name, "value": round(val, 2), "unit": "GB/s",
+                "frac_of_peak": round(val / HBM_PEAK_GBS, 4), "ms_per_step": round(res["ms_per_step"], 4),
+                "main_kernel_ms": round(res["main_kernel_ms"], 4),
+                "combine_kernel_ms": round(res["combine_kernel_ms"], 4),
+                "main_kernel_GBps": round(kern, 2), "path": res["path"],
+                "pages_per_split": res["pages_per_split"], "max_splits": res["max_splits"]}
+    val = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
+    return {"workload": name, "value": round(val, 2), "unit": "TFLOP/s",
+            "frac_of_peak": round(val / BF16_PEAK_TFLOPS, 4), "ms_per_step": round(res["ms_per_step"], 4),
+            "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"]}
+
+
+def cpu_baseline(res, max_seconds=20.0):
+    """Time the fp64 CPU oracle on a bounded sample of the primary workload
+    (a prefix of its sequences) and report the same metric's unit."""
+    import oracle
+    from dataclasses import replace
+    case = res["case"]
+    name = res["workload"]
+    nthreads = oracle.num_threads()
+    # grow the sample until it takes a few seconds or covers the batch
+    k = 1
+    t_used = 0.0
+    while True:
+        sub = _prefix_case(case, k)
+        t = time.perf_counter()
+        oracle.paged_attn(sub.q, sub.kv, sub.block_table, sub.seq_lens, sub.cu_q, sub.scale,
+                          sub.causal)
+        t_used = time.perf_counter() - t
+        if t_used * 2 > max_seconds / 2 or k >= case.n_seqs:
+            break
+        k = min(case.n_seqs, k * 2)
+    if BOUND[name] == "hbm":
+        val = algorithmic_bytes(sub) / t_used / 1e9
+        unit = "GB/s"
+    else:
+        val = algorithmic_flops(sub) / t_used / 1e12
+        unit = "TFLOP/s"
+    return {"value": round(val, 4), "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": "first %d of %d sequences of the %s workload (%.2f s of fp64 oracle time, "
+                      "OpenMP threads=%d)" % (k, case.n_seqs, name, t_used, nthreads)}
+
+
+def _prefix_case(case, k):
+    """CPU copy of the first k sequences (pages gathered into a compact pool)."""
+    from dataclasses import replace
+    bt = case.block_table.cpu()
+    P = case.kv.shape[1]
+    pages, rows = [], []
+    for b in range(k):
+        npg = (case.kv_lens[b] + P - 1) // P
+        ids = bt[b, :npg].tolist()
+        rows.append(list(range(len(pages), len(pages) + npg)) + [-1] * (bt.shape[1] - npg))
+        pages.extend(ids)
+    kv = case.kv.index_select(0, torch.tensor(pages, dtype=torch.long, device=case.kv.device)).cpu()
+    T = sum(case.q_lens[:k])
+    return replace(case, q=case.q[:T].cpu(), kv=kv, pool_storage=kv,
+                   block_table=torch.tensor(rows, dtype=torch.int32),
+                   seq_lens=case.seq_lens[:k].cpu(), cu_q=case.cu_q[:k + 1].cpu(),
+                   q_lens=case.q_lens[:k], kv_lens=case.kv_lens[:k])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn",
+                    help="comma list of extra workloads to time ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--path", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.manual_seed(0)
+    prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path)
+    s = summarize(prim)
+    log("[bench] %s" % json.dumps(s))
+    secondary = []
+    for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        r = run_workload(name, max(3, args.steps // 2), max(1, args.warmup // 2))
+        ss = summarize(r)
+        log("[bench] %s" % json.dumps(ss))
+        secondary.append(ss)
+        del r
+        torch.cuda.empty_cache()
+    bound = BOUND[args.workload]
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": s["main_kernel_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(s["main_kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "paged_decode_split_kernel" if "split" in prim["path"] else "paged_prefill_kernel",
+                "kernel_ms": s["main_kernel_ms"]}
+    else:
+        ach = prim["flops"] / (prim["main_kernel_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "paged_prefill_kernel", "kernel_ms": s["main_kernel_ms"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(prim)
+        log("[bench] cpu baseline %s" % json.dumps(cpu))
+    case = prim["case"]
+    line = {
+        "metric": METRIC, "value": s["value"], "unit": s["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(prim["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page pool)",
+        "config": {"workload": DESCR[args.workload], "n_seqs": case.n_seqs,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "page_size": 64, "total_kv_tokens": sum(case.kv_lens),
+                   "algorithmic_bytes": prim["bytes"], "path": prim["path"],
+                   "pages_per_split": prim["pages_per_split"], "max_splits": prim["max_splits"]},
+        "frac_of_peak": s["frac_of_peak"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

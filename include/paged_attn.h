@@ -1,0 +1,181 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged grouped-query attention
+ * library (libpaged_attn.so).
+ *
+ * Operation (defined once, used by every entry point below).  For each
+ * sequence b in [0, n_seqs), with n_b = cu_q[b+1] - cu_q[b] new query tokens
+ * and L_b = seq_lens[b] cached keys, query token i (row t = cu_q[b] + i) of
+ * q head h attends to the keys j in [0, vis) of KV head g = h / G, where
+ * G = num_q_heads / num_kv_heads, pos = L_b - n_b + i and
+ * vis = causal ? clamp(pos + 1, 0, L_b) : L_b:
+ *
+ *     out[t, h, :] = sum_j softmax_j(scale * <q[t, h, :], K_j>) * V_j
+ *
+ * Key j lives in page block_table[b, j / P], slot j % P of the pool.  Rows
+ * with no visible key are written as zeros.
+ *   - Scaled dot-product attention over a paged KV cache, causal or unmasked,
+ *     with ragged lengths and grouped q heads: Mojo SM100MHA2Q API docs
+ *     (struct summary; parameters KVLUTType, MaskType, ValidLengthType,
+ *     PartitionType; comptime members group, fuse_gqa, page_size).
+ *   - Pool, block table, lengths and cumulative query offsets as separate
+ *     device buffers, K and V as offsets into one pool: kern-kernels
+ *     examples/decode.json (buffers; ops.decode.params; programs.decode).
+ *   - The cache already holds the step's own tokens when attention runs:
+ *     metrale blueprint graph.json (node l3.attn.kv_write precedes
+ *     l3.attn.attend), hence queries sit at the tail (bottom-right causal).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  bf16 is IEEE bfloat16 stored in
+ *     16 bits; int32 is little-endian two's complement.
+ *   - Every call validates its arguments on the host before launching
+ *     anything and returns an attn_status code (0 = success, negative =
+ *     error).  A call that fails validation launches nothing and leaves `out`
+ *     untouched.  Errors inside kernels (for example a page id outside
+ *     [0, num_pages)) are not detected; they surface at the caller's next
+ *     synchronisation as a HIP error.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Calls are re-entrant as long as concurrent calls use
+ *     distinct workspaces.
+ *   - Strides are in ELEMENTS; the head_dim axis must be contiguous.  Base
+ *     pointers must be 16-byte aligned and every bf16 stride a multiple of 8.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+    ATTN_ERR_UNSUPPORTED = -3, /* head_dim not in {128, 256}, page_size != 64, ... */
+    ATTN_ERR_STRIDE = -4,      /* bad stride (non-positive, not a multiple of 8, overlapping) */
+    ATTN_ERR_ALIGN = -5,       /* base pointer not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = -6,   /* workspace missing, misaligned or too small */
+    ATTN_ERR_HIP = -7          /* a HIP runtime call failed (launch error) */
+} attn_status;
+
+/* Sizes and element strides of the paged attention operands. */
+typedef struct attn_paged_dims {
+    int32_t num_q_heads;       /* Hq */
+    int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0, G = Hq / Hkv */
+    int32_t head_dim;          /* D: 128 or 256 */
+    int32_t page_size;         /* P: 64 (slots per page) */
+    int32_t num_pages;         /* NP: pages in the pool (valid ids are [0, NP)) */
+    int32_t max_pages_per_seq; /* MP: block-table columns; every L_b <= MP * P */
+    int64_t num_tokens;        /* rows of q and out (>= cu_q[n_seqs]) */
+    int64_t q_stride_token;    /* q[t, h, d] at q + t*q_stride_token + h*q_stride_head + d */
+    int64_t q_stride_head;
+    int64_t o_stride_token;    /* out[t, h, d] likewise */
+    int64_t o_stride_head;
+    int64_t kv_stride_page;    /* K_j of head g: pool + page*kv_stride_page + slot*kv_stride_slot */
+    int64_t kv_stride_slot;    /*                  + g*kv_stride_head;  V_j = that + kv_stride_kv */
+    int64_t kv_stride_head;
+    int64_t kv_stride_kv;
+    int64_t bt_stride;         /* elements between block-table rows (>= MP) */
+} attn_paged_dims;
+
+/* Execution plan chosen for a call (host-side; no device access). */
+typedef struct attn_paged_plan {
+    int32_t path;              /* ATTN_PATH_SPLIT_DECODE or ATTN_PATH_PREFILL */
+    int32_t pages_per_split;   /* KV pages one workgroup streams (split path) */
+    int32_t max_splits;        /* ceil(MP / pages_per_split) */
+    int32_t grid_x, grid_y, grid_z;
+    int32_t block_threads;
+    size_t workspace_bytes;    /* bytes of workspace the call needs (0 if none) */
+} attn_paged_plan;
+
+enum {
+    ATTN_PATH_AUTO = 0,
+    ATTN_PATH_SPLIT_DECODE = 1, /* split-KV partial kernel + log-sum-exp combine kernel */
+    ATTN_PATH_PREFILL = 2       /* q-tile kernel with causal tile skipping, one pass */
+};
+
+/*
+ * attn_paged_make_plan -- choose path, split size and grid for a call with
+ * these sizes.  path_hint: ATTN_PATH_AUTO or a forced path; pages_per_split:
+ * 0 = automatic, otherwise forced (split path only).  Pure host logic: it
+ * reads no device memory and may be called without a GPU.
+ * Split-KV partial outputs and (max, sum) statistics per split follow the
+ * decode.json manifest's scratch buffers partial / stats (ops.decode.impl
+ * .scratch) and the Mojo docs' PartitionType (KV-cache partition scheme).
+ * Returns ATTN_OK or a validation error.
+ */
+int attn_paged_make_plan(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                         int32_t path_hint, int32_t pages_per_split, attn_paged_plan *plan);
+
+/*
+ * attn_paged_workspace_bytes -- device workspace (bytes) that attn_paged_fwd
+ * needs for these sizes under the automatic plan; writes it to *bytes.
+ * Host-only, may be called without a GPU.
+ */
+int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                               size_t *bytes);
+
+/*
+ * attn_paged_fwd -- paged GQA attention forward (the operation above).
+ *   out          bf16 [num_tokens, Hq, D] (strided); rows [0, cu_q[n_seqs])
+ *                are written, other rows untouched.
+ *   q            bf16 [num_tokens, Hq, D] (strided).
+ *   kv_pool      bf16 pool; K/V rows addressed through dims' kv strides.
+ *   block_table  int32 [n_seqs, MP] (row stride dims->bt_stride); only the
+ *                first ceil(L_b / P) entries of row b are read.
+ *   seq_lens     int32 [n_seqs]: L_b, the total KV length including this
+ *                step's n_b tokens; 0 <= L_b <= MP * P.
+ *   cu_q         int32 [n_seqs + 1]: cu_q[0] = 0, non-decreasing,
+ *                cu_q[n_seqs] <= num_tokens.
+ *   n_seqs       number of sequences (>= 0; 0 is a no-op).
+ *   max_q        host-side upper bound on every n_b (sizes the grid without
+ *                reading device memory); n_b > max_q is a caller error.
+ *   scale        softmax scale applied to q.K (for example 1/sqrt(D)).
+ *   causal       nonzero = bottom-right aligned causal mask.
+ *   workspace    device buffer of >= attn_paged_workspace_bytes bytes,
+ *                256-byte aligned (may be NULL when that size is 0); holds
+ *                split-KV partials between the two kernels of the split path.
+ *   stream       hipStream_t to enqueue on (NULL = default stream).
+ */
+int attn_paged_fwd(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * attn_paged_fwd_ex -- attn_paged_fwd with a forced path and split size
+ * (path_hint / pages_per_split as in attn_paged_make_plan).  The workspace
+ * must hold the workspace_bytes of that plan.  For tests and tuning.
+ */
+int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                      const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                      float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                      size_t workspace_bytes, void *stream, int32_t path_hint,
+                      int32_t pages_per_split);
+
+/*
+ * Kernel timing (instrumentation for benchmarks).  While enabled, every
+ * launch is bracketed by HIP events recorded on the launch stream; the
+ * elapsed times of the main attention kernel and of the combine kernel are
+ * summed per kernel.  attn_kernel_timing_read synchronises on the recorded
+ * events, returns the totals (milliseconds) and launch counts, and resets
+ * them.  Returns ATTN_ERR_HIP if an event call fails.
+ */
+int attn_kernel_timing_enable(int32_t enable);
+int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
+                            int32_t *combine_launches);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char *attn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

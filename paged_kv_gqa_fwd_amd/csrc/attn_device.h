@@ -1,0 +1,84 @@
+// Device-side helpers and kernel argument blocks for the gfx950 paged
+// attention kernels.  Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 64;      // keys per page (one KV tile)
+constexpr int kThreads = 256;  // 4 wave64 per workgroup
+
+// Arguments shared by the split-KV decode kernel and the prefill kernel.
+struct AttnArgs {
+    uint16_t *out;              // bf16 [T, Hq, D] (strided)
+    const uint16_t *q;          // bf16 [T, Hq, D] (strided)
+    const uint16_t *kv;         // bf16 pool
+    const int32_t *block_table; // [B, MP] (row stride bt_stride)
+    const int32_t *seq_lens;    // [B]
+    const int32_t *cu_q;        // [B + 1]
+    float *part_o;              // f32 [T, Hq, S, D] split partials (unnormalised)
+    float *part_ml;             // f32 [T, Hq, S, 2] split (max in log2 units, sum)
+    int64_t q_st, q_sh, o_st, o_sh;
+    int64_t kv_sp, kv_ss, kv_sh, kv_skv;
+    int64_t bt_stride;
+    int32_t n_seqs, max_q, hq, hkv, group;
+    int32_t pages_per_split, max_splits;
+    int32_t causal;
+    float scale_log2;           // scale * log2(e): scores live in log2 units
+};
+
+struct CombineArgs {
+    uint16_t *out;
+    const float *part_o;
+    const float *part_ml;
+    const int32_t *seq_lens;
+    const int32_t *cu_q;
+    int64_t o_st, o_sh;
+    int32_t n_seqs, max_q, hq, pages_per_split, max_splits;
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+// Number of keys visible to query i of a sequence with n queries and L keys
+// (bottom-right causal alignment; all L keys when not causal).
+__device__ __forceinline__ int visible_keys(int L, int n, int i, int causal) {
+    if (!causal) return L;
+    int v = L - n + i + 1;
+    return v < 0 ? 0 : (v > L ? L : v);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane s supplies the address of 4 consecutive bf16; lane j receives
+// element (j % 4) of lanes 4r + j/4 for r = 0..3.  With lane s pointing at
+// row (s / 4), columns 4*(s % 4) .. +3 of a row-major tile, lane j receives
+// column j of the four rows.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t *lds_ptr) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(const_cast<uint16_t *>(lds_ptr)));
+}
+
+}  // namespace pa

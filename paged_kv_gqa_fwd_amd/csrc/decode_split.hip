@@ -1,0 +1,317 @@
+// Split-KV paged decode kernel and log-sum-exp combine kernel (gfx950).
+//
+// What is computed follows the split-KV scheme of the kern-kernels
+// examples/decode.json manifest (ops.decode.impl.scratch: per-split partial
+// outputs and per-row (max, sum) statistics, grid.x = KV splits per
+// (KV head, sequence)) and the Mojo SM100MHA2Q docs (PartitionType: KV-cache
+// partition scheme; MaskType: causal or unmasked).  The pages' kernels fuse
+// the merge through a counter; here it is a second, separate kernel.
+//
+// Design (MI355X): one workgroup of 4 wave64 per (sequence, KV head, split).
+// The split's pages stream through LDS with 16-byte coalesced loads, staged
+// in registers one page ahead.  The G q heads x n query tokens of the KV
+// head (<= 16 rows) form the N side of the MFMA and the keys the M side
+// ("swap AB"), so the score tile's C layout is directly the B operand of the
+// P.V MFMA.  Each wave owns 16 keys of every page and keeps its own online
+// softmax state; the four waves merge in LDS at the end.
+#include "attn_device.h"
+
+namespace pa {
+
+template <int D>
+struct DecodeCfg {
+    static constexpr int KROW = D + 8;    // bf16 per LDS K row (16 B pad: conflict-free b128 reads)
+    static constexpr int VROW = D + 16;   // bf16 per LDS V row (32 B pad: conflict-free tr reads)
+    static constexpr int CHUNKS = 2 * kPage * D / 8;          // 16-byte chunks per K+V page
+    static constexpr int CH_PER_THREAD = CHUNKS / kThreads;   // D/16
+    static constexpr int LDS_ELEMS = kPage * (KROW + VROW);
+};
+
+// Issue the 16-byte loads of one page (K and V rows of one KV head) into
+// registers.  Chunk c -> key = c / (D/4), kv = (c / (D/8)) % 2, dc = c % (D/8):
+// consecutive threads read consecutive 16 bytes of one key's K row then V row.
+// Slots at or past `valid` (the tail of a sequence's last page) are not read
+// and stage as zeros: their memory may hold anything, and a non-finite V
+// would turn the zero softmax weight of a masked key into NaN in P.V.
+template <int D>
+__device__ __forceinline__ void load_page(u32x4 (&stage)[DecodeCfg<D>::CH_PER_THREAD],
+                                          const uint16_t *head_base, int64_t page_off,
+                                          int64_t kv_ss, int64_t kv_skv, int tid, int valid) {
+    constexpr int DC = D / 8;
+#pragma unroll
+    for (int it = 0; it < DecodeCfg<D>::CH_PER_THREAD; ++it) {
+        const int c = it * kThreads + tid;
+        const int dc = c % DC;
+        const int kv = (c / DC) & 1;
+        const int key = c / (2 * DC);
+        const uint16_t *src = head_base + page_off + (int64_t)key * kv_ss + kv * kv_skv + dc * 8;
+        stage[it] = key < valid ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_page(const u32x4 (&stage)[DecodeCfg<D>::CH_PER_THREAD],
+                                           uint16_t *ks, uint16_t *vs, int tid) {
+    constexpr int DC = D / 8;
+#pragma unroll
+    for (int it = 0; it < DecodeCfg<D>::CH_PER_THREAD; ++it) {
+        const int c = it * kThreads + tid;
+        const int dc = c % DC;
+        const int kv = (c / DC) & 1;
+        const int key = c / (2 * DC);
+        uint16_t *dst = kv ? (vs + key * DecodeCfg<D>::VROW + dc * 8)
+                           : (ks + key * DecodeCfg<D>::KROW + dc * 8);
+        *reinterpret_cast<u32x4 *>(dst) = stage[it];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void paged_decode_split_kernel(const AttnArgs a) {
+    using C = DecodeCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+    __shared__ float red_m[4][16];
+    __shared__ float red_l[4][16];
+    uint16_t *ks = smem;
+    uint16_t *vs = smem + kPage * C::KROW;
+
+    const int s = blockIdx.x;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+
+    const int L = a.seq_lens[b];
+    const int q0 = a.cu_q[b];
+    int n = a.cu_q[b + 1] - q0;
+    if (n > a.max_q) n = a.max_q;  // caller contract: n_b <= max_q
+    const int npages = (L + kPage - 1) / kPage;
+    const int p_begin = s * a.pages_per_split;
+    // Uniform across the workgroup.  A split past the sequence's last page
+    // writes nothing (the combine never reads it); without splitting, an
+    // empty sequence still runs the epilogue so its rows are written as zeros.
+    if (n <= 0 || (s > 0 && p_begin >= npages)) return;
+    const int p_end = min(npages, p_begin + a.pages_per_split);
+    const int G = a.group;
+    int rows = n * G;
+    if (rows > 16) rows = 16;
+
+    // This lane's query row (the N index of the MFMA tiles).
+    const int row = lane & 15;
+    const bool row_ok = row < rows;
+    const int qi = row / G;
+    const int h = g * G + (row - qi * G);
+    const int vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
+
+    // Q^T as the B operand of v_mfma_f32_16x16x32_bf16: lane holds
+    // q[row, 32*kk + 8*(lane/16) .. +7] for kk = 0 .. D/32-1.
+    bf16x8 qreg[D / 32];
+    {
+        const uint16_t *qp = a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk);
+            qreg[kk] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    const uint16_t *head_base = a.kv + (int64_t)g * a.kv_sh;
+    const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
+
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
+    float l_part = 0.f;        // this lane's share of the running sum
+
+    u32x4 stage[C::CH_PER_THREAD];
+    if (p_begin < p_end)
+        load_page<D>(stage, head_base, (int64_t)bt_row[p_begin] * a.kv_sp, a.kv_ss, a.kv_skv, tid,
+                     L - p_begin * kPage);
+
+    for (int p = p_begin; p < p_end; ++p) {
+        __syncthreads();                 // previous page fully consumed
+        store_page<D>(stage, ks, vs, tid);
+        __syncthreads();
+        if (p + 1 < p_end)
+            load_page<D>(stage, head_base, (int64_t)bt_row[p + 1] * a.kv_sp, a.kv_ss, a.kv_skv, tid,
+                         L - (p + 1) * kPage);
+
+        // S^T[16 keys x 16 rows] for keys 16w .. 16w+15 of this page.
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint16_t *kp = ks + (16 * w + (lane & 15)) * C::KROW + 8 * (lane >> 4);
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 32 * kk);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], sacc, 0, 0, 0);
+            }
+        }
+        // sacc[i] = score of key p*64 + 16w + 4*(lane/16) + i for this lane's row.
+        const int key0 = p * kPage + 16 * w + 4 * (lane >> 4);
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sv[i] = (key0 + i < vis) ? sacc[i] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[i]);
+        }
+        mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run - m_use);
+        m_run = m_new;
+        bf16x4 pb;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const __bf16 pr = (__bf16)exp2_fast(sv[i] - m_use);
+            pb[i] = pr;
+            psum += (float)pr;   // the sum uses the same rounded P as the P.V product
+        }
+        l_part = l_part * alpha + psum;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+        }
+        // O^T[d, row] += V^T[d, key] P^T[key, row] over this wave's 16 keys.
+        const i16x4 pop = __builtin_bit_cast(i16x4, pb);
+        const uint16_t *vp = vs + (16 * w + 4 * (lane >> 4) + ((lane & 15) >> 2)) * C::VROW + 4 * (lane & 3);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * db));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four waves' (m, l, O) in LDS --------------------------
+    float l_row = l_part + shfl_xor_f32(l_part, 16);
+    l_row += shfl_xor_f32(l_row, 32);
+    if (lane < 16) {
+        red_m[w][lane] = m_run;
+        red_l[w][lane] = l_row;
+    }
+    __syncthreads();   // also: all waves are done with the K/V tiles
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][row]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float wgt = exp2_fast(m_run - M_use);
+    float *ored = reinterpret_cast<float *>(smem);   // [4 waves][16 rows][D] f32
+    static_assert(4 * 16 * D * 4 <= C::LDS_ELEMS * 2, "LDS too small for the merge");
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d = 16 * db + 4 * (lane >> 4) + i;
+            ored[(w * 16 + row) * D + d] = oacc[db][i] * wgt;
+        }
+    }
+    __syncthreads();
+
+    const bool split = a.max_splits > 1;
+    // Thread -> (rows r = tid / D + k * (256 / D), column d = tid % D).
+    constexpr int RSTEP = kThreads / D;   // 1 (D=256) or 2 (D=128)
+    const int d = tid % D;
+    for (int r = tid / D; r < rows; r += RSTEP) {
+        float Mr = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) Mr = fmaxf(Mr, red_m[ww][r]);
+        const float Mr_use = (Mr == -INFINITY) ? 0.f : Mr;
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            lsum += red_l[ww][r] * exp2_fast(red_m[ww][r] - Mr_use);
+            osum += ored[(ww * 16 + r) * D + d];
+        }
+        const int ri = r / G;
+        const int rh = g * G + (r - ri * G);
+        const int64_t t = q0 + ri;
+        if (split) {
+            // partial rows are indexed by (sequence, query index), not token,
+            // so the workspace scales with n_seqs * max_q
+            const int64_t prow = (int64_t)b * a.max_q + ri;
+            const int64_t slot = (prow * a.hq + rh) * a.max_splits + s;
+            a.part_o[slot * D + d] = osum;
+            if (d == 0) {
+                a.part_ml[slot * 2 + 0] = Mr;
+                a.part_ml[slot * 2 + 1] = lsum;
+            }
+        } else {
+            const float o = lsum > 0.f ? osum / lsum : 0.f;
+            a.out[t * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(o);
+        }
+    }
+}
+
+// Log-sum-exp merge of the split partials: per (token, q head) row,
+// M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s.
+// One wave64 per row; splits that hold no page of the sequence are skipped.
+template <int D>
+__global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int i = blockIdx.y;
+    const int b = blockIdx.z;
+    if (h >= a.hq) return;
+    const int q0 = a.cu_q[b];
+    int n = a.cu_q[b + 1] - q0;
+    if (n > a.max_q) n = a.max_q;
+    if (i >= n) return;
+    const int L = a.seq_lens[b];
+    const int npages = (L + kPage - 1) / kPage;
+    int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
+    if (ns > a.max_splits) ns = a.max_splits;
+    const int64_t t = q0 + i;
+    const int64_t base = (((int64_t)b * a.max_q + i) * a.hq + h) * a.max_splits;
+
+    float M = -INFINITY;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_ml[(base + s) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float lsum = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const float ms = a.part_ml[(base + s) * 2];
+            const float ls = a.part_ml[(base + s) * 2 + 1];
+            const float wgt = exp2_fast(ms - M);   // ms = -inf gives 0
+            lsum += wgt * ls;
+            const float *po = a.part_o + (base + s) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wgt * po[lane + 64 * e];
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t *op = a.out + t * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) op[lane + 64 * e] = f32_to_bf16_bits(acc[e] * inv);
+}
+
+template <int D>
+hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL(paged_decode_split_kernel<D>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
+    dim3 grid((a.hq + 3) / 4, a.max_q, a.n_seqs);
+    hipLaunchKernelGGL(paged_combine_kernel<D>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    return D == 128 ? launch_decode_split<128>(a, grid, stream) : launch_decode_split<256>(a, grid, stream);
+}
+
+hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream) {
+    return D == 128 ? launch_combine<128>(a, stream) : launch_combine<256>(a, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,311 @@
+// Host side of libpaged_attn: argument validation, execution planning and
+// kernel launches behind the C ABI declared in include/paged_attn.h.
+//
+// Validation and planning are pure host logic and touch no HIP API, so they
+// run (and are tested) on machines without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "attn_device.h"
+#include "paged_attn.h"
+
+namespace pa {
+hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
+hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
+hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
+}  // namespace pa
+
+namespace {
+
+constexpr int kVersion = 10000;          // 1.0.0
+constexpr int kMaxDecodeRows = 16;       // G * max_q rows fit one 16-wide MFMA tile
+constexpr int kPrefillRows = 128;        // packed query rows per prefill workgroup
+constexpr int kGridYZMax = 65535;
+constexpr size_t kWsAlign = 256;
+// Target number of split workgroups for the decode path: enough to cover the
+// 256 compute units several times over so the page streams stay balanced.
+constexpr int64_t kSplitTargetWorkgroups = 4096;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int validate_dims(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q) {
+    if (!d) return ATTN_ERR_NULL;
+    if (d->head_dim != 128 && d->head_dim != 256) return ATTN_ERR_UNSUPPORTED;
+    if (d->page_size != pa::kPage) return ATTN_ERR_UNSUPPORTED;
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return ATTN_ERR_SHAPE;
+    if (d->num_q_heads % d->num_kv_heads != 0) return ATTN_ERR_SHAPE;
+    if (d->num_kv_heads > kGridYZMax) return ATTN_ERR_SHAPE;
+    if (d->num_pages <= 0 || d->max_pages_per_seq <= 0) return ATTN_ERR_SHAPE;
+    if (d->num_tokens < 0) return ATTN_ERR_SHAPE;
+    if (n_seqs < 0 || n_seqs > kGridYZMax) return ATTN_ERR_SHAPE;
+    if (n_seqs > 0 && (max_q <= 0 || (int64_t)max_q > d->num_tokens)) return ATTN_ERR_SHAPE;
+    const int64_t D = d->head_dim, hq = d->num_q_heads;
+    // Element strides: positive, multiples of 8 (16-byte aligned rows), rows disjoint.
+    const int64_t strides[] = {d->q_stride_token, d->q_stride_head, d->o_stride_token,
+                               d->o_stride_head, d->kv_stride_page, d->kv_stride_slot,
+                               d->kv_stride_head, d->kv_stride_kv};
+    for (int64_t s : strides)
+        if (s <= 0 || (s & 7) != 0) return ATTN_ERR_STRIDE;
+    if (d->q_stride_head < D || d->q_stride_token < hq * d->q_stride_head) return ATTN_ERR_STRIDE;
+    if (d->o_stride_head < D || d->o_stride_token < hq * d->o_stride_head) return ATTN_ERR_STRIDE;
+    if (d->kv_stride_kv < D) return ATTN_ERR_STRIDE;
+    if (d->bt_stride < d->max_pages_per_seq) return ATTN_ERR_STRIDE;
+    return ATTN_OK;
+}
+
+int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
+              int32_t pps, attn_paged_plan *plan) {
+    int rc = validate_dims(d, n_seqs, max_q);
+    if (rc != ATTN_OK) return rc;
+    if (!plan) return ATTN_ERR_NULL;
+    if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_PREFILL) return ATTN_ERR_SHAPE;
+    if (pps < 0) return ATTN_ERR_SHAPE;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const int64_t mq = std::max<int32_t>(max_q, 1);
+    int path = path_hint;
+    if (path == ATTN_PATH_AUTO)
+        path = (mq * G <= kMaxDecodeRows) ? ATTN_PATH_SPLIT_DECODE : ATTN_PATH_PREFILL;
+    if (path == ATTN_PATH_SPLIT_DECODE && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
+    *plan = attn_paged_plan{};
+    plan->path = path;
+    plan->block_threads = pa::kThreads;
+    const int64_t MP = d->max_pages_per_seq;
+    if (path == ATTN_PATH_SPLIT_DECODE) {
+        int64_t p = pps;
+        if (p == 0) {
+            const int64_t bound = MP * std::max<int64_t>(n_seqs, 1) * d->num_kv_heads;
+            p = (bound + kSplitTargetWorkgroups - 1) / kSplitTargetWorkgroups;
+        }
+        p = std::min<int64_t>(std::max<int64_t>(p, 1), MP);
+        const int64_t S = (MP + p - 1) / p;
+        plan->pages_per_split = (int32_t)p;
+        plan->max_splits = (int32_t)S;
+        plan->grid_x = (int32_t)S;
+        plan->grid_y = d->num_kv_heads;
+        plan->grid_z = n_seqs;
+        if (S > 1) {
+            const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads * (size_t)S;
+            plan->workspace_bytes = align_up(rows * (size_t)d->head_dim * 4, kWsAlign) + align_up(rows * 8, kWsAlign);
+        }
+    } else {
+        const int64_t tiles = (mq * G + kPrefillRows - 1) / kPrefillRows;
+        if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
+        plan->pages_per_split = (int32_t)MP;
+        plan->max_splits = 1;
+        plan->grid_x = (int32_t)tiles;
+        plan->grid_y = d->num_kv_heads;
+        plan->grid_z = n_seqs;
+    }
+    return ATTN_OK;
+}
+
+// ---- kernel timing instrumentation ---------------------------------------
+struct TimedLaunch {
+    hipEvent_t start, stop;
+    bool combine;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimedLaunch> g_timed;
+
+int record_event(hipEvent_t *ev, hipStream_t stream) {
+    if (hipEventCreate(ev) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipEventRecord(*ev, stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+}
+
+int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                   size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps) {
+    attn_paged_plan plan;
+    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, &plan);
+    if (rc != ATTN_OK) return rc;
+    if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+    if (n_seqs == 0) return ATTN_OK;
+    if (!out || !q || !kv_pool || !block_table || !seq_lens || !cu_q) return ATTN_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return ATTN_ERR_ALIGN;
+    if (!aligned4(block_table) || !aligned4(seq_lens) || !aligned4(cu_q)) return ATTN_ERR_ALIGN;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0)
+            return ATTN_ERR_WORKSPACE;
+        if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
+    }
+
+    const int D = dims->head_dim;
+    const int G = dims->num_q_heads / dims->num_kv_heads;
+    pa::AttnArgs a{};
+    a.out = static_cast<uint16_t *>(out);
+    a.q = static_cast<const uint16_t *>(q);
+    a.kv = static_cast<const uint16_t *>(kv_pool);
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.cu_q = cu_q;
+    a.q_st = dims->q_stride_token;
+    a.q_sh = dims->q_stride_head;
+    a.o_st = dims->o_stride_token;
+    a.o_sh = dims->o_stride_head;
+    a.kv_sp = dims->kv_stride_page;
+    a.kv_ss = dims->kv_stride_slot;
+    a.kv_sh = dims->kv_stride_head;
+    a.kv_skv = dims->kv_stride_kv;
+    a.bt_stride = dims->bt_stride;
+    a.n_seqs = n_seqs;
+    a.max_q = max_q;
+    a.hq = dims->num_q_heads;
+    a.hkv = dims->num_kv_heads;
+    a.group = G;
+    a.pages_per_split = plan.pages_per_split;
+    a.max_splits = plan.max_splits;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    if (plan.workspace_bytes > 0) {
+        const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
+        a.part_o = static_cast<float *>(workspace);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(rows * (size_t)D * 4, kWsAlign));
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(plan.grid_x, plan.grid_y, plan.grid_z);
+    bool timing;
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        timing = g_timing_on;
+    }
+    TimedLaunch t_main{}, t_comb{};
+    if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+    hipError_t e = plan.path == ATTN_PATH_SPLIT_DECODE ? pa::launch_decode_split_any(D, a, grid, st)
+                                                      : pa::launch_prefill_any(D, a, grid, st);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (timing && record_event(&t_main.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+    const bool need_combine = plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1;
+    if (need_combine) {
+        pa::CombineArgs c{};
+        c.out = a.out;
+        c.part_o = a.part_o;
+        c.part_ml = a.part_ml;
+        c.seq_lens = seq_lens;
+        c.cu_q = cu_q;
+        c.o_st = a.o_st;
+        c.o_sh = a.o_sh;
+        c.n_seqs = n_seqs;
+        c.max_q = max_q;
+        c.hq = a.hq;
+        c.pages_per_split = plan.pages_per_split;
+        c.max_splits = plan.max_splits;
+        if (timing && record_event(&t_comb.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+        e = pa::launch_combine_any(D, c, st);
+        if (e != hipSuccess) return ATTN_ERR_HIP;
+        if (timing && record_event(&t_comb.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+    }
+    if (timing) {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        t_main.combine = false;
+        g_timed.push_back(t_main);
+        if (need_combine) {
+            t_comb.combine = true;
+            g_timed.push_back(t_comb);
+        }
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_paged_make_plan(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                         int32_t path_hint, int32_t pages_per_split, attn_paged_plan *plan) {
+    return make_plan(dims, n_seqs, max_q, path_hint, pages_per_split, plan);
+}
+
+int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                               size_t *bytes) {
+    if (!bytes) return ATTN_ERR_NULL;
+    attn_paged_plan plan;
+    int rc = make_plan(dims, n_seqs, max_q, ATTN_PATH_AUTO, 0, &plan);
+    if (rc != ATTN_OK) return rc;
+    *bytes = plan.workspace_bytes;
+    return ATTN_OK;
+}
+
+int attn_paged_fwd(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale,
+                          causal, dims, workspace, workspace_bytes, stream, ATTN_PATH_AUTO, 0);
+}
+
+int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                      const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                      float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                      size_t workspace_bytes, void *stream, int32_t path_hint,
+                      int32_t pages_per_split) {
+    return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale,
+                          causal, dims, workspace, workspace_bytes, stream, path_hint,
+                          pages_per_split);
+}
+
+int attn_kernel_timing_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing_on = enable != 0;
+    return ATTN_OK;
+}
+
+int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
+                            int32_t *combine_launches) {
+    std::vector<TimedLaunch> v;
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        v.swap(g_timed);
+    }
+    double tm = 0, tc = 0;
+    int nm = 0, nc = 0;
+    int rc = ATTN_OK;
+    for (auto &t : v) {
+        float ms = 0.f;
+        if (hipEventSynchronize(t.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+            rc = ATTN_ERR_HIP;
+        if (t.combine) {
+            tc += ms;
+            ++nc;
+        } else {
+            tm += ms;
+            ++nm;
+        }
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    if (main_ms) *main_ms = tm;
+    if (main_launches) *main_launches = nm;
+    if (combine_ms) *combine_ms = tc;
+    if (combine_launches) *combine_launches = nc;
+    return rc;
+}
+
+const char *attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head_dim, page_size or rows)";
+        case ATTN_ERR_STRIDE: return "invalid stride";
+        case ATTN_ERR_ALIGN: return "pointer not aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int attn_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before launching anything.
+No call here reaches a kernel launch (every call fails validation, plans, or
+is the n_seqs == 0 no-op), so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_STRIDE, E_ALIGN, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000   # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import paged_kv_gqa_fwd_amd as mod
+    from paged_kv_gqa_fwd_amd import build as b
+    if not os.path.exists(mod.LIB_PATH):
+        b.build()
+    mod.load_library()
+    return mod
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    fns = header_functions()
+    for name in ("attn_paged_fwd", "attn_paged_fwd_ex", "attn_paged_make_plan",
+                 "attn_paged_workspace_bytes", "attn_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_header_function(pa):
+    lib = ctypes.CDLL(pa.LIB_PATH)
+    missing = [f for f in header_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def dims(**kw):
+    import paged_kv_gqa_fwd_amd as mod
+    d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, num_pages=100,
+             max_pages_per_seq=16, num_tokens=64, q_stride_token=32 * 128, q_stride_head=128,
+             o_stride_token=32 * 128, o_stride_head=128, kv_stride_page=64 * 8 * 2 * 128,
+             kv_stride_slot=8 * 2 * 128, kv_stride_head=2 * 128, kv_stride_kv=128, bt_stride=16)
+    d.update(kw)
+    return mod.attn_paged_dims(**d)
+
+
+def call(pa, d, n_seqs=4, max_q=1, out=FAKE, q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, cq=FAKE,
+         scale=0.1, causal=1, ws=None, ws_bytes=0, path=0, pps=0):
+    lib = pa.load_library()
+    return lib.attn_paged_fwd_ex(out, q, kv, bt, sl, cq, n_seqs, max_q, scale, causal,
+                                 ctypes.byref(d) if d is not None else None, ws, ws_bytes, None,
+                                 path, pps)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(head_dim=64), E_UNSUP),
+    (dict(head_dim=192), E_UNSUP),
+    (dict(page_size=32), E_UNSUP),
+    (dict(num_q_heads=30), E_SHAPE),
+    (dict(num_kv_heads=0), E_SHAPE),
+    (dict(num_pages=0), E_SHAPE),
+    (dict(max_pages_per_seq=0), E_SHAPE),
+    (dict(q_stride_head=100), E_STRIDE),
+    (dict(q_stride_head=120), E_STRIDE),
+    (dict(q_stride_token=128), E_STRIDE),
+    (dict(o_stride_head=0), E_STRIDE),
+    (dict(kv_stride_kv=64), E_STRIDE),
+    (dict(kv_stride_slot=-256), E_STRIDE),
+    (dict(bt_stride=8), E_STRIDE),
+])
+def test_invalid_dims_rejected(pa, kw, expect):
+    assert call(pa, dims(**kw)) == expect
+
+
+def test_null_dims(pa):
+    assert call(pa, None) == E_NULL
+
+
+@pytest.mark.parametrize("which", ["out", "q", "kv", "bt", "sl", "cq"])
+def test_null_pointers(pa, which):
+    assert call(pa, dims(), **{which: None}) == E_NULL
+
+
+@pytest.mark.parametrize("which,val", [("out", FAKE + 2), ("q", FAKE + 8), ("kv", FAKE + 4),
+                                       ("bt", FAKE + 1), ("sl", FAKE + 2), ("cq", FAKE + 3)])
+def test_misaligned_pointers(pa, which, val):
+    assert call(pa, dims(), **{which: val}) == E_ALIGN
+
+
+def test_bad_sizes(pa):
+    assert call(pa, dims(), n_seqs=-1) == E_SHAPE
+    assert call(pa, dims(), n_seqs=70000) == E_SHAPE
+    assert call(pa, dims(), max_q=0) == E_SHAPE
+    assert call(pa, dims(), max_q=65) == E_SHAPE         # > num_tokens
+    assert call(pa, dims(), scale=float("nan")) == E_SHAPE
+    assert call(pa, dims(), scale=float("inf")) == E_SHAPE
+    assert call(pa, dims(), path=7) == E_SHAPE
+    assert call(pa, dims(), pps=-1) == E_SHAPE
+
+
+def test_forced_split_path_row_limit(pa):
+    # G = 4; max_q = 5 -> 20 rows > 16: the split kernel cannot take it
+    assert call(pa, dims(), max_q=5, path=1) == E_UNSUP
+
+
+def test_workspace_checks(pa):
+    import paged_kv_gqa_fwd_amd as mod
+    d = dims(max_pages_per_seq=128, bt_stride=128)
+    plan = mod.make_plan(d, 64, 1)
+    assert plan.path == mod.PATH_SPLIT_DECODE and plan.max_splits > 1 and plan.workspace_bytes > 0
+    assert call(pa, d, n_seqs=64) == E_WS                                   # missing
+    assert call(pa, d, n_seqs=64, ws=FAKE + 16, ws_bytes=1 << 30) == E_WS   # misaligned
+    assert call(pa, d, n_seqs=64, ws=FAKE, ws_bytes=plan.workspace_bytes - 1) == E_WS
+
+
+def test_zero_sequences_is_noop(pa):
+    assert call(pa, dims(), n_seqs=0, out=None, q=None) == OK
+
+
+def test_plan_paths_and_sizes(pa):
+    import paged_kv_gqa_fwd_amd as mod
+    # decode batch: 64 seqs, G=4, MP=128 -> split decode
+    d = dims(max_pages_per_seq=128, bt_stride=128)
+    p = mod.make_plan(d, 64, 1)
+    assert p.path == mod.PATH_SPLIT_DECODE
+    assert p.grid_x == p.max_splits and p.grid_y == 8 and p.grid_z == 64
+    assert p.max_splits == -(-128 // p.pages_per_split)
+    rows = 64 * 1 * 32 * p.max_splits
+    assert p.workspace_bytes >= rows * 128 * 4 + rows * 8
+    # many query rows -> prefill, no workspace
+    d2 = dims(num_q_heads=24, num_kv_heads=4, head_dim=256, q_stride_token=24 * 256,
+              q_stride_head=256, o_stride_token=24 * 256, o_stride_head=256, num_tokens=4096,
+              kv_stride_page=64 * 4 * 2 * 256, kv_stride_slot=4 * 2 * 256, kv_stride_head=512,
+              kv_stride_kv=256, max_pages_per_seq=192, bt_stride=192)
+    p2 = mod.make_plan(d2, 8, 4096)
+    assert p2.path == mod.PATH_PREFILL and p2.workspace_bytes == 0
+    assert p2.grid_x == -(-4096 * 6 // 128) and p2.grid_y == 4 and p2.grid_z == 8
+    # forced split sizes are clamped to [1, MP]
+    p3 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 1000)
+    assert p3.pages_per_split == 128 and p3.max_splits == 1 and p3.workspace_bytes == 0
+    p4 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 3)
+    assert p4.pages_per_split == 3 and p4.max_splits == 43
+    # long decode: 128 seqs x 512 pages, 2 KV heads -> at least 16 splits' worth of workgroups
+    d5 = dims(num_q_heads=16, num_kv_heads=2, head_dim=256, q_stride_token=16 * 256, q_stride_head=256,
+              o_stride_token=16 * 256, o_stride_head=256, kv_stride_page=64 * 2 * 2 * 256,
+              kv_stride_slot=2 * 2 * 256, kv_stride_head=512, kv_stride_kv=256,
+              max_pages_per_seq=512, bt_stride=512, num_tokens=128)
+    p5 = mod.make_plan(d5, 128, 1)
+    assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_x * 2 * 128 >= 2048
+
+
+def test_workspace_bytes_query(pa):
+    lib = pa.load_library()
+    n = ctypes.c_size_t(0)
+    d = dims(max_pages_per_seq=128, bt_stride=128)
+    assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, ctypes.byref(n)) == OK
+    assert n.value == pa.make_plan(d, 64, 1).workspace_bytes
+    assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, None) == E_NULL
+
+
+def test_status_strings(pa):
+    lib = pa.load_library()
+    for s in (OK, E_NULL, E_SHAPE, E_UNSUP, E_STRIDE, E_ALIGN, E_WS, E_HIP, 12345):
+        assert lib.attn_status_string(s)
+    assert lib.attn_version() >= 10000
+
+
+def test_python_binding_refuses_cpu_tensors(pa):
+    import torch
+    q = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(2, 64, 2, 2, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.paged_attention(q, kv, bt, torch.ones(1, dtype=torch.int32),
+                           torch.tensor([0, 1], dtype=torch.int32), 1, 0.1)

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance (bf16 output vs fp64 oracle, over every written row):
+max-abs <= 2e-2 and relative RMS <= 5e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity_util import compare, log, oracle_for, run_gpu, sub_case_rows
+
+pytestmark = pytest.mark.gpu
+
+PATH_AUTO, PATH_SPLIT, PATH_PREFILL = 0, 1, 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_gqa_fwd_amd as pa
+    pa.load_library()
+
+
+def _check(oracle_mod, case, what, **kw):
+    ref = oracle_for(oracle_mod, case)
+    out = run_gpu(case, **kw)
+    return compare(out, ref, what=what)
+
+
+# ---------------------------------------------------------------- workloads
+def test_tiny_mixed_full(oracle_mod):
+    """2 seqs x 32 queries, 24/4 heads, D 256, the manifest's two-layer pool."""
+    case = workloads.tiny_mixed()
+    _check(oracle_mod, case, "tiny_mixed")
+
+
+@pytest.mark.parametrize("path,pps", [(PATH_AUTO, 0), (PATH_PREFILL, 0)])
+def test_tiny_mixed_paths(oracle_mod, path, pps):
+    case = workloads.tiny_mixed()
+    _check(oracle_mod, case, "tiny_mixed path=%d" % path, path=path, pages_per_split=pps)
+
+
+def test_decode_batch_full(oracle_mod):
+    """The full 64-sequence decode batch (32/8 heads, D 128, L in [1024, 8192])."""
+    case = workloads.decode_batch(device="cuda")
+    _check(oracle_mod, case, "decode_batch")
+
+
+@pytest.mark.parametrize("pps", [1, 3, 16, 128])
+def test_decode_batch_split_sizes(oracle_mod, pps):
+    case = workloads.decode_batch(n_seqs=8, seed=202)
+    _check(oracle_mod, case, "decode_batch pps=%d" % pps, path=PATH_SPLIT, pages_per_split=pps)
+
+
+def test_long_decode_reduced(oracle_mod):
+    """8 sequences at context 32768, 16/2 heads, D 256, 1% outlier keys x4."""
+    case = workloads.long_decode(device="cuda", n_seqs=8)
+    _check(oracle_mod, case, "long_decode(8 seqs)")
+
+
+def test_long_decode_full_sampled(oracle_mod):
+    """Full 128 x 32768 workload in the benchmark's launch configuration; the
+    oracle checks every row of 6 sampled sequences."""
+    case = workloads.long_decode(device="cuda")
+    out = run_gpu(case)
+    seqs = [0, 17, 42, 77, 100, 127]
+    sub, rows = sub_case_rows(case, seqs)
+    ref = oracle_for(oracle_mod, sub)
+    compare(out[rows], ref, what="long_decode full, sampled seqs")
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_chunked_prefill_reduced(oracle_mod):
+    case = workloads.chunked_prefill(n_seqs=3, q_lo=100, q_hi=300, ctx_hi=700, seed=204)
+    _check(oracle_mod, case, "chunked_prefill(reduced)")
+
+
+def test_chunked_prefill_full_sampled(oracle_mod):
+    """Full 8-sequence chunked prefill; oracle on a seeded sample of token rows
+    (first/last tokens of every sequence plus random ones)."""
+    case = workloads.chunked_prefill(device="cuda")
+    out = run_gpu(case)
+    T = sum(case.q_lens)
+    cu = case.cu_q.cpu().tolist()
+    g = torch.Generator().manual_seed(9)
+    pick = set(torch.randint(0, T, (24,), generator=g).tolist())
+    for b in range(case.n_seqs):
+        pick.update({cu[b], cu[b] + 63, cu[b] + 64, cu[b + 1] - 1})
+    mask = np.zeros(T, dtype=np.uint8)
+    mask[sorted(pick)] = 1
+    ref = oracle_for(oracle_mod, case, row_mask=mask)
+    rows = np.nonzero(mask)[0]
+    compare(out, ref, rows=rows, what="chunked_prefill full, %d sampled rows" % len(rows))
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_dit_reduced(oracle_mod):
+    case = workloads.dit_self_attn(n_tokens=1000, heads=8)
+    _check(oracle_mod, case, "dit(1000 tokens, 8 heads)")
+
+
+def test_dit_full_sampled(oracle_mod):
+    """Full 37810-token, 56-head non-causal workload; oracle on 16 sampled tokens
+    (including both ends and a 64-row tile boundary)."""
+    case = workloads.dit_self_attn(device="cuda")
+    out = run_gpu(case)
+    T = case.q.shape[0]
+    picks = sorted({0, 1, 63, 64, 127, 128, T - 51, T - 50, T - 1} |
+                   set(torch.randint(0, T, (7,), generator=torch.Generator().manual_seed(5)).tolist()))
+    mask = np.zeros(T, dtype=np.uint8)
+    mask[picks] = 1
+    ref = oracle_for(oracle_mod, case, row_mask=mask)
+    compare(out, ref, rows=np.array(picks), what="dit full, %d sampled tokens" % len(picks))
+    del case
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE = [
+    # name, q_lens, kv_lens, hq, hkv, d, causal
+    ("single key", [1], [1], 8, 8, 128, True),
+    ("tail 63/64/65", [1, 1, 1], [63, 64, 65], 32, 8, 128, True),
+    ("tail 127/128/129", [1, 1, 1], [127, 128, 129], 16, 2, 256, True),
+    ("n > L rows see nothing", [6, 1], [3, 5], 8, 4, 128, True),
+    ("empty seq n=0", [0, 1, 0], [0, 70, 5], 8, 2, 128, True),
+    ("zero-length kv", [1, 1], [0, 9], 8, 2, 256, True),
+    ("G=1 decode", [1, 1], [300, 1000], 4, 4, 128, True),
+    ("G=6 decode two tokens", [2, 1], [130, 64], 24, 4, 256, True),
+    ("G=8 noncausal", [1, 2], [500, 70], 16, 2, 256, False),
+    ("prefill tile boundary 128/129 rows", [64, 65], [64, 200], 4, 2, 128, True),
+    ("prefill q > 128 rows per head group", [300], [300], 6, 1, 128, True),
+    ("prefill noncausal ragged", [37, 100], [50, 333], 12, 3, 256, False),
+    ("prefill G=6 D256 chunked", [77, 130], [400, 130], 24, 4, 256, True),
+]
+
+
+@pytest.mark.parametrize("name,q_lens,kv_lens,hq,hkv,d,causal", EDGE, ids=[e[0] for e in EDGE])
+@pytest.mark.parametrize("path", [PATH_AUTO, PATH_PREFILL])
+def test_edge_cases(oracle_mod, name, q_lens, kv_lens, hq, hkv, d, causal, path):
+    case = workloads.make_case(name, 300 + len(name), q_lens, kv_lens, hq, hkv, d, causal=causal,
+                               extra_pages=1, poison=True)
+    ref = oracle_for(oracle_mod, case)
+    out = run_gpu(case, path=path)
+    compare(out, ref, what="%s path=%d" % (name, path))
+
+
+def test_rows_outside_cu_q_untouched():
+    case = workloads.make_case("untouched", 401, [1, 1], [100, 60], 8, 2, 128, causal=True)
+    g = case.to("cuda")
+    T = case.q.shape[0]
+    big_q = torch.zeros((T + 5, 8, 128), dtype=torch.bfloat16, device="cuda")
+    big_q[:T] = g.q
+    out = torch.full_like(big_q, 7.0)
+    import paged_kv_gqa_fwd_amd as pa
+    pa.paged_attention(big_q, g.kv, g.block_table, g.seq_lens, g.cu_q, 1, case.scale, True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[T:] == 7.0)
+
+
+def test_strided_q_and_out(oracle_mod):
+    """q and out as views with padded token/head strides."""
+    case = workloads.make_case("strided", 402, [3, 1], [200, 90], 12, 4, 128, causal=True)
+    g = case.to("cuda")
+    T, hq, d = case.q.shape
+    qbig = torch.zeros((T, hq + 2, d + 64), dtype=torch.bfloat16, device="cuda")
+    qv = qbig[:, 1:hq + 1, :d]
+    qv.copy_(g.q)
+    obig = torch.zeros((T, hq + 3, d + 8), dtype=torch.bfloat16, device="cuda")
+    ov = obig[:, 2:hq + 2, :d]
+    import paged_kv_gqa_fwd_amd as pa
+    pa.paged_attention(qv, g.kv, g.block_table, g.seq_lens, g.cu_q, 3, case.scale, True, out=ov)
+    torch.cuda.synchronize()
+    compare(ov, oracle_for(oracle_mod, case), what="strided q/out")
+
+
+# ---------------------------------------------------------------- invariants
+def test_page_relocation_bitwise():
+    case = workloads.decode_batch(n_seqs=6, seed=501)
+    base = run_gpu(case).cpu()
+    NP = case.kv.shape[0]
+    pi = torch.randperm(NP, generator=torch.Generator().manual_seed(2))
+    kv2 = torch.empty_like(case.kv)
+    kv2[pi] = case.kv
+    bt = case.block_table.clone()
+    valid = bt >= 0
+    bt[valid] = pi[bt[valid].long()].to(torch.int32)
+    import dataclasses
+    c2 = dataclasses.replace(case, kv=kv2, pool_storage=kv2, block_table=bt)
+    moved = run_gpu(c2).cpu()
+    assert torch.equal(base.view(torch.int16), moved.view(torch.int16))
+
+
+def test_split_vs_single_pass(oracle_mod):
+    case = workloads.long_decode(n_seqs=2, ctx=4096, seed=502)
+    one = run_gpu(case, path=PATH_SPLIT, pages_per_split=64)
+    many = run_gpu(case, path=PATH_SPLIT, pages_per_split=4)
+    compare(many, one.float().cpu().double().numpy(), what="16 splits vs 1 split",
+            max_abs=2e-2, rel_rms=5e-3)
+
+
+def test_deterministic_bitwise():
+    case = workloads.decode_batch(n_seqs=16, seed=503).to("cuda")
+    a = run_gpu(case).clone()
+    b = run_gpu(case).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c = workloads.chunked_prefill(n_seqs=2, q_lo=100, q_hi=200, ctx_hi=300, seed=504).to("cuda")
+    x = run_gpu(c).clone()
+    y = run_gpu(c).clone()
+    assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_constant_v_gives_that_row():
+    case = workloads.make_case("constv", 505, [1, 40], [700, 900], 24, 4, 256, causal=True)
+    row = torch.randn(256, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    case.kv[:, :, :, 1, :] = row
+    out = run_gpu(case).cpu()
+    exp = row.float().expand(out.shape[0], 24, 256)
+    assert torch.allclose(out.float(), exp, atol=1e-2, rtol=0)
