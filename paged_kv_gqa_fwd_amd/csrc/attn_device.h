@@ -18,6 +18,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = 64;      // keys per page (one KV tile)
 constexpr int kThreads = 256;  // 4 wave64 per workgroup
 
+// Split-decode tuning (compile-time knobs; the defaults are the measured best
+// on MI355X): register stages = pages in flight per workgroup, and the
+// resident waves per SIMD requested from the register allocator.  The host
+// planner sizes splits from the same numbers.
+#ifndef PA_DECODE_STAGES_128
+#define PA_DECODE_STAGES_128 2
+#endif
+#ifndef PA_DECODE_STAGES_256
+#define PA_DECODE_STAGES_256 1
+#endif
+#ifndef PA_DECODE_WAVES_128
+#define PA_DECODE_WAVES_128 2
+#endif
+#ifndef PA_DECODE_WAVES_256
+#define PA_DECODE_WAVES_256 1
+#endif
+constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
+constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
+
 // Arguments shared by the split-KV decode kernel and the prefill kernel.
 struct AttnArgs {
     uint16_t *out;              // bf16 [T, Hq, D] (strided)

@@ -7,9 +7,9 @@
 // partition scheme; MaskType: causal or unmasked).  The pages' kernels fuse
 // the merge through a counter; here it is a second, separate kernel.
 //
-// Design (MI355X): one workgroup of 4 wave64 per (sequence, KV head, split).
+// Design (MI355X): one workgroup of 4 wave64 per (KV head, sequence, split).
 // The split's pages stream through LDS with 16-byte coalesced loads, staged
-// in registers one page ahead.  The G q heads x n query tokens of the KV
+// in registers two pages ahead.  The G q heads x n query tokens of the KV
 // head (<= 16 rows) form the N side of the MFMA and the keys the M side
 // ("swap AB"), so the score tile's C layout is directly the B operand of the
 // P.V MFMA.  Each wave owns 16 keys of every page and keeps its own online
@@ -20,6 +20,8 @@ namespace pa {
 
 template <int D>
 struct DecodeCfg {
+    static constexpr int STAGES = decode_stages(D);
+    static constexpr int WAVES_PER_SIMD = decode_waves_per_simd(D);
     static constexpr int KROW = D + 8;    // bf16 per LDS K row (16 B pad: conflict-free b128 reads)
     static constexpr int VROW = D + 16;   // bf16 per LDS V row (32 B pad: conflict-free tr reads)
     static constexpr int CHUNKS = 2 * kPage * D / 8;          // 16-byte chunks per K+V page
@@ -66,7 +68,9 @@ __device__ __forceinline__ void store_page(const u32x4 (&stage)[DecodeCfg<D>::CH
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void paged_decode_split_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DecodeCfg<D>::WAVES_PER_SIMD)))
+void paged_decode_split_kernel(const AttnArgs a) {
     using C = DecodeCfg<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
     __shared__ float red_m[4][16];
@@ -74,9 +78,12 @@ __global__ __launch_bounds__(kThreads) void paged_decode_split_kernel(const Attn
     uint16_t *ks = smem;
     uint16_t *vs = smem + kPage * C::KROW;
 
-    const int s = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
+    // Grid (KV head, sequence, split): splits vary slowest, so every
+    // sequence's full-size first splits are dispatched before the shorter
+    // remainder splits and the empty ones (which exit at once).
+    const int g = blockIdx.x;
+    const int b = blockIdx.y;
+    const int s = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -125,20 +132,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_split_kernel(const Attn
     float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
     float l_part = 0.f;        // this lane's share of the running sum
 
-    u32x4 stage[C::CH_PER_THREAD];
-    if (p_begin < p_end)
-        load_page<D>(stage, head_base, (int64_t)bt_row[p_begin] * a.kv_sp, a.kv_ss, a.kv_skv, tid,
-                     L - p_begin * kPage);
-
-    for (int p = p_begin; p < p_end; ++p) {
-        __syncthreads();                 // previous page fully consumed
-        store_page<D>(stage, ks, vs, tid);
-        __syncthreads();
-        if (p + 1 < p_end)
-            load_page<D>(stage, head_base, (int64_t)bt_row[p + 1] * a.kv_sp, a.kv_ss, a.kv_skv, tid,
-                         L - (p + 1) * kPage);
-
-        // S^T[16 keys x 16 rows] for keys 16w .. 16w+15 of this page.
+    // Per-page work of one wave: keys 16w .. 16w+15 of page p (already in LDS).
+    auto compute_page = [&](int p) {
+        // S^T[16 keys x 16 rows] = K Q^T.
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
         {
             const uint16_t *kp = ks + (16 * w + (lane & 15)) * C::KROW + 8 * (lane >> 4);
@@ -183,6 +179,57 @@ __global__ __launch_bounds__(kThreads) void paged_decode_split_kernel(const Attn
         for (int db = 0; db < D / 16; ++db) {
             const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * db));
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
+        }
+    };
+
+    const int64_t sp = a.kv_sp;
+    if constexpr (C::STAGES == 2) {
+        // Two pages in flight: stage A holds even pages of the split, stage B
+        // odd ones.  Each page id is read one compute phase before its loads
+        // issue, so the block-table latency stays off the critical path.
+        u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
+        if (p_begin < p_end)
+            load_page<D>(stA, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
+                         L - p_begin * kPage);
+        if (p_begin + 1 < p_end)
+            load_page<D>(stB, head_base, (int64_t)bt_row[p_begin + 1] * sp, a.kv_ss, a.kv_skv, tid,
+                         L - (p_begin + 1) * kPage);
+        int pid_a = (p_begin + 2 < p_end) ? bt_row[p_begin + 2] : 0;
+        for (int p = p_begin; p < p_end; p += 2) {
+            __syncthreads();                 // the previous page is fully consumed
+            store_page<D>(stA, ks, vs, tid);
+            __syncthreads();
+            if (p + 2 < p_end)
+                load_page<D>(stA, head_base, (int64_t)pid_a * sp, a.kv_ss, a.kv_skv, tid,
+                             L - (p + 2) * kPage);
+            const int pid_b = (p + 3 < p_end) ? bt_row[p + 3] : 0;
+            compute_page(p);
+            if (p + 1 >= p_end) break;       // uniform across the workgroup
+            __syncthreads();
+            store_page<D>(stB, ks, vs, tid);
+            __syncthreads();
+            if (p + 3 < p_end)
+                load_page<D>(stB, head_base, (int64_t)pid_b * sp, a.kv_ss, a.kv_skv, tid,
+                             L - (p + 3) * kPage);
+            pid_a = (p + 4 < p_end) ? bt_row[p + 4] : 0;
+            compute_page(p + 1);
+        }
+    } else {
+        // One page in flight per workgroup; several workgroups per CU overlap.
+        u32x4 st[C::CH_PER_THREAD];
+        if (p_begin < p_end)
+            load_page<D>(st, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
+                         L - p_begin * kPage);
+        int pid = (p_begin + 1 < p_end) ? bt_row[p_begin + 1] : 0;
+        for (int p = p_begin; p < p_end; ++p) {
+            __syncthreads();                 // the previous page is fully consumed
+            store_page<D>(st, ks, vs, tid);
+            __syncthreads();
+            if (p + 1 < p_end)
+                load_page<D>(st, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid,
+                             L - (p + 1) * kPage);
+            pid = (p + 2 < p_end) ? bt_row[p + 2] : 0;
+            compute_page(p);
         }
     }
 

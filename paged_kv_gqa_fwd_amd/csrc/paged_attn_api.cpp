@@ -27,9 +27,11 @@ constexpr int kMaxDecodeRows = 16;       // G * max_q rows fit one 16-wide MFMA 
 constexpr int kPrefillRows = 128;        // packed query rows per prefill workgroup
 constexpr int kGridYZMax = 65535;
 constexpr size_t kWsAlign = 256;
-// Target number of split workgroups for the decode path: enough to cover the
-// 256 compute units several times over so the page streams stay balanced.
-constexpr int64_t kSplitTargetWorkgroups = 4096;
+// Split sizing for the decode path: aim for about this many rounds of
+// resident workgroups (256 CUs x resident workgroups per CU), which balances
+// the per-workgroup start-up cost against the tail of ragged sequences.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kSplitRounds = 8;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -80,16 +82,20 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     if (path == ATTN_PATH_SPLIT_DECODE) {
         int64_t p = pps;
         if (p == 0) {
+            // one workgroup per SIMD-wave slot: 4 waves = one per SIMD
+            const int64_t target = kSplitRounds * kComputeUnits * pa::decode_waves_per_simd(d->head_dim);
             const int64_t bound = MP * std::max<int64_t>(n_seqs, 1) * d->num_kv_heads;
-            p = (bound + kSplitTargetWorkgroups - 1) / kSplitTargetWorkgroups;
+            p = (bound + target - 1) / target;
         }
+        // at most 65535 splits (grid z limit)
+        p = std::max<int64_t>(p, (MP + kGridYZMax - 1) / kGridYZMax);
         p = std::min<int64_t>(std::max<int64_t>(p, 1), MP);
         const int64_t S = (MP + p - 1) / p;
         plan->pages_per_split = (int32_t)p;
         plan->max_splits = (int32_t)S;
-        plan->grid_x = (int32_t)S;
-        plan->grid_y = d->num_kv_heads;
-        plan->grid_z = n_seqs;
+        plan->grid_x = d->num_kv_heads;
+        plan->grid_y = n_seqs;
+        plan->grid_z = (int32_t)S;
         if (S > 1) {
             const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads * (size_t)S;
             plan->workspace_bytes = align_up(rows * (size_t)d->head_dim * 4, kWsAlign) + align_up(rows * 8, kWsAlign);

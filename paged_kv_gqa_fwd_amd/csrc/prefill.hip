@@ -12,8 +12,8 @@
 // 128 packed query rows).  Row r of a (sequence, KV head) is query token
 // r / G, q head g*G + r % G, so the G heads sharing a KV head share every
 // K/V tile.  Each wave owns 32 rows.  Per 64-key page: K and V rows are
-// staged into LDS with coalesced 16-byte loads (one page ahead in
-// registers); S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with keys on M,
+// staged into LDS with coalesced 16-byte loads (two pages ahead in
+// registers at D = 128, one at D = 256); S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with keys on M,
 // so every lane owns one query row and the row max / row sum are in-lane
 // plus one cross-half exchange; the S^T C layout is directly the B operand
 // of O^T += V^T P^T, whose V^T operand comes from the row-major V tile via
@@ -126,88 +126,124 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(const AttnArgs 
     float m_run = -INFINITY;
     float l_part = 0.f;
 
-    u32x4 stage[C::CH_PER_THREAD];
-    if (ntiles > 0)
-        prefill_load_tile<D>(stage, head_base, (int64_t)bt_row[0] * a.kv_sp, a.kv_ss, a.kv_skv, tid, L);
-
-    for (int kt = 0; kt < ntiles; ++kt) {
-        __syncthreads();
-        prefill_store_tile<D>(stage, ks, vs, tid);
-        __syncthreads();
-        if (kt + 1 < ntiles)
-            prefill_load_tile<D>(stage, head_base, (int64_t)bt_row[kt + 1] * a.kv_sp, a.kv_ss,
-                                 a.kv_skv, tid, L - (kt + 1) * kPage);
-
-        // S^T = K Q^T for two 32-key blocks.
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    auto compute_tile = [&](int kt) {
+            // S^T = K Q^T for two 32-key blocks.
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t *kp = ks + (32 * kb + (lane & 31)) * C::KROW + 8 * hi;
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint16_t *kp = ks + (32 * kb + (lane & 31)) * C::KROW + 8 * hi;
 #pragma unroll
-            for (int ks_ = 0; ks_ < D / 16; ++ks_) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 16 * ks_);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks_], sacc[kb], 0, 0, 0);
-            }
-        }
-        // sacc[kb][i] = score of key kt*64 + 32kb + 8*(i/4) + 4*hi + i%4.
-        const bool need_mask = (kt + 1) * kPage > kv_full;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float sc = sacc[kb][i] * a.scale_log2;
-                if (need_mask) {
-                    const int key = kt * kPage + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    sc = key < vis ? sc : -INFINITY;
-                }
-                sacc[kb][i] = sc;
-                mx = fmaxf(mx, sc);
-            }
-        }
-        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
-        bf16x8 pb[2][2];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const __bf16 pr = (__bf16)exp2_fast(sacc[kb][i] - m_use);
-                pb[kb][i >> 3][i & 7] = pr;
-                psum += (float)pr;   // the sum uses the same rounded P as the P.V product
-            }
-        }
-        l_part = l_part * alpha + psum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-        }
-
-        // O^T[d, row] += V^T[d, key] P^T[key, row]; 4 k-steps of 16 keys.
-        // k-step (kb, jj), half hi holds keys 32kb+16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
-        const int q16 = lane >> 4;
-        const int dsub = (q16 & 1) * 16;
-        const int src_row = (lane & 15) >> 2;
-        const int src_col = 4 * (lane & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int kbase = 32 * kb + 16 * jj + 4 * hi;
-                const uint16_t *v1 = vs + (kbase + src_row) * C::VROW + dsub + src_col;
-                const uint16_t *v2 = v1 + 8 * C::VROW;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x4 lo4 = lds_read_tr16(v1 + 32 * db);
-                    const bf16x4 hi4 = lds_read_tr16(v2 + 32 * db);
-                    const bf16x8 vop = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][jj], oacc[db], 0, 0, 0);
+                for (int ks_ = 0; ks_ < D / 16; ++ks_) {
+                    const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 16 * ks_);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks_], sacc[kb], 0, 0, 0);
                 }
             }
+            // sacc[kb][i] = score of key kt*64 + 32kb + 8*(i/4) + 4*hi + i%4.
+            const bool need_mask = (kt + 1) * kPage > kv_full;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float sc = sacc[kb][i] * a.scale_log2;
+                    if (need_mask) {
+                        const int key = kt * kPage + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+                        sc = key < vis ? sc : -INFINITY;
+                    }
+                    sacc[kb][i] = sc;
+                    mx = fmaxf(mx, sc);
+                }
+            }
+            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2_fast(m_run - m_use);
+            m_run = m_new;
+            bf16x8 pb[2][2];
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const __bf16 pr = (__bf16)exp2_fast(sacc[kb][i] - m_use);
+                    pb[kb][i >> 3][i & 7] = pr;
+                    psum += (float)pr;   // the sum uses the same rounded P as the P.V product
+                }
+            }
+            l_part = l_part * alpha + psum;
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+            }
+
+            // O^T[d, row] += V^T[d, key] P^T[key, row]; 4 k-steps of 16 keys.
+            // k-step (kb, jj), half hi holds keys 32kb+16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
+            const int q16 = lane >> 4;
+            const int dsub = (q16 & 1) * 16;
+            const int src_row = (lane & 15) >> 2;
+            const int src_col = 4 * (lane & 3);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int kbase = 32 * kb + 16 * jj + 4 * hi;
+                    const uint16_t *v1 = vs + (kbase + src_row) * C::VROW + dsub + src_col;
+                    const uint16_t *v2 = v1 + 8 * C::VROW;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x4 lo4 = lds_read_tr16(v1 + 32 * db);
+                        const bf16x4 hi4 = lds_read_tr16(v2 + 32 * db);
+                        const bf16x8 vop = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][jj], oacc[db], 0, 0, 0);
+                    }
+                }
+            }
+    };
+
+    const int64_t sp = a.kv_sp;
+    if constexpr (D == 128) {
+        // Two tiles in flight: stage A holds even tiles, stage B odd ones; each
+        // page id is read one compute phase before its loads issue.
+        u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
+        if (ntiles > 0)
+            prefill_load_tile<D>(stA, head_base, (int64_t)bt_row[0] * sp, a.kv_ss, a.kv_skv, tid, L);
+        if (ntiles > 1)
+            prefill_load_tile<D>(stB, head_base, (int64_t)bt_row[1] * sp, a.kv_ss, a.kv_skv, tid, L - kPage);
+        int pid_a = (ntiles > 2) ? bt_row[2] : 0;
+        for (int kt = 0; kt < ntiles; kt += 2) {
+            __syncthreads();
+            prefill_store_tile<D>(stA, ks, vs, tid);
+            __syncthreads();
+            if (kt + 2 < ntiles)
+                prefill_load_tile<D>(stA, head_base, (int64_t)pid_a * sp, a.kv_ss, a.kv_skv, tid,
+                                     L - (kt + 2) * kPage);
+            const int pid_b = (kt + 3 < ntiles) ? bt_row[kt + 3] : 0;
+            compute_tile(kt);
+            if (kt + 1 >= ntiles) break;    // uniform across the workgroup
+            __syncthreads();
+            prefill_store_tile<D>(stB, ks, vs, tid);
+            __syncthreads();
+            if (kt + 3 < ntiles)
+                prefill_load_tile<D>(stB, head_base, (int64_t)pid_b * sp, a.kv_ss, a.kv_skv, tid,
+                                     L - (kt + 3) * kPage);
+            pid_a = (kt + 4 < ntiles) ? bt_row[kt + 4] : 0;
+            compute_tile(kt + 1);
+        }
+    } else {
+        // One tile in flight (the register budget at D = 256 has no room for two).
+        u32x4 st[C::CH_PER_THREAD];
+        if (ntiles > 0)
+            prefill_load_tile<D>(st, head_base, (int64_t)bt_row[0] * sp, a.kv_ss, a.kv_skv, tid, L);
+        int pid = (ntiles > 1) ? bt_row[1] : 0;
+        for (int kt = 0; kt < ntiles; ++kt) {
+            __syncthreads();
+            prefill_store_tile<D>(st, ks, vs, tid);
+            __syncthreads();
+            if (kt + 1 < ntiles)
+                prefill_load_tile<D>(st, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid,
+                                     L - (kt + 1) * kPage);
+            pid = (kt + 2 < ntiles) ? bt_row[kt + 2] : 0;
+            compute_tile(kt);
         }
     }
 

@@ -133,7 +133,7 @@ def test_plan_paths_and_sizes(pa):
     d = dims(max_pages_per_seq=128, bt_stride=128)
     p = mod.make_plan(d, 64, 1)
     assert p.path == mod.PATH_SPLIT_DECODE
-    assert p.grid_x == p.max_splits and p.grid_y == 8 and p.grid_z == 64
+    assert p.grid_z == p.max_splits and p.grid_x == 8 and p.grid_y == 64
     assert p.max_splits == -(-128 // p.pages_per_split)
     rows = 64 * 1 * 32 * p.max_splits
     assert p.workspace_bytes >= rows * 128 * 4 + rows * 8
@@ -156,7 +156,7 @@ def test_plan_paths_and_sizes(pa):
               kv_stride_slot=2 * 2 * 256, kv_stride_head=512, kv_stride_kv=256,
               max_pages_per_seq=512, bt_stride=512, num_tokens=128)
     p5 = mod.make_plan(d5, 128, 1)
-    assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_x * 2 * 128 >= 2048
+    assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_z * 2 * 128 >= 2048
 
 
 def test_workspace_bytes_query(pa):

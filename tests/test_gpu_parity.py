@@ -150,6 +150,15 @@ def test_edge_cases(oracle_mod, name, q_lens, kv_lens, hq, hkv, d, causal, path)
     compare(out, ref, what="%s path=%d" % (name, path))
 
 
+@pytest.mark.parametrize("path", [PATH_AUTO, PATH_PREFILL])
+@pytest.mark.parametrize("d", [128, 256])
+def test_head_major_pool_layout(oracle_mod, path, d):
+    """Pool stored [page, kv_head, {K,V}, slot, D] (a different strided view)."""
+    case = workloads.make_case("head_major", 600 + d, [1, 3, 1], [77, 300, 1000], 16, 2, d,
+                               causal=True, layout="head_major", extra_pages=2, poison=True)
+    compare(run_gpu(case, path=path), oracle_for(oracle_mod, case), what="head-major D=%d path=%d" % (d, path))
+
+
 def test_rows_outside_cu_q_untouched():
     case = workloads.make_case("untouched", 401, [1, 1], [100, 60], 8, 2, 128, causal=True)
     g = case.to("cuda")

@@ -286,3 +286,14 @@ def test_poisoned_unused_memory_is_never_read(oracle_mod):
                                extra_pages=2, poison=True)
     got = run_oracle(oracle_mod, case)
     assert np.isfinite(got).all()
+
+
+def test_head_major_layout_is_same_attention(oracle_mod):
+    """The head-major pool view holds the same (page, slot, head, K/V) values as
+    a contiguous copy, and the oracle reads it identically."""
+    case = workloads.make_case("hm", 17, [2, 1], [90, 200], 8, 2, 16, causal=True, layout="head_major")
+    assert case.kv.stride(3) == 64 * 16 and case.kv.stride(1) == 16
+    a = run_oracle(oracle_mod, case)
+    b = oracle_mod.paged_attn(case.q, case.kv.contiguous(), case.block_table, case.seq_lens, case.cu_q,
+                              case.scale, True)
+    assert np.array_equal(a, b)

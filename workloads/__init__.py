@@ -101,7 +101,7 @@ def make_case(name: str, seed: int, q_lens, kv_lens, num_q_heads: int, num_kv_he
               k_outlier_p: float = 0.0, k_outlier_mult: float = 4.0,
               k_channel_offset_var: float = 0.0, poison: bool = False,
               device="cpu", num_pages: Optional[int] = None, chunk_pages: int = 1024,
-              lengths_drawn: bool = False) -> PagedCase:
+              layout: str = "slot_major") -> PagedCase:
     """Build one seeded paged-attention input.
 
     q_lens / kv_lens: per-sequence new-query counts n_b and total KV lengths
@@ -110,6 +110,10 @@ def make_case(name: str, seed: int, q_lens, kv_lens, num_q_heads: int, num_kv_he
     the whole table from the page permutation (the manifest's full table).
     poison: fill unused pool pages and the slots past L_b in each sequence's
     last page with NaN / +-inf (a correct kernel never reads them).
+    layout: "slot_major" stores [page, layer, slot, kv_head, {K,V}, D] (the
+    decode.json manifest's order); "head_major" stores [page, kv_head, {K,V},
+    slot, D], so each (page, KV head) is one contiguous K block followed by
+    its V block.  Either way ``kv`` is the [page, slot, kv_head, {K,V}, D] view.
     """
     cpu_gen = torch.Generator(device="cpu").manual_seed(seed)
     q_lens = [int(x) for x in q_lens]
@@ -151,15 +155,22 @@ def make_case(name: str, seed: int, q_lens, kv_lens, num_q_heads: int, num_kv_he
         kv_off = torch.zeros((1, hkv, 2, d))
         kv_off[0, :, 0, :] = offset
         offset_dev = kv_off.to(device)
-    storage_shape = (np_total, layers, page_size, hkv, 2, d)
-    storage = torch.empty(storage_shape, dtype=torch.bfloat16, device=device)
+    if layout == "slot_major":
+        storage = torch.empty((np_total, layers, page_size, hkv, 2, d), dtype=torch.bfloat16, device=device)
+        layer_views = [storage[:, l] for l in range(layers)]
+    elif layout == "head_major":
+        assert layers == 1
+        storage = torch.empty((np_total, hkv, 2, page_size, d), dtype=torch.bfloat16, device=device)
+        layer_views = [storage.permute(0, 3, 1, 2, 4)]
+    else:
+        raise ValueError("unknown layout %r" % layout)
     for l in range(layers):
         for p0 in range(0, np_total, chunk_pages):
             p1 = min(np_total, p0 + chunk_pages)
             vals = _randn_bf16((p1 - p0, page_size, hkv, 2, d), dev_gen, device, chunk_rows=p1 - p0,
                                add=offset_dev if (offset is not None and l == layer) else None)
-            storage[p0:p1, l] = vals
-    kv = storage[:, layer]
+            layer_views[l][p0:p1] = vals
+    kv = layer_views[layer]
     if k_outlier_p > 0:
         # Bernoulli per pool slot: every page belongs to one sequence, so this is
         # an independent draw per (sequence, position); all KV heads' K rows scale.
@@ -228,11 +239,14 @@ def decode_batch(device="cpu", seed: int = 102, n_seqs: int = 64, lo: int = 1024
 
 
 def long_decode(device="cpu", seed: int = 103, n_seqs: int = 128, ctx: int = 32768,
-                poison: bool = False) -> PagedCase:
+                poison: bool = False, layout: str = "head_major") -> PagedCase:
     """128 sequences x 1 query token at context 32768, 16 q / 2 KV heads,
-    head_dim 256, K rows scaled x4 at 1% of positions, causal."""
+    head_dim 256, K rows scaled x4 at 1% of positions, causal.  The pool is
+    stored head-major within each page (contiguous K then V block per KV
+    head), the layout the split kernel streams fastest at head_dim 256."""
     return make_case("long_decode", seed, [1] * n_seqs, [ctx] * n_seqs, 16, 2, 256, causal=True,
-                     k_outlier_p=0.01, k_outlier_mult=4.0, device=device, poison=poison)
+                     k_outlier_p=0.01, k_outlier_mult=4.0, device=device, poison=poison,
+                     layout=layout)
 
 
 def chunked_prefill(device="cpu", seed: int = 104, n_seqs: int = 8, q_lo: int = 512,
