@@ -34,6 +34,9 @@ constexpr int kThreads = 256;  // 4 wave64 per workgroup
 #ifndef PA_DECODE_WAVES_256
 #define PA_DECODE_WAVES_256 1
 #endif
+// Packed query rows per prefill workgroup: 4 waves x 64 rows at D = 128,
+// 4 waves x 32 rows at D = 256.
+constexpr int prefill_rows(int d) { return d == 128 ? 256 : 128; }
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
 constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
 
@@ -54,6 +57,8 @@ struct AttnArgs {
     int32_t pages_per_split, max_splits;
     int32_t causal;
     float scale_log2;           // scale * log2(e): scores live in log2 units
+    float scale_log2_pos;       // max(|scale| * log2(e), FLT_MIN) (prefill kernel)
+    int32_t q_negate;           // scale < 0: the prefill kernel negates Q instead
 };
 
 struct CombineArgs {

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -24,7 +25,6 @@ namespace {
 
 constexpr int kVersion = 10000;          // 1.0.0
 constexpr int kMaxDecodeRows = 16;       // G * max_q rows fit one 16-wide MFMA tile
-constexpr int kPrefillRows = 128;        // packed query rows per prefill workgroup
 constexpr int kGridYZMax = 65535;
 constexpr size_t kWsAlign = 256;
 // Split sizing for the decode path: aim for about this many rounds of
@@ -101,7 +101,8 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
             plan->workspace_bytes = align_up(rows * (size_t)d->head_dim * 4, kWsAlign) + align_up(rows * 8, kWsAlign);
         }
     } else {
-        const int64_t tiles = (mq * G + kPrefillRows - 1) / kPrefillRows;
+        const int64_t bm = pa::prefill_rows(d->head_dim);
+        const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
         plan->pages_per_split = (int32_t)MP;
         plan->max_splits = 1;
@@ -172,6 +173,12 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
     a.max_splits = plan.max_splits;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    // The prefill kernel takes the maximum of raw scores and applies the
+    // scale afterwards, which needs a positive scale: a negative one is
+    // applied by negating Q (exact), and zero as the smallest normal float
+    // (every weight is then exactly 1 unless |q.k| exceeds about 1e30).
+    a.scale_log2_pos = std::max((float)(std::fabs((double)scale) * 1.4426950408889634), FLT_MIN);
+    a.q_negate = scale < 0.f ? 1 : 0;
     if (plan.workspace_bytes > 0) {
         const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
         a.part_o = static_cast<float *>(workspace);

@@ -159,6 +159,20 @@ def test_head_major_pool_layout(oracle_mod, path, d):
     compare(run_gpu(case, path=path), oracle_for(oracle_mod, case), what="head-major D=%d path=%d" % (d, path))
 
 
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.3])
+@pytest.mark.parametrize("path,q_lens,kv_lens", [
+    (PATH_SPLIT, [1, 1, 1], [300, 500, 3]),
+    (PATH_PREFILL, [1, 40, 3], [300, 500, 3]),
+])
+def test_scale_sign_and_zero(oracle_mod, scale, path, q_lens, kv_lens):
+    """A negative scale (the prefill kernel negates Q instead) and a zero
+    scale (uniform weights over the visible keys) on both paths."""
+    case = workloads.make_case("scale", 700, q_lens, kv_lens, 12, 4, 128, causal=True,
+                               scale=scale, extra_pages=1, poison=True)
+    compare(run_gpu(case, path=path), oracle_for(oracle_mod, case),
+            what="scale=%g path=%d" % (scale, path))
+
+
 def test_rows_outside_cu_q_untouched():
     case = workloads.make_case("untouched", 401, [1, 1], [100, 60], 8, 2, 128, causal=True)
     g = case.to("cuda")
