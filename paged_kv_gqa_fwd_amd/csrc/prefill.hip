@@ -16,11 +16,14 @@
 //    V operand read from LDS feeds two MFMAs: 64 FLOP per LDS byte, half of
 //    the LDS bandwidth the MFMA rate needs with 32 rows per wave.
 //  * K/V pages (64 keys) stream HBM -> LDS with direct 16-byte loads
-//    (global_load_lds_dwordx4), no register staging, through a ring of
-//    STAGES page buffers (3 at D = 128, 2 at D = 256).  Rows are stored with
-//    an XOR swizzle of their 16-byte chunks (chunk c of key k at c ^ 2(k&7))
-//    so both the b128 K reads and the transposing V reads are bank-conflict
-//    free without padding.
+//    (global_load_lds_dwordx4), no register staging, through rings of K and
+//    V page buffers with one or two pages in flight beyond the next one.
+//    Rows are stored with an XOR swizzle of their 16-byte chunks (chunk c of
+//    key k at c ^ 2(k&7)) so both the b128 K reads and the transposing V
+//    reads are bank-conflict free without padding.
+//  * The 32-key steps are software pipelined: the P.V MFMAs of step j-1
+//    run while the VALU takes the row max of step j, and the Q.K MFMAs of
+//    step j+1 run while the VALU exponentiates step j.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with keys on M: each lane owns
 //    one query row per block, so row max / row sum are in-lane plus one
 //    permlane32 swap.  The S^T C layout is directly the B operand of
@@ -30,9 +33,8 @@
 //    reference only moves (and O, l are rescaled) when a row's max exceeds
 //    it by more than 2^8, so P <= 256 and rescales are rare.  The result is
 //    the same softmax; only the common factor cancelled at the end differs.
-//  * Tiles past the causal frontier of the workgroup's last row are never
-//    loaded; a wave skips the tiles past its own rows' frontier; tiles below
-//    the first row's frontier skip the mask.
+//  * Keys past the causal frontier of the workgroup's last row are never
+//    loaded; steps below the frontier of a wave's first row skip the mask.
 #include "attn_device.h"
 
 namespace pa {
@@ -42,15 +44,18 @@ struct PfCfg {
     static constexpr int WAVES = 4;
     // 32-row MFMA blocks per wave: two at D = 128 (every LDS operand feeds
     // two MFMAs); one at D = 256, where two blocks' Q and O would not fit
-    // the 512 registers of a lane.
+    // the registers of a lane.
     static constexpr int RB = D == 128 ? 2 : 1;
     static constexpr int BM = WAVES * RB * 32;      // packed query rows per workgroup
     static constexpr int CH = D / 8;                // 16-byte chunks per K or V row
-    static constexpr int STAGES = D == 128 ? 3 : 2;
-    static constexpr int TILE = kPage * D;          // bf16 elements of one K (or V) page tile
-    static constexpr int KSTEP = 32;                // keys per softmax step
-    static constexpr int KB = KSTEP / 32;           // 32-key MFMA blocks per softmax step
-    static constexpr int LOADS = kPage * CH / kThreads;  // 16-byte loads per thread per K tile
+    static constexpr int TILE = kPage * D;          // bf16 elements of one K (or V) page
+    static constexpr int LOADS = kPage * CH / kThreads;  // 16-byte loads per thread per K page
+    // Pages in flight beyond the next one, and the K / V ring depths that
+    // allow it with the step pipeline below (K of page t+1 and V of page t
+    // are read in the same step).
+    static constexpr int LEAD = D == 128 ? 2 : 1;
+    static constexpr int NK = LEAD + 1;
+    static constexpr int NV = LEAD + 2;
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
@@ -115,13 +120,8 @@ __device__ __forceinline__ int load_page_id(const int32_t *bt_row, int j) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnArgs a) {
     using C = PfCfg<D>;
-    // One LDS object per ring stage.
-    constexpr int T2 = C::STAGES > 2 ? C::TILE : 8;
-    __shared__ __attribute__((aligned(1024))) uint16_t sk0[C::TILE], sv0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sk1[C::TILE], sv1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sk2[T2], sv2[T2];
-    auto kbuf = [&](int st) -> uint16_t * { return st == 0 ? sk0 : (st == 1 ? sk1 : sk2); };
-    auto vbuf = [&](int st) -> uint16_t * { return st == 0 ? sv0 : (st == 1 ? sv1 : sv2); };
+    __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TILE];
 
     const int g = blockIdx.y;
     const int b = blockIdx.z;
@@ -155,14 +155,37 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     }
     const int r_last = min(R, r0 + C::BM) - 1;
     const int kv_end = visible_keys(L, n, r_last / G, a.causal);   // max over the workgroup's rows
-    const int ntiles = (kv_end + kPage - 1) / kPage;
-    // this wave's own frontier: keys past it are masked for all its rows
-    const int wr_last = min(R, r0 + 32 * C::RB * (w + 1)) - 1;
-    const int w_end = (r0 + 32 * C::RB * w < R) ? visible_keys(L, n, wr_last / G, a.causal) : 0;
+    // keys below this wave's first row's frontier are visible to all its rows
     const int w_full = visible_keys(L, n, min(R - 1, r0 + 32 * C::RB * w) / G, a.causal);
+    const int nsteps = (kv_end + 31) / 32;     // 32-key softmax steps
+    const int ntiles = (nsteps + 1) / 2;       // 64-key pages
 
     const uint16_t *head_base = a.kv + (int64_t)g * a.kv_sh;
     const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
+
+    // Q^T as the B operand of v_mfma_f32_32x32x16_bf16: lane holds
+    // q[row, 16*ks + 8*hi .. +7]; a negative scale is applied by negating Q
+    // (exact in bf16) so the kernel's scale is always positive.  Issued
+    // before the page loads so that waiting for page 0 also covers Q.
+    bf16x8 qreg[C::RB][D / 16];
+    {
+        const uint32_t qflip = a.q_negate ? 0x80008000u : 0u;
+        u32x4 qraw[C::RB][D / 16];
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+            const int qrow = row_ok[rb] ? qi_[rb] : 0;   // rows past the end read token 0
+            const uint16_t *qp = a.q + (int64_t)(q0 + qrow) * a.q_st + (int64_t)h_[rb] * a.q_sh + 8 * hi;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) qraw[rb][ks] = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
+        }
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+            const uint32_t keep = row_ok[rb] ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                qreg[rb][ks] = __builtin_bit_cast(bf16x8, (qraw[rb][ks] ^ qflip) & keep);
+        }
+    }
 
     // This thread's page-relative load offsets (fixed for every page).
     uint32_t ld_off[C::LOADS], ld_off0[C::LOADS];
@@ -175,33 +198,30 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
         ld_off[i] = (uint32_t)(ld_key[i] * a.kv_ss + c * 8) * 2u;
         ld_off0[i] = (uint32_t)(c * 8) * 2u;
     }
-    auto issue_page = [&](int j, int st) {
-        const int pid = load_page_id(bt_row, j);
-        pf_load_page<D>(kbuf(st), vbuf(st), head_base + (int64_t)pid * a.kv_sp, ld_off, ld_off0, ld_key,
-                        a.kv_skv, w, L - j * kPage);
+    auto issue_page = [&](int t) {
+        const int pid = load_page_id(bt_row, t);
+        pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, ld_off,
+                        ld_off0, ld_key, a.kv_skv, w, L - t * kPage);
+    };
+    // Wait until page t has landed in LDS: pages t+1 .. `issued` were
+    // issued after it and may stay in flight (loads complete in issue order).
+    int issued = -1;
+    auto wait_page = [&](int t) {
+        const int younger = issued - t;
+        if (C::LEAD == 2 && younger == 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * C::LOADS) : "memory");
+        else if (younger >= 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
-    // Start the first pages streaming before anything else.
 #pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s)
-        if (s < ntiles) issue_page(s, s);
-
-    // Q^T as the B operand of v_mfma_f32_32x32x16_bf16: lane holds
-    // q[row, 16*ks + 8*hi .. +7]; a negative scale is applied by negating Q
-    // (exact in bf16) so the kernel's scale is always positive.
-    bf16x8 qreg[C::RB][D / 16];
-    const uint32_t qflip = a.q_negate ? 0x80008000u : 0u;
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-        const uint16_t *qp = a.q + (int64_t)(q0 + qi_[rb]) * a.q_st + (int64_t)h_[rb] * a.q_sh + 8 * hi;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok[rb]) v = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
-            v ^= qflip;
-            qreg[rb][ks] = __builtin_bit_cast(bf16x8, v);
+    for (int t = 0; t <= C::LEAD; ++t)
+        if (t < ntiles) {
+            issue_page(t);
+            issued = t;
         }
-    }
 
     f32x16 oacc[C::RB][D / 32];
 #pragma unroll
@@ -217,56 +237,81 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     const float sl2 = a.scale_log2_pos;   // > 0
 
     // Per-lane LDS offsets (elements) of the K operand (key = lane & 31 of a
-    // 32-key block, chunk 2 ks + hi, swizzled) and of the transposing V reads.
+    // 32-key step, chunk 2 ks + hi, swizzled) and of the transposing V reads.
     const int klane = (lane & 31) * D;
     const int kswz = 2 * (lane & 7);
     const int q16 = lane >> 4;
-    const int src_row = (lane & 15) >> 2;
-    const int vkey = 4 * hi + src_row;          // key within a 16-key step (plus 8 for the 2nd read)
+    const int vkey = 4 * hi + ((lane & 15) >> 2);   // key within a 16-key k-step (plus 8 for the 2nd read)
+    const int vlane = vkey * D + ((4 * (lane & 3)) & 7);
     const int vswz = 2 * (vkey & 7);
     const int vcol_chunk = 2 * (q16 & 1) + ((4 * (lane & 3)) >> 3);
-    const int vcol_in = (4 * (lane & 3)) & 7;
 
-    // One softmax step over KSTEP keys starting at key kbase (tile-relative
-    // offset koff) of the LDS tile (ks_t, vs_t).
-    auto step = [&](const uint16_t *ks_t, const uint16_t *vs_t, int koff, int kbase, bool need_mask) {
-        f32x16 sacc[C::RB][C::KB];
+    // S^T = K Q^T for the 32 keys of step j (raw scores, f32).
+    // s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4 for this lane's row of block rb.
+    auto qk = [&](int j, f32x16 (&s)[C::RB]) {
+        const uint16_t *kp = sk[(j >> 1) % C::NK] + (32 * (j & 1)) * D + klane;
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb)
+        for (int rb = 0; rb < C::RB; ++rb) s[rb] = f32x16{};
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) sacc[rb][kb] = f32x16{};
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const int pc = (2 * ks + hi) ^ kswz;
+            const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + pc * 8);
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            const uint16_t *kp = ks_t + (koff + 32 * kb) * D + klane;
+            for (int rb = 0; rb < C::RB; ++rb)
+                s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rb][ks], s[rb], 0, 0, 0);
+        }
+    };
+    // O^T[d, row] += V^T[d, key] P^T[key, row] over the 32 keys of step j.
+    // Half hi of k-step jj holds keys 32j + 16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
+    auto pv = [&](int j, const bf16x8 (&p)[C::RB][2]) {
+        const uint16_t *vt = sv[(j >> 1) % C::NV] + (32 * (j & 1)) * D + vlane;
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const int pc = (2 * ks + hi) ^ kswz;
-                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + pc * 8);
+        for (int jj = 0; jj < 2; ++jj) {
+            const uint16_t *v1 = vt + (16 * jj) * D;
+            const uint16_t *v2 = v1 + 8 * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int pc = (4 * db + vcol_chunk) ^ vswz;
+                const bf16x4 lo4 = lds_read_tr16(v1 + pc * 8);
+                const bf16x4 hi4 = lds_read_tr16(v2 + pc * 8);
+                const bf16x8 vop = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb)
-                    sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rb][ks], sacc[rb][kb], 0, 0, 0);
+                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[rb][jj], oacc[rb][db], 0, 0, 0);
             }
         }
-        // sacc[rb][kb][i] = raw score of key kbase + 32kb + 8(i/4) + 4hi + i%4.
-        bf16x8 pb[C::RB][C::KB][2];
-        float alpha[C::RB];
+    };
+
+    // Software pipeline over 32-key steps j (page t = j / 2):
+    //   A(j): O += P_{j-1} V_{j-1}   with the row max of S_j on the VALU
+    //   (rare) rescale of O and l when a row's reference max moves
+    //   B(j): S_{j+1} = K_{j+1} Q^T  with P_j = exp2(S_j - m) on the VALU
+    // One barrier per page, before B of its last step, publishes the next
+    // page and frees the K / V stages the next refill overwrites.
+    bf16x8 pb[C::RB][2];
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) pb[rb][0] = pb[rb][1] = bf16x8{};
+    // One pipelined step: scur holds S_j on entry; snext receives S_{j+1}.
+    auto step = [&](int j, f32x16 (&scur)[C::RB], f32x16 (&snext)[C::RB]) {
+        // ---- mask (diagonal and tail steps only)
+        if (32 * j + 32 > w_full) {
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 32 * j + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    scur[rb][i] = key < vis[rb] ? scur[rb][i] : -INFINITY;
+                }
+        }
+        // ---- A(j): at j = 0, P is zero and page 0's V (landed) is read
+        pv(j > 0 ? j - 1 : 0, pb);
+        float alpha[C::RB], m_use[C::RB];
         bool any_upd = false;
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) {
-            float mx = -INFINITY;
+            float mx = scur[rb][0];
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float sc = sacc[rb][kb][i];
-                    if (need_mask) {
-                        const int key = kbase + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                        sc = key < vis[rb] ? sc : -INFINITY;
-                        sacc[rb][kb][i] = sc;
-                    }
-                    mx = fmaxf(mx, sc);
-                }
-            }
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, scur[rb][i]);
             mx = max_xor32(mx);
             const float mt = mx * sl2;                 // -inf stays -inf (sl2 > 0)
             const bool upd = mt > m_ref[rb] + kRescaleThreshold;
@@ -274,91 +319,60 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
             alpha[rb] = upd ? exp2_fast(m_ref[rb] - m_new) : 1.f;
             any_upd |= upd;
             m_ref[rb] = m_new;
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = exp2_fast(fmaf(sacc[rb][kb][i], sl2, -m_use));
-                    const float p1 = exp2_fast(fmaf(sacc[rb][kb][i + 1], sl2, -m_use));
-                    pb[rb][kb][i >> 3][i & 7] = (__bf16)p0;
-                    pb[rb][kb][i >> 3][(i & 7) + 1] = (__bf16)p1;
-                }
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    // the row sum uses the same rounded P as the P.V product
-                    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const bf16x2 pp = {pb[rb][kb][jj][e], pb[rb][kb][jj][e + 1]};
-                        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
-                    }
-                }
-            }
-            l_part[rb] = l_part[rb] * alpha[rb] + psum;
+            m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
         }
+        // ---- rescale (rare: only when a row's max rose by more than 2^8)
         if (__any(any_upd)) {
 #pragma unroll
-            for (int rb = 0; rb < C::RB; ++rb)
+            for (int rb = 0; rb < C::RB; ++rb) {
+                l_part[rb] *= alpha[rb];
 #pragma unroll
                 for (int i = 0; i < D / 32; ++i) oacc[rb][i] *= alpha[rb];
-        }
-
-        // O^T[d, row] += V^T[d, key] P^T[key, row]; k-steps of 16 keys.
-        // Half hi of k-step (kb, jj) holds keys 32kb + 16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const uint16_t *v1 = vs_t + (koff + 32 * kb + 16 * jj + vkey) * D + vcol_in;
-                const uint16_t *v2 = v1 + 8 * D;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int pc = (4 * db + vcol_chunk) ^ vswz;
-                    const bf16x4 lo4 = lds_read_tr16(v1 + pc * 8);
-                    const bf16x4 hi4 = lds_read_tr16(v2 + pc * 8);
-                    const bf16x8 vop = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int rb = 0; rb < C::RB; ++rb)
-                        oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[rb][kb][jj], oacc[rb][db], 0, 0, 0);
-                }
             }
+        }
+        // ---- page boundary: publish page t+1, refill with page t+1+LEAD
+        const int t = j >> 1;
+        if ((j & 1) && t + 1 < ntiles) {
+            wait_page(t + 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            if (t + 1 + C::LEAD < ntiles) {
+                issue_page(t + 1 + C::LEAD);
+                issued = t + 1 + C::LEAD;
+            }
+        }
+        // ---- B(j): after the last step the product reads a stale stage
+        // (in bounds) and is discarded
+        qk(j + 1, snext);
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float p0 = exp2_fast(fmaf(scur[rb][i], sl2, -m_use[rb]));
+                const float p1 = exp2_fast(fmaf(scur[rb][i + 1], sl2, -m_use[rb]));
+                pb[rb][i >> 3][i & 7] = (__bf16)p0;
+                pb[rb][i >> 3][(i & 7) + 1] = (__bf16)p1;
+                // the row sum uses the same rounded P as the P.V product
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 pp = {pb[rb][i >> 3][i & 7], pb[rb][i >> 3][(i & 7) + 1]};
+                const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+                psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
+            }
+            l_part[rb] += psum;
         }
     };
 
-    auto tile_body = [&](int kt, int s) {
-        // Wait until this thread's loads of tile kt have landed (loads
-        // complete in issue order; the pages issued after it may stay in
-        // flight), then make the whole page visible to every wave.
-        if (C::STAGES == 3 && kt + 1 < ntiles)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        // Refill the stage freed by tile kt-1 with tile kt + STAGES - 1.
-        const int nt = kt + C::STAGES - 1;
-        if (nt < ntiles) issue_page(nt, (s + C::STAGES - 1) % C::STAGES);
-        const int k0 = kt * kPage;
-        if (k0 < w_end) {   // uniform per wave
-#pragma unroll
-            for (int kk = 0; kk < kPage; kk += C::KSTEP) {
-                const bool need_mask = k0 + kk + C::KSTEP > w_full;
-                step(kbuf(s), vbuf(s), kk, k0 + kk, need_mask);
-            }
-        }
-    };
-
-    int kt = 0;
-    for (; kt + C::STAGES <= ntiles; kt += C::STAGES) {
-#pragma unroll
-        for (int s = 0; s < C::STAGES; ++s) tile_body(kt + s, s);
+    wait_page(0);
+    __builtin_amdgcn_s_barrier();
+    f32x16 sA[C::RB], sB[C::RB];
+    qk(0, sA);
+    // Two steps per page; the S registers alternate roles between them.
+    for (int t = 0; t < ntiles; ++t) {
+        step(2 * t, sA, sB);
+        if (2 * t + 1 < nsteps) step(2 * t + 1, sB, sA);
     }
-#pragma unroll
-    for (int s = 0; s < C::STAGES; ++s)
-        if (kt + s < ntiles) tile_body(kt + s, s);
+    if (nsteps > 0) pv(nsteps - 1, pb);
 
     // Epilogue: out = O / l, rounded to bf16.  oacc[rb][db][i] holds
     // d = 32db + 8(i/4) + 4hi + i%4 of this lane's row in block rb.
