@@ -236,58 +236,68 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     }
     const float sl2 = a.scale_log2_pos;   // > 0
 
-    // Per-lane LDS offsets (elements) of the K operand (key = lane & 31 of a
-    // 32-key step, chunk 2 ks + hi, swizzled) and of the transposing V reads.
+    // Per-lane LDS element offsets.  K operand of a 32-key step: key
+    // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ 2(lane & 7).
+    // V operand (transposing reads): key vkey (+8), columns of chunk
+    // 4 db + vcol_chunk, physical chunk ^ 2(vkey & 7).
     const int klane = (lane & 31) * D;
     const int kswz = 2 * (lane & 7);
     const int q16 = lane >> 4;
-    const int vkey = 4 * hi + ((lane & 15) >> 2);   // key within a 16-key k-step (plus 8 for the 2nd read)
+    const int vkey = 4 * hi + ((lane & 15) >> 2);
     const int vlane = vkey * D + ((4 * (lane & 3)) & 7);
     const int vswz = 2 * (vkey & 7);
     const int vcol_chunk = 2 * (q16 & 1) + ((4 * (lane & 3)) >> 3);
 
-    // S^T = K Q^T for the 32 keys of step j (raw scores, f32).
-    // s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4 for this lane's row of block rb.
+    constexpr int NKS = D / 16;            // Q.K MFMA k-steps per 32-key step
+    constexpr int NPV = 2 * (D / 32);      // P.V (16-key half, 32-column block) pairs
+    constexpr int NEL = C::RB * 16;        // scores per lane per step
+    constexpr int EB = NEL / NKS;          // scores exponentiated per Q.K k-step
+    constexpr int EA = NEL / NPV;          // scores max-reduced per P.V pair
+    static_assert(EB * NKS == NEL && EA * NPV == NEL, "even split");
+
+    auto kread = [&](const uint16_t *kp, int ks) {
+        return *reinterpret_cast<const bf16x8 *>(kp + ((2 * ks + hi) ^ kswz) * 8);
+    };
+    auto vread = [&](const uint16_t *vt, int k) {
+        const int jj = k / (D / 32), db = k % (D / 32);
+        const uint16_t *v1 = vt + (16 * jj) * D + ((4 * db + vcol_chunk) ^ vswz) * 8;
+        const bf16x4 lo4 = lds_read_tr16(v1);
+        const bf16x4 hi4 = lds_read_tr16(v1 + 8 * D);
+        return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto kstage = [&](int j) { return sk[(j >> 1) % C::NK] + (32 * (j & 1)) * D + klane; };
+    auto vstage = [&](int j) { return sv[(j >> 1) % C::NV] + (32 * (j & 1)) * D + vlane; };
+
+    // S^T = K Q^T for the 32 keys of step j (raw scores, f32); no overlap
+    // (pipeline prologue).  s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4
+    // for this lane's row of block rb.
     auto qk = [&](int j, f32x16 (&s)[C::RB]) {
-        const uint16_t *kp = sk[(j >> 1) % C::NK] + (32 * (j & 1)) * D + klane;
+        const uint16_t *kp = kstage(j);
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) s[rb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const int pc = (2 * ks + hi) ^ kswz;
-            const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + pc * 8);
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 kop = kread(kp, ks);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
                 s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rb][ks], s[rb], 0, 0, 0);
         }
     };
-    // O^T[d, row] += V^T[d, key] P^T[key, row] over the 32 keys of step j.
-    // Half hi of k-step jj holds keys 32j + 16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
+    // O^T[d, row] += V^T[d, key] P^T[key, row] over the 32 keys of step j;
+    // no overlap (pipeline epilogue).  Half hi of k-step jj holds keys
+    // 32j + 16jj + {4hi..4hi+3, 8+4hi..8+4hi+3}.
     auto pv = [&](int j, const bf16x8 (&p)[C::RB][2]) {
-        const uint16_t *vt = sv[(j >> 1) % C::NV] + (32 * (j & 1)) * D + vlane;
+        const uint16_t *vt = vstage(j);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const uint16_t *v1 = vt + (16 * jj) * D;
-            const uint16_t *v2 = v1 + 8 * D;
+        for (int k = 0; k < NPV; ++k) {
+            const bf16x8 vop = vread(vt, k);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int pc = (4 * db + vcol_chunk) ^ vswz;
-                const bf16x4 lo4 = lds_read_tr16(v1 + pc * 8);
-                const bf16x4 hi4 = lds_read_tr16(v2 + pc * 8);
-                const bf16x8 vop = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int rb = 0; rb < C::RB; ++rb)
-                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[rb][jj], oacc[rb][db], 0, 0, 0);
-            }
+            for (int rb = 0; rb < C::RB; ++rb)
+                oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    vop, p[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
         }
     };
 
-    // Software pipeline over 32-key steps j (page t = j / 2):
-    //   A(j): O += P_{j-1} V_{j-1}   with the row max of S_j on the VALU
-    //   (rare) rescale of O and l when a row's reference max moves
-    //   B(j): S_{j+1} = K_{j+1} Q^T  with P_j = exp2(S_j - m) on the VALU
-    // One barrier per page, before B of its last step, publishes the next
-    // page and frees the K / V stages the next refill overwrites.
     bf16x8 pb[C::RB][2];
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) pb[rb][0] = pb[rb][1] = bf16x8{};
@@ -303,17 +313,35 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
                     scur[rb][i] = key < vis[rb] ? scur[rb][i] : -INFINITY;
                 }
         }
-        // ---- A(j): at j = 0, P is zero and page 0's V (landed) is read
-        pv(j > 0 ? j - 1 : 0, pb);
+        // ---- A(j): P_{j-1} V_{j-1} on the MFMA pipe, two V operands
+        // ahead, with the row max of S_j on the VALU.  At j = 0, P is zero
+        // and page 0's V (landed) is read.
+        float mx[C::RB];
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) mx[rb] = -INFINITY;
+        {
+            const uint16_t *vt = vstage(j > 0 ? j - 1 : 0);
+            bf16x8 vop[3];
+            vop[0] = vread(vt, 0);
+            vop[1] = vread(vt, 1);
+#pragma unroll
+            for (int k = 0; k < NPV; ++k) {
+                if (k + 2 < NPV) vop[(k + 2) % 3] = vread(vt, k + 2);
+#pragma unroll
+                for (int rb = 0; rb < C::RB; ++rb)
+                    oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vop[k % 3], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+#pragma unroll
+                for (int e = k * EA; e < (k + 1) * EA; ++e)
+                    mx[e / 16] = fmaxf(mx[e / 16], scur[e / 16][e % 16]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         float alpha[C::RB], m_use[C::RB];
         bool any_upd = false;
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) {
-            float mx = scur[rb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, scur[rb][i]);
-            mx = max_xor32(mx);
-            const float mt = mx * sl2;                 // -inf stays -inf (sl2 > 0)
+            const float mt = max_xor32(mx[rb]) * sl2;   // -inf stays -inf (sl2 > 0)
             const bool upd = mt > m_ref[rb] + kRescaleThreshold;
             const float m_new = upd ? mt : m_ref[rb];
             alpha[rb] = upd ? exp2_fast(m_ref[rb] - m_new) : 1.f;
@@ -341,25 +369,45 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
                 issued = t + 1 + C::LEAD;
             }
         }
-        // ---- B(j): after the last step the product reads a stale stage
-        // (in bounds) and is discarded
-        qk(j + 1, snext);
+        // ---- B(j): S_{j+1} = K_{j+1} Q^T on the MFMA pipe, two K operands
+        // ahead, with P_j = exp2(S_j scale - m) on the VALU.  After the last
+        // step the product reads a stale stage (in bounds) and is discarded.
+        {
+            const uint16_t *kp = kstage(j + 1);
+            bf16x8 kop[3];
+            kop[0] = kread(kp, 0);
+            kop[1] = kread(kp, 1);
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-            float psum = 0.f;
+            for (int rb = 0; rb < C::RB; ++rb) snext[rb] = f32x16{};
+            float pf[NEL];
+            float psum[C::RB];
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const float p0 = exp2_fast(fmaf(scur[rb][i], sl2, -m_use[rb]));
-                const float p1 = exp2_fast(fmaf(scur[rb][i + 1], sl2, -m_use[rb]));
-                pb[rb][i >> 3][i & 7] = (__bf16)p0;
-                pb[rb][i >> 3][(i & 7) + 1] = (__bf16)p1;
-                // the row sum uses the same rounded P as the P.V product
-                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                const bf16x2 pp = {pb[rb][i >> 3][i & 7], pb[rb][i >> 3][(i & 7) + 1]};
-                const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-                psum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum, false);
+            for (int rb = 0; rb < C::RB; ++rb) psum[rb] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (ks + 2 < NKS) kop[(ks + 2) % 3] = kread(kp, ks + 2);
+#pragma unroll
+                for (int rb = 0; rb < C::RB; ++rb)
+                    snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % 3], qreg[rb][ks], snext[rb], 0, 0, 0);
+#pragma unroll
+                for (int e = ks * EB; e < (ks + 1) * EB; ++e) {
+                    const int rb = e / 16, i = e % 16;
+                    pf[e] = exp2_fast(fmaf(scur[rb][i], sl2, -m_use[rb]));
+                    if (i & 1) {
+                        // round the pair to bf16; the row sum uses the same
+                        // rounded P as the P.V product
+                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                        const bf16x2 pp = {(__bf16)pf[e - 1], (__bf16)pf[e]};
+                        pb[rb][i >> 3][(i & 7) - 1] = pp[0];
+                        pb[rb][i >> 3][i & 7] = pp[1];
+                        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+                        psum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum[rb], false);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            l_part[rb] += psum;
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb) l_part[rb] += psum[rb];
         }
     };
 
