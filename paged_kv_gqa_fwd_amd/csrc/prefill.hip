@@ -18,9 +18,9 @@
 //  * K/V pages (64 keys) stream HBM -> LDS with direct 16-byte loads
 //    (global_load_lds_dwordx4), no register staging, through rings of K and
 //    V page buffers with one or two pages in flight beyond the next one.
-//    Rows are stored with an XOR swizzle of their 16-byte chunks (chunk c of
-//    key k at c ^ 2(k&7)) so both the b128 K reads and the transposing V
-//    reads are bank-conflict free without padding.
+//    Rows are stored with an XOR swizzle of their 16-byte chunks (K: chunk c
+//    of key k at c ^ (k&7); V: at c ^ 2(k&3)) so both the b128 K reads and
+//    the transposing V reads are bank-conflict free without padding.
 //  * The 32-key steps are software pipelined: the P.V MFMAs of step j-1
 //    run while the VALU takes the row max of step j, and the Q.K MFMAs of
 //    step j+1 run while the VALU exponentiates step j.
@@ -59,6 +59,10 @@ struct PfCfg {
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
+#ifndef PA_PREFILL_PREFETCH
+#define PA_PREFILL_PREFETCH 2
+#endif
+
 constexpr float kRescaleThreshold = 8.f;   // log2 units: P stays <= 256
 
 __device__ __forceinline__ float max_xor32(float x) {
@@ -88,25 +92,32 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t v
 
 // Direct HBM -> LDS loads of one page (K and V rows of one KV head).  LDS
 // position p = i*256 + tid of a tile holds key p / CH, physical chunk
-// p % CH, i.e. logical chunk (p % CH) ^ 2(key & 7).  `off[i]` is this
-// thread's byte offset of that chunk within a page; `off0[i]` the same
-// chunk of key 0.  Keys at or past `valid` re-read key 0 (always valid when
-// a page is loaded): their weight is exactly zero, but a poisoned
+// p % CH.  The 16-byte chunks of a row are permuted so that the operand
+// reads hit 32 distinct 4-byte banks per LDS cycle: K chunk c of key k is
+// stored at c ^ (k & 7) (eight keys per b128 read cycle), V chunk c at
+// c ^ 2(k & 3) (four keys x two chunks per transposing read cycle).
+// kof / vof hold this thread's byte offsets within a page, kof0 / vof0 the
+// same chunks of key 0.  Keys at or past `valid` re-read key 0 (always valid
+// when a page is loaded): their weight is exactly zero, but a poisoned
 // (non-finite) V row there would turn 0 * V into NaN.
 template <int D>
+struct PageLoad {
+    uint32_t kof[PfCfg<D>::LOADS], vof[PfCfg<D>::LOADS];
+    uint32_t kof0[PfCfg<D>::LOADS], vof0[PfCfg<D>::LOADS];
+    int key[PfCfg<D>::LOADS];
+};
+
+template <int D>
 __device__ __forceinline__ void pf_load_page(uint16_t *lds_k, uint16_t *lds_v, const uint16_t *page_base,
-                                             const uint32_t (&off)[PfCfg<D>::LOADS],
-                                             const uint32_t (&off0)[PfCfg<D>::LOADS],
-                                             const int (&key)[PfCfg<D>::LOADS], int64_t kv_skv,
-                                             int w, int valid) {
+                                             const PageLoad<D> &pl, int64_t kv_skv, int w, int valid) {
     using C = PfCfg<D>;
     const uint16_t *vbase = page_base + kv_skv;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const uint32_t o = key[i] < valid ? off[i] : off0[i];
+        const bool ok = pl.key[i] < valid;
         const int slot = (i * kThreads + w * 64) * 8;   // wave-uniform LDS element offset
-        dma16(lds_address(lds_k + slot), page_base, o);
-        dma16(lds_address(lds_v + slot), vbase, o);
+        dma16(lds_address(lds_k + slot), page_base, ok ? pl.kof[i] : pl.kof0[i]);
+        dma16(lds_address(lds_v + slot), vbase, ok ? pl.vof[i] : pl.vof0[i]);
     }
 }
 
@@ -188,20 +199,23 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     }
 
     // This thread's page-relative load offsets (fixed for every page).
-    uint32_t ld_off[C::LOADS], ld_off0[C::LOADS];
-    int ld_key[C::LOADS];
+    PageLoad<D> pl;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int p = i * kThreads + tid;
-        ld_key[i] = p / C::CH;
-        const int c = (p % C::CH) ^ (2 * (ld_key[i] & 7));
-        ld_off[i] = (uint32_t)(ld_key[i] * a.kv_ss + c * 8) * 2u;
-        ld_off0[i] = (uint32_t)(c * 8) * 2u;
+        const int key = p / C::CH;
+        const int ck = (p % C::CH) ^ (key & 7);
+        const int cv = (p % C::CH) ^ (2 * (key & 3));
+        pl.key[i] = key;
+        pl.kof[i] = (uint32_t)(key * a.kv_ss + ck * 8) * 2u;
+        pl.vof[i] = (uint32_t)(key * a.kv_ss + cv * 8) * 2u;
+        pl.kof0[i] = (uint32_t)(ck * 8) * 2u;
+        pl.vof0[i] = (uint32_t)(cv * 8) * 2u;
     }
     auto issue_page = [&](int t) {
         const int pid = load_page_id(bt_row, t);
-        pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, ld_off,
-                        ld_off0, ld_key, a.kv_skv, w, L - t * kPage);
+        pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, pl,
+                        a.kv_skv, w, L - t * kPage);
     };
     // Wait until page t has landed in LDS: pages t+1 .. `issued` were
     // issued after it and may stay in flight (loads complete in issue order).
@@ -237,15 +251,15 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     const float sl2 = a.scale_log2_pos;   // > 0
 
     // Per-lane LDS element offsets.  K operand of a 32-key step: key
-    // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ 2(lane & 7).
+    // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ (lane & 7).
     // V operand (transposing reads): key vkey (+8), columns of chunk
-    // 4 db + vcol_chunk, physical chunk ^ 2(vkey & 7).
+    // 4 db + vcol_chunk, physical chunk ^ 2(vkey & 3).
     const int klane = (lane & 31) * D;
-    const int kswz = 2 * (lane & 7);
+    const int kswz = lane & 7;
     const int q16 = lane >> 4;
     const int vkey = 4 * hi + ((lane & 15) >> 2);
     const int vlane = vkey * D + ((4 * (lane & 3)) & 7);
-    const int vswz = 2 * (vkey & 7);
+    const int vswz = 2 * (vkey & 3);
     const int vcol_chunk = 2 * (q16 & 1) + ((4 * (lane & 3)) >> 3);
 
     constexpr int NKS = D / 16;            // Q.K MFMA k-steps per 32-key step
@@ -254,6 +268,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     constexpr int EB = NEL / NKS;          // scores exponentiated per Q.K k-step
     constexpr int EA = NEL / NPV;          // scores max-reduced per P.V pair
     static_assert(EB * NKS == NEL && EA * NPV == NEL, "even split");
+    static_assert(EB % C::RB == 0 && EA % C::RB == 0, "even split per MFMA");
+    constexpr int PF = PA_PREFILL_PREFETCH;   // LDS operand reads in flight ahead of their MFMA
 
     auto kread = [&](const uint16_t *kp, int ks) {
         return *reinterpret_cast<const bf16x8 *>(kp + ((2 * ks + hi) ^ kswz) * 8);
@@ -321,20 +337,23 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
         for (int rb = 0; rb < C::RB; ++rb) mx[rb] = -INFINITY;
         {
             const uint16_t *vt = vstage(j > 0 ? j - 1 : 0);
-            bf16x8 vop[3];
-            vop[0] = vread(vt, 0);
-            vop[1] = vread(vt, 1);
+            bf16x8 vop[PF + 1];
+#pragma unroll
+            for (int k = 0; k < PF; ++k) vop[k] = vread(vt, k);
 #pragma unroll
             for (int k = 0; k < NPV; ++k) {
-                if (k + 2 < NPV) vop[(k + 2) % 3] = vread(vt, k + 2);
+                if (k + PF < NPV) vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
+                // one MFMA, then its share of the VALU work
 #pragma unroll
-                for (int rb = 0; rb < C::RB; ++rb)
+                for (int rb = 0; rb < C::RB; ++rb) {
                     oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        vop[k % 3], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+                        vop[k % (PF + 1)], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+                    constexpr int EH = EA / C::RB;
 #pragma unroll
-                for (int e = k * EA; e < (k + 1) * EA; ++e)
-                    mx[e / 16] = fmaxf(mx[e / 16], scur[e / 16][e % 16]);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int e = (k * C::RB + rb) * EH; e < (k * C::RB + rb + 1) * EH; ++e)
+                        mx[e / 16] = fmaxf(mx[e / 16], scur[e / 16][e % 16]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         float alpha[C::RB], m_use[C::RB];
@@ -374,9 +393,9 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
         // step the product reads a stale stage (in bounds) and is discarded.
         {
             const uint16_t *kp = kstage(j + 1);
-            bf16x8 kop[3];
-            kop[0] = kread(kp, 0);
-            kop[1] = kread(kp, 1);
+            bf16x8 kop[PF + 1];
+#pragma unroll
+            for (int k = 0; k < PF; ++k) kop[k] = kread(kp, k);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb) snext[rb] = f32x16{};
             float pf[NEL];
@@ -385,26 +404,29 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
             for (int rb = 0; rb < C::RB; ++rb) psum[rb] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                if (ks + 2 < NKS) kop[(ks + 2) % 3] = kread(kp, ks + 2);
+                if (ks + PF < NKS) kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
+                // one MFMA, then its share of the VALU work
 #pragma unroll
-                for (int rb = 0; rb < C::RB; ++rb)
-                    snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % 3], qreg[rb][ks], snext[rb], 0, 0, 0);
+                for (int rb = 0; rb < C::RB; ++rb) {
+                    snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % (PF + 1)], qreg[rb][ks], snext[rb], 0, 0, 0);
+                    constexpr int EH = EB / C::RB;
 #pragma unroll
-                for (int e = ks * EB; e < (ks + 1) * EB; ++e) {
-                    const int rb = e / 16, i = e % 16;
-                    pf[e] = exp2_fast(fmaf(scur[rb][i], sl2, -m_use[rb]));
-                    if (i & 1) {
-                        // round the pair to bf16; the row sum uses the same
-                        // rounded P as the P.V product
-                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                        const bf16x2 pp = {(__bf16)pf[e - 1], (__bf16)pf[e]};
-                        pb[rb][i >> 3][(i & 7) - 1] = pp[0];
-                        pb[rb][i >> 3][i & 7] = pp[1];
-                        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-                        psum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum[rb], false);
+                    for (int e = (ks * C::RB + rb) * EH; e < (ks * C::RB + rb + 1) * EH; ++e) {
+                        const int rr = e / 16, i = e % 16;
+                        pf[e] = exp2_fast(fmaf(scur[rr][i], sl2, -m_use[rr]));
+                        if (i & 1) {
+                            // round the pair to bf16; the row sum uses the same
+                            // rounded P as the P.V product
+                            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                            const bf16x2 pp = {(__bf16)pf[e - 1], (__bf16)pf[e]};
+                            pb[rr][i >> 3][(i & 7) - 1] = pp[0];
+                            pb[rr][i >> 3][i & 7] = pp[1];
+                            const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+                            psum[rr] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, psum[rr], false);
+                        }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb) l_part[rb] += psum[rb];
