@@ -7,8 +7,10 @@ next to this file is compiled by ``gcc`` on its own.
 
 ``paged_attn`` is masked softmax attention written out as its definition
 (see the header of ``paged_attn_oracle.c`` for the formula and the pages it
-follows).  ``quant_attn`` (in ``quant.py``) emulates the int8 QK / fp8 PV
-quantised variant step by step.
+follows).  ``quant_prep`` / ``quant_attn`` emulate the int8 Q.K / fp8 P.V
+quantised variant step by step (``quant_oracle.c``); the rounding of the
+softmax weights to fp8 inside the fused loop is "parity unpinned": the page
+names that step but not its arithmetic.
 """
 from __future__ import annotations
 
@@ -49,10 +51,14 @@ def _load():
             p, p, p, i64, i64, p, i64, i64, i64, i64, p, i64, p, p,
             i32, i32, i32, i32, i32, f64, i32, p, i64, i32]
         lib.oracle_num_threads.restype = ctypes.c_int
-        if hasattr(lib, "oracle_quant_attn"):
-            lib.oracle_quant_attn.restype = ctypes.c_int
-            lib.oracle_quant_attn.argtypes = [
-                p, p, p, p, i32, i32, i32, i32, f64, i32, i32, p, i32]
+        lib.oracle_quant_prep.restype = ctypes.c_int
+        lib.oracle_quant_prep.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p, p, p, p, p, i32]
+        lib.oracle_quant_attn.restype = ctypes.c_int
+        lib.oracle_quant_attn.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, f64, i32, i32, p, p, i32]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [f64]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         _lib = lib
     return _lib
 
@@ -102,3 +108,61 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
     if rc != 0:
         raise RuntimeError("oracle_paged_attn failed with status %d" % rc)
     return (out, lse) if return_lse else out
+
+
+QBLOCK = 64  # tokens per int8 scale block
+
+
+def e4m3_encode(x: float) -> int:
+    """OCP E4M3 code of x (round to nearest even, saturating at +-448)."""
+    return int(_load().oracle_e4m3_encode(float(x)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(code) & 0xFF))
+
+
+def quant_prep(q, k, v, nthreads: int = 0) -> dict:
+    """Quantisation steps of the int8/fp8 attention variant.
+
+    q, k, v: bf16 [B, N, H, D] CPU tensors (made contiguous here).
+    Returns numpy arrays: mk f32 [B,H,D]; qi, ki int8 [B,N,H,D];
+    sq, sk f32 [B,H,ceil(N/64)]; vq uint8 e4m3 codes [B,H,D,N]; sv f32 [B,H,D].
+    """
+    lib = _load()
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.shape == k.shape == v.shape
+    B, N, H, D = q.shape
+    NB = (N + QBLOCK - 1) // QBLOCK
+    r = {"mk": np.zeros((B, H, D), np.float32), "qi": np.zeros((B, N, H, D), np.int8),
+         "sq": np.zeros((B, H, NB), np.float32), "ki": np.zeros((B, N, H, D), np.int8),
+         "sk": np.zeros((B, H, NB), np.float32), "vq": np.zeros((B, H, D, N), np.uint8),
+         "sv": np.zeros((B, H, D), np.float32)}
+    rc = lib.oracle_quant_prep(_ptr(q), _ptr(k), _ptr(v), B, N, H, D, r["mk"].ctypes.data,
+                               r["qi"].ctypes.data, r["sq"].ctypes.data, r["ki"].ctypes.data,
+                               r["sk"].ctypes.data, r["vq"].ctypes.data, r["sv"].ctypes.data,
+                               int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_quant_prep failed with status %d" % rc)
+    r["shape"] = (B, N, H, D)
+    return r
+
+
+def quant_attn(prep: dict, scale: float, causal: bool, quant_p: bool = True, row_mask=None,
+               nthreads: int = 0) -> np.ndarray:
+    """Quantised attention from ``quant_prep`` outputs; fp64 [B, N, H, D]."""
+    lib = _load()
+    B, N, H, D = prep["shape"]
+    out = np.zeros((B, N, H, D), np.float64)
+    rm = None
+    if row_mask is not None:
+        rm = np.ascontiguousarray(np.asarray(row_mask, dtype=np.uint8))
+        assert rm.shape == (N,)
+    arrs = [np.ascontiguousarray(prep[x]) for x in ("qi", "sq", "ki", "sk", "vq", "sv")]
+    rc = lib.oracle_quant_attn(*[a.ctypes.data for a in arrs], B, N, H, D, float(scale),
+                               int(bool(causal)), int(bool(quant_p)),
+                               rm.ctypes.data if rm is not None else None, out.ctypes.data,
+                               int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_quant_attn failed with status %d" % rc)
+    return out
