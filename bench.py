@@ -32,6 +32,7 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+Q8_PEAK_TOPS = 5000.0          # MI355X dense int8 / fp8 MFMA, 5.0 P(FL)OP/s
 METRIC = "decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% bf16 MFMA peak)"
 
 DESCR = {
@@ -78,6 +79,35 @@ def algorithmic_flops(case) -> int:
     return 4 * case.head_dim * case.num_q_heads * visible_pairs(case)
 
 
+def _time_steps(fn, steps):
+    """Average ms per call of fn() over `steps` calls, events on the current stream."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def _kernel_times(fn, steps):
+    """Per-kind average kernel ms from the library's per-launch HIP events
+    (recorded on the launch stream), in a separate pass so the step timing
+    above carries no instrumentation."""
+    import paged_kv_gqa_fwd_amd as pa
+    torch.cuda.synchronize()
+    pa.kernel_timing_read()                      # discard anything recorded before
+    pa.kernel_timing_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    pa.kernel_timing_enable(False)
+    mm, mn, cm, cn, pm, pn = pa.kernel_timing_read()
+    return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
+
+
 def run_workload(name, steps, warmup, pps=0, path=0):
     import paged_kv_gqa_fwd_amd as pa
     log("[bench] generating %s" % name)
@@ -87,30 +117,47 @@ def run_workload(name, steps, warmup, pps=0, path=0):
             case.scale, case.causal)
     dims = pa.make_dims(case.q, case.kv, case.block_table, out)
     plan = pa.make_plan(dims, case.n_seqs, max(case.max_q, 1), path, pps)
+
+    def step():
+        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
+
     for _ in range(warmup):
-        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
-    torch.cuda.synchronize()
-    pa.kernel_timing_read()                      # discard anything recorded before
-    pa.kernel_timing_enable(True)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps):
-        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
-    t1.record()
-    torch.cuda.synchronize()
-    pa.kernel_timing_enable(False)
-    step_ms = t0.elapsed_time(t1) / steps
-    main_ms, main_n, comb_ms, comb_n = pa.kernel_timing_read()
+        step()
+    step_ms = _time_steps(step, steps)
+    main_ms, comb_ms, _ = _kernel_times(step, steps)
     res = {
         "workload": name, "case": case, "ms_per_step": step_ms,
-        "main_kernel_ms": main_ms / max(main_n, 1), "combine_kernel_ms": comb_ms / max(comb_n, 1) if comb_n else 0.0,
+        "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": "split_decode+combine" if plan.path == pa.PATH_SPLIT_DECODE else "prefill",
         "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
         "bytes": algorithmic_bytes(case), "flops": algorithmic_flops(case),
     }
     return res
+
+
+def run_quant(steps, warmup):
+    """The quantised path (attn_quant_fwd: preparation + fused int8/fp8 loop)
+    on the video-DiT shape, same seeded Q/K/V as the bf16 DiT workload."""
+    import paged_kv_gqa_fwd_amd as pa
+    log("[bench] generating dit_self_attn (quantised path)")
+    case = workloads.dit_self_attn(device="cuda")
+    q, k, v = workloads.dense_from_case(case)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        pa.quant_attention(q, k, v, case.scale, False, out=out)
+
+    for _ in range(warmup):
+        step()
+    step_ms = _time_steps(step, steps)
+    main_ms, _, prep_ms = _kernel_times(step, steps)
+    flops = algorithmic_flops(case)
+    return {"workload": "dit_quant", "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
+            "mainloop_ms": round(main_ms, 4), "prep_ms": round(prep_ms, 4),
+            "mainloop_TOPS": round(flops / (main_ms * 1e-3) / 1e12, 2),
+            "frac_of_int8_fp8_peak": round(flops / (step_ms * 1e-3) / 1e12 / Q8_PEAK_TOPS, 4),
+            "path": "quant (int8 QK, fp8 PV)"}
 
 
 def summarize(res):
@@ -192,7 +239,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn",
+    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant",
                     help="comma list of extra workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
@@ -211,6 +258,12 @@ def main():
     log("[bench] %s" % json.dumps(s))
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        if name == "dit_quant":
+            ss = run_quant(max(3, args.steps // 2), max(1, args.warmup // 2))
+            log("[bench] %s" % json.dumps(ss))
+            secondary.append(ss)
+            torch.cuda.empty_cache()
+            continue
         r = run_workload(name, max(3, args.steps // 2), max(1, args.warmup // 2))
         ss = summarize(r)
         log("[bench] %s" % json.dumps(ss))

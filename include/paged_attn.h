@@ -156,17 +156,85 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
                       size_t workspace_bytes, void *stream, int32_t path_hint,
                       int32_t pages_per_split);
 
+/* ---------------------------------------------------------------------------
+ * Quantised attention (int8 Q.K, fp8 P.V) over dense Q, K, V.
+ *
+ * Operation: softmax(scale * Q K^T) V per (batch b, head h) over the N tokens
+ * of a sequence (queries and keys are the same N tokens; causal = query i
+ * sees keys 0..i), computed through the quantisation steps named by the
+ * SageAttention2 block-24 baseline page (h3-blackwell-runtime
+ * benchmarks/gb10-sage2-block24-scheduler-baseline.json, phase_timings and
+ * fused_mainloop_phases):
+ *   1. K smoothing: mk = mean over tokens of K per (b, h, channel); K' = K - mk.
+ *   2. Q and K' to int8 per (b, h, 64-token block): s = amax / 127 (1 for an
+ *      all-zero block), code = clamp(rne(x / s), -127, 127).
+ *   3. V to fp8 e4m3 per (b, h, channel): s_v = amax over tokens / 448,
+ *      code = e4m3(V / s_v) (OCP e4m3, round to nearest even); stored
+ *      transposed [b, h, channel, token] and padded to a multiple of 64
+ *      tokens, with the tokens of every 64-token tile permuted.
+ *   4. Fused loop over 64-key tiles: scores from the int8 products times the
+ *      two block scales and scale; online softmax with the running maximum
+ *      taken per tile; the weight w (<= 1) enters P.V as e4m3(448 w); the row
+ *      sum uses the unrounded w; out = O s_v / (448 l), rounded to bf16.
+ * Supported: head_dim 128.
+ */
+typedef struct attn_quant_dims {
+    int32_t batch;        /* B */
+    int32_t seq_len;      /* N: tokens per sequence (queries = keys) */
+    int32_t num_heads;    /* H (one K/V head per q head) */
+    int32_t head_dim;     /* D: 128 */
+    int64_t q_stride[3];  /* element strides of (batch, token, head); D contiguous */
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+} attn_quant_dims;
+
+/* Byte offsets of the quantised intermediates inside the caller's workspace
+ * (all 256-byte aligned).  Layouts: mk, sv f32 [B, H, D]; sq, sk f32
+ * [B, H, blocks]; qi, ki int8 [B, N, H, D]; vt e4m3 codes [B, H, D, vt_stride]
+ * where the token at offset j (< 64) of a 64-token tile is stored at position
+ * 32 ((j % 8) / 4) + 16 (j / 32) + 4 ((j % 32) / 8) + j % 4 of the tile, and
+ * padding tokens hold code 0; ksum (f64) and vmax (f32) [B, H, chunks, D] are
+ * scratch. */
+typedef struct attn_quant_layout {
+    size_t workspace_bytes;
+    size_t off_mk, off_sv, off_sq, off_sk, off_qi, off_ki, off_vt, off_ksum, off_vmax;
+    int32_t blocks;       /* ceil(N / 64) */
+    int32_t chunks;       /* ceil(N / 256) */
+    int32_t vt_stride;    /* blocks * 64 */
+} attn_quant_layout;
+
+/* Workspace size and layout for these sizes (host only; no GPU needed).
+ * Returns ATTN_OK or a validation error (head_dim != 128 is UNSUPPORTED). */
+int attn_quant_layout_of(const attn_quant_dims *dims, attn_quant_layout *layout);
+
+/* Steps 1-3: q, k, v bf16 device tensors (strides in dims) -> workspace. */
+int attn_quant_prep(const void *q, const void *k, const void *v, const attn_quant_dims *dims,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step 4 from a workspace filled by attn_quant_prep: out bf16 [B, N, H, D]
+ * (o_stride).  scale: finite; causal: nonzero = query i sees keys 0..i. */
+int attn_quant_attend(void *out, const attn_quant_dims *dims, float scale, int32_t causal,
+                      const void *workspace, size_t workspace_bytes, void *stream);
+
+/* Steps 1-4 in one call (all arguments validated before anything launches). */
+int attn_quant_fwd(void *out, const void *q, const void *k, const void *v,
+                   const attn_quant_dims *dims, float scale, int32_t causal, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /*
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
- * launch is bracketed by HIP events recorded on the launch stream; the
- * elapsed times of the main attention kernel and of the combine kernel are
- * summed per kernel.  attn_kernel_timing_read synchronises on the recorded
- * events, returns the totals (milliseconds) and launch counts, and resets
- * them.  Returns ATTN_ERR_HIP if an event call fails.
+ * launch is bracketed by HIP events recorded on the launch stream; elapsed
+ * times are summed per kind: the main attention kernel (split-KV partials,
+ * prefill or the quantised loop), the split-KV combine kernel, and the
+ * quantised path's preparation kernels.  attn_kernel_timing_read
+ * synchronises on the recorded events, returns the totals (milliseconds)
+ * and launch counts (any pointer may be NULL), and resets them.  Returns
+ * ATTN_ERR_HIP if an event call fails.
  */
 int attn_kernel_timing_enable(int32_t enable);
 int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
-                            int32_t *combine_launches);
+                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches);
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char *attn_status_string(int status);

@@ -46,6 +46,31 @@ class attn_paged_dims(ctypes.Structure):
     ]
 
 
+class attn_quant_dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class attn_quant_layout(ctypes.Structure):
+    _fields_ = [
+        ("workspace_bytes", ctypes.c_size_t),
+        ("off_mk", ctypes.c_size_t), ("off_sv", ctypes.c_size_t), ("off_sq", ctypes.c_size_t),
+        ("off_sk", ctypes.c_size_t), ("off_qi", ctypes.c_size_t), ("off_ki", ctypes.c_size_t),
+        ("off_vt", ctypes.c_size_t), ("off_ksum", ctypes.c_size_t), ("off_vmax", ctypes.c_size_t),
+        ("blocks", ctypes.c_int32),
+        ("chunks", ctypes.c_int32),
+        ("vt_stride", ctypes.c_int32),
+    ]
+
+
 class attn_paged_plan(ctypes.Structure):
     _fields_ = [
         ("path", ctypes.c_int32),
@@ -85,9 +110,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_kernel_timing_enable.argtypes = [i32]
     lib.attn_kernel_timing_enable.restype = ctypes.c_int
-    lib.attn_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
-                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    dp, ip = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)
+    lib.attn_kernel_timing_read.argtypes = [dp, ip, dp, ip, dp, ip]
     lib.attn_kernel_timing_read.restype = ctypes.c_int
+    qd_p = ctypes.POINTER(attn_quant_dims)
+    lib.attn_quant_layout_of.argtypes = [qd_p, ctypes.POINTER(attn_quant_layout)]
+    lib.attn_quant_layout_of.restype = ctypes.c_int
+    lib.attn_quant_prep.argtypes = [p, p, p, qd_p, p, sz, p]
+    lib.attn_quant_prep.restype = ctypes.c_int
+    lib.attn_quant_attend.argtypes = [p, qd_p, ctypes.c_float, i32, p, sz, p]
+    lib.attn_quant_attend.restype = ctypes.c_int
+    lib.attn_quant_fwd.argtypes = [p, p, p, p, qd_p, ctypes.c_float, i32, p, sz, p]
+    lib.attn_quant_fwd.restype = ctypes.c_int
     lib.attn_version.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -202,11 +236,119 @@ def kernel_timing_enable(on: bool) -> None:
 
 
 def kernel_timing_read():
-    """(main_ms_total, main_launches, combine_ms_total, combine_launches)."""
+    """(main_ms_total, main_launches, combine_ms_total, combine_launches,
+    prep_ms_total, prep_launches)."""
     lib = load_library()
-    mm, cm = ctypes.c_double(), ctypes.c_double()
-    mn, cn = ctypes.c_int32(), ctypes.c_int32()
-    rc = lib.attn_kernel_timing_read(ctypes.byref(mm), ctypes.byref(mn), ctypes.byref(cm), ctypes.byref(cn))
+    v = [ctypes.c_double(), ctypes.c_int32(), ctypes.c_double(), ctypes.c_int32(),
+         ctypes.c_double(), ctypes.c_int32()]
+    rc = lib.attn_kernel_timing_read(*[ctypes.byref(x) for x in v])
     if rc != ATTN_OK:
         raise AttnError(rc)
-    return mm.value, mn.value, cm.value, cn.value
+    return tuple(x.value for x in v)
+
+
+# ---------------------------------------------------------------- quantised path
+def make_quant_dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> attn_quant_dims:
+    """Sizes and element strides of dense [B, N, H, D] q / k / v / out."""
+    out = q if out is None else out
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or tuple(t.shape) != tuple(q.shape):
+            raise ValueError("%s must be [B, N, H, D] like q" % name)
+        if t.stride(3) != 1:
+            raise ValueError("head_dim axis of %s must be contiguous" % name)
+    B, N, H, D = q.shape
+    dims = attn_quant_dims(batch=B, seq_len=N, num_heads=H, head_dim=D)
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        arr = getattr(dims, field)
+        for i in range(3):
+            arr[i] = t.stride(i)
+    return dims
+
+
+def quant_layout(dims: attn_quant_dims) -> attn_quant_layout:
+    lay = attn_quant_layout()
+    rc = load_library().attn_quant_layout_of(ctypes.byref(dims), ctypes.byref(lay))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return lay
+
+
+def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               workspace: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None):
+    """Quantisation steps (``attn_quant_prep``); returns (workspace, layout)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t, torch.bfloat16)
+    dims = make_quant_dims(q, k, v)
+    lay = quant_layout(dims)
+    if workspace is None:
+        workspace = torch.empty(lay.workspace_bytes, dtype=torch.uint8, device=q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.attn_quant_prep(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(dims),
+                             workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return workspace, lay
+
+
+def quant_attend(q_shape_like: torch.Tensor, workspace: torch.Tensor, scale: float,
+                 causal: bool = False, out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Fused quantised attention loop (``attn_quant_attend``) from a prepared
+    workspace; ``q_shape_like`` gives the [B, N, H, D] shape and device."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q_shape_like.shape, dtype=torch.bfloat16, device=q_shape_like.device)
+    _check_device_tensor("out", out, torch.bfloat16)
+    _check_device_tensor("workspace", workspace, torch.uint8)
+    dims = make_quant_dims(out, out, out, out)
+    st = stream if stream is not None else torch.cuda.current_stream(out.device)
+    rc = lib.attn_quant_attend(out.data_ptr(), ctypes.byref(dims), float(scale), int(bool(causal)),
+                               workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return out
+
+
+def quant_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
+                    causal: bool = False, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Quantised attention in one call (``attn_quant_fwd``): q, k, v dense
+    bf16 [B, N, H, D] on the GPU; returns out bf16 [B, N, H, D]."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t, torch.bfloat16)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check_device_tensor("out", out, torch.bfloat16)
+    dims = make_quant_dims(q, k, v, out)
+    lay = quant_layout(dims)
+    if workspace is None:
+        workspace = _workspace(lay.workspace_bytes, q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.attn_quant_fwd(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            ctypes.byref(dims), float(scale), int(bool(causal)), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return out
+
+
+def quant_workspace_views(workspace: torch.Tensor, lay: attn_quant_layout, shape):
+    """Typed views of the quantised intermediates inside a workspace."""
+    B, N, H, D = shape
+    def view(off, n, dtype):
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return workspace[off:off + nbytes].view(dtype)
+    return {
+        "mk": view(lay.off_mk, B * H * D, torch.float32).view(B, H, D),
+        "sv": view(lay.off_sv, B * H * D, torch.float32).view(B, H, D),
+        "sq": view(lay.off_sq, B * H * lay.blocks, torch.float32).view(B, H, lay.blocks),
+        "sk": view(lay.off_sk, B * H * lay.blocks, torch.float32).view(B, H, lay.blocks),
+        "qi": view(lay.off_qi, B * N * H * D, torch.int8).view(B, N, H, D),
+        "ki": view(lay.off_ki, B * N * H * D, torch.int8).view(B, N, H, D),
+        "vt": view(lay.off_vt, B * H * D * lay.vt_stride, torch.uint8).view(B, H, D, lay.vt_stride),
+    }

@@ -14,11 +14,14 @@
 
 #include "attn_device.h"
 #include "paged_attn.h"
+#include "quant_device.h"
 
 namespace pa {
 hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
+hipError_t launch_quant_prep(const QuantArgs &a, hipStream_t stream);
+hipError_t launch_quant_attn(const QuantArgs &a, hipStream_t stream);
 }  // namespace pa
 
 namespace {
@@ -114,9 +117,10 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
 }
 
 // ---- kernel timing instrumentation ---------------------------------------
+enum TimedKind { kTimedMain = 0, kTimedCombine = 1, kTimedPrep = 2 };
 struct TimedLaunch {
     hipEvent_t start, stop;
-    bool combine;
+    int kind;
 };
 std::mutex g_timing_mu;
 bool g_timing_on = false;
@@ -126,6 +130,16 @@ int record_event(hipEvent_t *ev, hipStream_t stream) {
     if (hipEventCreate(ev) != hipSuccess) return ATTN_ERR_HIP;
     if (hipEventRecord(*ev, stream) != hipSuccess) return ATTN_ERR_HIP;
     return ATTN_OK;
+}
+
+bool timing_enabled() {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    return g_timing_on;
+}
+
+void timing_push(const TimedLaunch &t) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timed.push_back(t);
 }
 
 int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
@@ -187,11 +201,7 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(plan.grid_x, plan.grid_y, plan.grid_z);
-    bool timing;
-    {
-        std::lock_guard<std::mutex> lk(g_timing_mu);
-        timing = g_timing_on;
-    }
+    const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
     if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
     hipError_t e = plan.path == ATTN_PATH_SPLIT_DECODE ? pa::launch_decode_split_any(D, a, grid, st)
@@ -219,13 +229,135 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
         if (timing && record_event(&t_comb.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
     }
     if (timing) {
-        std::lock_guard<std::mutex> lk(g_timing_mu);
-        t_main.combine = false;
-        g_timed.push_back(t_main);
+        t_main.kind = kTimedMain;
+        timing_push(t_main);
         if (need_combine) {
-            t_comb.combine = true;
-            g_timed.push_back(t_comb);
+            t_comb.kind = kTimedCombine;
+            timing_push(t_comb);
         }
+    }
+    return ATTN_OK;
+}
+
+// ---- quantised path -------------------------------------------------------
+int quant_layout(const attn_quant_dims *d, attn_quant_layout *lay) {
+    if (!d || !lay) return ATTN_ERR_NULL;
+    if (d->head_dim != pa::kQuantD) return ATTN_ERR_UNSUPPORTED;
+    if (d->batch <= 0 || d->seq_len <= 0 || d->num_heads <= 0) return ATTN_ERR_SHAPE;
+    if (d->batch > kGridYZMax || d->num_heads > kGridYZMax || 2 * (int64_t)d->batch > kGridYZMax)
+        return ATTN_ERR_SHAPE;
+    const int64_t *strides[] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+    for (const int64_t *st : strides) {
+        for (int i = 0; i < 3; ++i)
+            if (st[i] <= 0 || (st[i] & 7) != 0) return ATTN_ERR_STRIDE;
+        if (st[2] < d->head_dim || st[1] < (int64_t)d->num_heads * st[2] ||
+            st[0] < (int64_t)d->seq_len * st[1])
+            return ATTN_ERR_STRIDE;
+    }
+    const int64_t B = d->batch, N = d->seq_len, H = d->num_heads, D = d->head_dim;
+    const int64_t blocks = (N + pa::kQuantBlock - 1) / pa::kQuantBlock;
+    const int64_t chunks = (N + pa::kQuantChunk - 1) / pa::kQuantChunk;
+    if (blocks > INT32_MAX || blocks * pa::kQuantBlock > INT32_MAX) return ATTN_ERR_SHAPE;
+    // the attention kernel addresses one head's K codes and V^T with 32-bit offsets
+    if (N * H * D > INT32_MAX || D * blocks * pa::kQuantBlock > INT32_MAX) return ATTN_ERR_SHAPE;
+    *lay = attn_quant_layout{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, kWsAlign);
+        return o;
+    };
+    lay->off_mk = take((size_t)(B * H * D) * 4);
+    lay->off_sv = take((size_t)(B * H * D) * 4);
+    lay->off_sq = take((size_t)(B * H * blocks) * 4);
+    lay->off_sk = take((size_t)(B * H * blocks) * 4);
+    lay->off_qi = take((size_t)(B * N * H * D));
+    lay->off_ki = take((size_t)(B * N * H * D));
+    lay->off_vt = take((size_t)(B * H * D * blocks * pa::kQuantBlock));
+    lay->off_ksum = take((size_t)(B * H * chunks * D) * 8);
+    lay->off_vmax = take((size_t)(B * H * chunks * D) * 4);
+    lay->workspace_bytes = off;
+    lay->blocks = (int32_t)blocks;
+    lay->chunks = (int32_t)chunks;
+    lay->vt_stride = (int32_t)(blocks * pa::kQuantBlock);
+    return ATTN_OK;
+}
+
+int quant_args(const attn_quant_dims *d, void *workspace, size_t bytes, pa::QuantArgs *a) {
+    attn_quant_layout lay;
+    int rc = quant_layout(d, &lay);
+    if (rc != ATTN_OK) return rc;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0 ||
+        bytes < lay.workspace_bytes)
+        return ATTN_ERR_WORKSPACE;
+    char *w = static_cast<char *>(workspace);
+    *a = pa::QuantArgs{};
+    a->b = d->batch;
+    a->n = d->seq_len;
+    a->h = d->num_heads;
+    a->blocks = lay.blocks;
+    a->chunks = lay.chunks;
+    a->vt_stride = lay.vt_stride;
+    a->mk = reinterpret_cast<float *>(w + lay.off_mk);
+    a->sv = reinterpret_cast<float *>(w + lay.off_sv);
+    a->sq = reinterpret_cast<float *>(w + lay.off_sq);
+    a->sk = reinterpret_cast<float *>(w + lay.off_sk);
+    a->qi = reinterpret_cast<int8_t *>(w + lay.off_qi);
+    a->ki = reinterpret_cast<int8_t *>(w + lay.off_ki);
+    a->vt = reinterpret_cast<uint8_t *>(w + lay.off_vt);
+    a->ksum_part = reinterpret_cast<double *>(w + lay.off_ksum);
+    a->vmax_part = reinterpret_cast<float *>(w + lay.off_vmax);
+    return ATTN_OK;
+}
+
+int quant_prep_impl(const void *q, const void *k, const void *v, const attn_quant_dims *d,
+                    void *workspace, size_t bytes, void *stream) {
+    pa::QuantArgs a;
+    int rc = quant_args(d, workspace, bytes, &a);
+    if (rc != ATTN_OK) return rc;
+    if (!q || !k || !v) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.q_sb = d->q_stride[0]; a.q_st = d->q_stride[1]; a.q_sh = d->q_stride[2];
+    a.k_sb = d->k_stride[0]; a.k_st = d->k_stride[1]; a.k_sh = d->k_stride[2];
+    a.v_sb = d->v_stride[0]; a.v_st = d->v_stride[1]; a.v_sh = d->v_stride[2];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool timing = timing_enabled();
+    TimedLaunch tl{};
+    if (timing && record_event(&tl.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+    if (pa::launch_quant_prep(a, st) != hipSuccess) return ATTN_ERR_HIP;
+    if (timing) {
+        if (record_event(&tl.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+        tl.kind = kTimedPrep;
+        timing_push(tl);
+    }
+    return ATTN_OK;
+}
+
+int quant_attend_impl(void *out, const attn_quant_dims *d, float scale, int32_t causal,
+                      const void *workspace, size_t bytes, void *stream) {
+    pa::QuantArgs a;
+    int rc = quant_args(d, const_cast<void *>(workspace), bytes, &a);
+    if (rc != ATTN_OK) return rc;
+    if (!out) return ATTN_ERR_NULL;
+    if (!aligned16(out)) return ATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+    a.out = static_cast<uint16_t *>(out);
+    a.o_sb = d->o_stride[0]; a.o_st = d->o_stride[1]; a.o_sh = d->o_stride[2];
+    a.scale_log2_pos = std::max((float)(std::fabs((double)scale) * 1.4426950408889634), FLT_MIN);
+    a.q_negate = scale < 0.f ? 1 : 0;
+    a.causal = causal ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool timing = timing_enabled();
+    TimedLaunch tl{};
+    if (timing && record_event(&tl.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+    if (pa::launch_quant_attn(a, st) != hipSuccess) return ATTN_ERR_HIP;
+    if (timing) {
+        if (record_event(&tl.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+        tl.kind = kTimedMain;
+        timing_push(tl);
     }
     return ATTN_OK;
 }
@@ -274,35 +406,61 @@ int attn_kernel_timing_enable(int32_t enable) {
 }
 
 int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
-                            int32_t *combine_launches) {
+                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches) {
     std::vector<TimedLaunch> v;
     {
         std::lock_guard<std::mutex> lk(g_timing_mu);
         v.swap(g_timed);
     }
-    double tm = 0, tc = 0;
-    int nm = 0, nc = 0;
+    double tms[3] = {0, 0, 0};
+    int32_t cnt[3] = {0, 0, 0};
     int rc = ATTN_OK;
     for (auto &t : v) {
         float ms = 0.f;
         if (hipEventSynchronize(t.stop) != hipSuccess ||
             hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
             rc = ATTN_ERR_HIP;
-        if (t.combine) {
-            tc += ms;
-            ++nc;
-        } else {
-            tm += ms;
-            ++nm;
-        }
+        tms[t.kind] += ms;
+        ++cnt[t.kind];
         (void)hipEventDestroy(t.start);
         (void)hipEventDestroy(t.stop);
     }
-    if (main_ms) *main_ms = tm;
-    if (main_launches) *main_launches = nm;
-    if (combine_ms) *combine_ms = tc;
-    if (combine_launches) *combine_launches = nc;
+    if (main_ms) *main_ms = tms[kTimedMain];
+    if (main_launches) *main_launches = cnt[kTimedMain];
+    if (combine_ms) *combine_ms = tms[kTimedCombine];
+    if (combine_launches) *combine_launches = cnt[kTimedCombine];
+    if (prep_ms) *prep_ms = tms[kTimedPrep];
+    if (prep_launches) *prep_launches = cnt[kTimedPrep];
     return rc;
+}
+
+int attn_quant_layout_of(const attn_quant_dims *dims, attn_quant_layout *layout) {
+    return quant_layout(dims, layout);
+}
+
+int attn_quant_prep(const void *q, const void *k, const void *v, const attn_quant_dims *dims,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    return quant_prep_impl(q, k, v, dims, workspace, workspace_bytes, stream);
+}
+
+int attn_quant_attend(void *out, const attn_quant_dims *dims, float scale, int32_t causal,
+                      const void *workspace, size_t workspace_bytes, void *stream) {
+    return quant_attend_impl(out, dims, scale, causal, workspace, workspace_bytes, stream);
+}
+
+int attn_quant_fwd(void *out, const void *q, const void *k, const void *v,
+                   const attn_quant_dims *dims, float scale, int32_t causal, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    // validate everything before launching anything
+    pa::QuantArgs a;
+    int rc = quant_args(dims, workspace, workspace_bytes, &a);
+    if (rc != ATTN_OK) return rc;
+    if (!out || !q || !k || !v) return ATTN_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+    if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+    rc = quant_prep_impl(q, k, v, dims, workspace, workspace_bytes, stream);
+    if (rc != ATTN_OK) return rc;
+    return quant_attend_impl(out, dims, scale, causal, workspace, workspace_bytes, stream);
 }
 
 const char *attn_status_string(int status) {

@@ -34,7 +34,8 @@ def header_functions():
 def test_header_declares_entry_points():
     fns = header_functions()
     for name in ("attn_paged_fwd", "attn_paged_fwd_ex", "attn_paged_make_plan",
-                 "attn_paged_workspace_bytes", "attn_status_string"):
+                 "attn_paged_workspace_bytes", "attn_status_string", "attn_quant_fwd",
+                 "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of"):
         assert name in fns
 
 
@@ -183,3 +184,64 @@ def test_python_binding_refuses_cpu_tensors(pa):
     with pytest.raises(ValueError):
         pa.paged_attention(q, kv, bt, torch.ones(1, dtype=torch.int32),
                            torch.tensor([0, 1], dtype=torch.int32), 1, 0.1)
+
+
+# ---------------------------------------------------------------- quantised path
+def _qdims(pa, B=1, N=300, H=2, D=128):
+    d = pa.attn_quant_dims(batch=B, seq_len=N, num_heads=H, head_dim=D)
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = N * H * D, H * D, D
+    return d
+
+
+def test_quant_layout_sizes(pa):
+    import ctypes
+    d = _qdims(pa)
+    lay = pa.attn_quant_layout()
+    assert pa.load_library().attn_quant_layout_of(ctypes.byref(d), ctypes.byref(lay)) == 0
+    assert lay.blocks == 5 and lay.chunks == 2 and lay.vt_stride == 320
+    offs = [lay.off_mk, lay.off_sv, lay.off_sq, lay.off_sk, lay.off_qi, lay.off_ki, lay.off_vt,
+            lay.off_ksum, lay.off_vmax]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    # every region fits before the next one and inside the workspace
+    sizes = [2 * 128 * 4, 2 * 128 * 4, 2 * 5 * 4, 2 * 5 * 4, 300 * 2 * 128, 300 * 2 * 128,
+             2 * 128 * 320, 2 * 2 * 128 * 8, 2 * 2 * 128 * 4]
+    ends = [o + s for o, s in zip(offs, sizes)]
+    assert all(e <= n for e, n in zip(ends, offs[1:] + [lay.workspace_bytes]))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 256, -3), ("seq_len", 0, -2), ("num_heads", 0, -2), ("batch", 40000, -2)])
+def test_quant_layout_rejects(pa, field, value, status):
+    import ctypes
+    d = _qdims(pa)
+    setattr(d, field, value)
+    lay = pa.attn_quant_layout()
+    assert pa.load_library().attn_quant_layout_of(ctypes.byref(d), ctypes.byref(lay)) == status
+
+
+def test_quant_layout_rejects_bad_strides(pa):
+    import ctypes
+    d = _qdims(pa)
+    d.k_stride[1] = 100          # not a multiple of 8
+    lay = pa.attn_quant_layout()
+    assert pa.load_library().attn_quant_layout_of(ctypes.byref(d), ctypes.byref(lay)) == -4
+    d = _qdims(pa)
+    d.o_stride[2] = 64           # heads overlap
+    assert pa.load_library().attn_quant_layout_of(ctypes.byref(d), ctypes.byref(lay)) == -4
+
+
+def test_quant_calls_validate_before_launch(pa):
+    import ctypes
+    lib = pa.load_library()
+    d = _qdims(pa)
+    # workspace missing / too small / misaligned: rejected on the host
+    assert lib.attn_quant_fwd(0x1000, 0x1000, 0x1000, 0x1000, ctypes.byref(d), 0.1, 0, None, 0, None) == -6
+    assert lib.attn_quant_prep(0x1000, 0x1000, 0x1000, ctypes.byref(d), 0x1000, 16, None) == -6
+    assert lib.attn_quant_attend(0x1000, ctypes.byref(d), 0.1, 0, 0x1008, 1 << 30, None) == -6
+    # null and misaligned tensors
+    assert lib.attn_quant_fwd(None, 0x1000, 0x1000, 0x1000, ctypes.byref(d), 0.1, 0, 0x1000, 1 << 30, None) == -1
+    assert lib.attn_quant_fwd(0x1008, 0x1000, 0x1000, 0x1000, ctypes.byref(d), 0.1, 0, 0x1000, 1 << 30, None) == -5
+    # non-finite scale
+    assert lib.attn_quant_fwd(0x1000, 0x1000, 0x1000, 0x1000, ctypes.byref(d), float("nan"), 0, 0x1000, 1 << 30, None) == -2

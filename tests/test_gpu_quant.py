@@ -1,0 +1,143 @@
+"""GPU parity of the quantised path (int8 Q.K / fp8 P.V) through the C ABI.
+
+* Preparation (K mean, Q/K int8 codes and block scales, V fp8 codes and
+  channel scales): bit-exact against the oracle's quant_prep.  Both sides
+  take every rounding decision in f32 from identical f32 inputs; the K mean
+  is an fp64 sum, exact for these inputs, so its order does not matter.
+* Attention: relative RMS <= 1e-2 against the oracle that emulates the same
+  quantisation (the fp8 weight codes may differ where the kernel's f32 score
+  and the oracle's fp64 score round to different sides of a code boundary).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity_util import log
+
+pytestmark = pytest.mark.gpu
+
+REL_RMS_QUANT = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_gqa_fwd_amd as pa
+    pa.load_library()
+
+
+def quant_pos_of_key(j: int) -> int:
+    """Stored position of token j (< 64) within its tile of the fp8 V^T
+    workspace, as include/paged_attn.h documents it."""
+    return 32 * ((j % 8) // 4) + 16 * (j // 32) + 4 * ((j % 32) // 8) + j % 4
+
+
+def _unpermute_vt(vt: np.ndarray, n: int) -> np.ndarray:
+    """[B, H, D, Npad] stored layout -> [B, H, D, N] token order."""
+    npad = vt.shape[-1]
+    pos = np.array([64 * (j // 64) + quant_pos_of_key(j % 64) for j in range(npad)])
+    return vt[..., pos][..., :n]
+
+
+def _check_prep(q, k, v, oracle_mod, what):
+    import paged_kv_gqa_fwd_amd as pa
+    log("  gpu quant prep: %s shape=%s" % (what, tuple(q.shape)))
+    ws, lay = pa.quant_prep(q, k, v)
+    torch.cuda.synchronize()
+    views = {name: t.cpu().numpy() for name, t in pa.quant_workspace_views(ws, lay, q.shape).items()}
+    ref = oracle_mod.quant_prep(q.cpu(), k.cpu(), v.cpu())
+    for name in ("mk", "sv", "sq", "sk", "qi", "ki"):
+        assert np.array_equal(views[name], ref[name]), "%s: %s differs" % (what, name)
+    vt = _unpermute_vt(views["vt"], q.shape[1])
+    assert np.array_equal(vt, ref["vq"]), "%s: fp8 V codes differ" % what
+    # padding tokens of the last tile hold code 0
+    npad = views["vt"].shape[-1]
+    if npad > q.shape[1]:
+        tail = [64 * ((npad - 1) // 64) + quant_pos_of_key(j % 64) for j in range(q.shape[1], npad)]
+        assert not views["vt"][..., tail].any()
+    return ref
+
+
+def _compare(out, ref, what, rows=None, rel_rms=REL_RMS_QUANT):
+    g = out.float().cpu().double().numpy()
+    if rows is not None:
+        g, ref = g[:, rows], ref[:, rows]
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    rr = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+    ma = np.abs(g - ref).max()
+    log("  %s: rel_rms=%.3e max_abs=%.3e" % (what, rr, ma))
+    assert rr <= rel_rms, "%s: rel-RMS %.4g > %.4g" % (what, rr, rel_rms)
+    return rr
+
+
+QCASES = [
+    # name, B, N, H, causal, scale, k offset variance
+    ("one tile", 1, 64, 2, False, 128 ** -0.5, 0.0),
+    ("ragged tail 300", 2, 300, 3, False, 128 ** -0.5, 2.0),
+    ("short 37", 1, 37, 4, False, 128 ** -0.5, 2.0),
+    ("causal 200", 1, 200, 2, True, 128 ** -0.5, 0.0),
+    ("causal ragged 333", 2, 333, 2, True, 0.1, 2.0),
+    ("negative scale", 1, 150, 2, False, -0.05, 0.0),
+    ("several q tiles 700", 1, 700, 2, False, 128 ** -0.5, 2.0),
+]
+
+
+@pytest.mark.parametrize("name,B,N,H,causal,scale,koff", QCASES, ids=[c[0] for c in QCASES])
+def test_quant_prep_and_attention(oracle_mod, name, B, N, H, causal, scale, koff):
+    import paged_kv_gqa_fwd_amd as pa
+    q, k, v = workloads.dense_qkv(900 + N, B, N, H, k_channel_offset_var=koff, device="cuda")
+    prep = _check_prep(q, k, v, oracle_mod, name)
+    ref = oracle_mod.quant_attn(prep, scale, causal)
+    log("  gpu quant attention: %s" % name)
+    out = pa.quant_attention(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    _compare(out, ref, name)
+
+
+def test_quant_strided_inputs(oracle_mod):
+    """q/k/v as strided views (K and V interleaved, as in a paged pool), out
+    with a padded head stride."""
+    import paged_kv_gqa_fwd_amd as pa
+    case = workloads.dit_self_attn(device="cuda", n_tokens=500, heads=4)
+    q, k, v = workloads.dense_from_case(case)
+    assert not k.is_contiguous()
+    prep = _check_prep(q, k, v, oracle_mod, "strided")
+    ref = oracle_mod.quant_attn(prep, case.scale, False)
+    big = torch.zeros((1, 500, 5, 136), dtype=torch.bfloat16, device="cuda")
+    out = big[:, :, 1:5, :128]
+    pa.quant_attention(q, k, v, case.scale, False, out=out)
+    torch.cuda.synchronize()
+    _compare(out, ref, "strided q/k/v/out")
+    assert not big[:, :, 0].any() and not big[:, :, :, 128:].any()
+
+
+def test_quant_dit_full_size_sampled(oracle_mod):
+    """The full video-DiT shape [1, 37810, 56, 128] (non-causal, K channel
+    offsets), in the benchmark's launch configuration: preparation checked
+    bit-exactly in full, attention on sampled query tokens."""
+    import paged_kv_gqa_fwd_amd as pa
+    case = workloads.dit_self_attn(device="cuda")
+    q, k, v = workloads.dense_from_case(case)
+    prep = _check_prep(q, k, v, oracle_mod, "dit full")
+    log("  gpu quant attention: dit full")
+    out = pa.quant_attention(q, k, v, case.scale, False)
+    torch.cuda.synchronize()
+    N = q.shape[1]
+    rows = sorted({0, 1, 63, 64, 127, 128, N - 51, N - 50, N - 1} |
+                  set(torch.randint(0, N, (7,), generator=torch.Generator().manual_seed(5)).tolist()))
+    mask = np.zeros(N, dtype=np.uint8)
+    mask[rows] = 1
+    ref = oracle_mod.quant_attn(prep, case.scale, False, row_mask=mask)
+    _compare(out, ref, "dit full, %d sampled tokens" % len(rows), rows=np.array(rows))
+    del case, q, k, v, out
+    torch.cuda.empty_cache()
+
+
+def test_quant_run_to_run_bitwise():
+    import paged_kv_gqa_fwd_amd as pa
+    q, k, v = workloads.dense_qkv(950, 1, 400, 2, k_channel_offset_var=2.0, device="cuda")
+    a = pa.quant_attention(q, k, v, 0.09, False).clone()
+    b = pa.quant_attention(q, k, v, 0.09, False).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -270,6 +270,34 @@ def dit_self_attn(device="cpu", seed: int = 105, n_tokens: int = 37810, heads: i
                      causal=False, k_channel_offset_var=2.0, device=device)
 
 
+def dense_from_case(case: PagedCase):
+    """Dense [1, N, H, D] views (q, k, v) of a one-sequence self-attention case
+    (n = L): the pages are gathered in block-table order, K and V stay
+    interleaved (strided views)."""
+    assert case.n_seqs == 1 and case.q_lens[0] == case.kv_lens[0]
+    N = case.kv_lens[0]
+    P = case.kv.shape[1]
+    npg = (N + P - 1) // P
+    idx = case.block_table[0, :npg].to(torch.long).to(case.kv.device)
+    kv = case.kv.index_select(0, idx).reshape(npg * P, *case.kv.shape[2:])[:N]
+    return case.q[None], kv[None, :, :, 0, :], kv[None, :, :, 1, :]
+
+
+def dense_qkv(seed: int, batch: int, n: int, heads: int, head_dim: int = 128,
+              k_channel_offset_var: float = 0.0, device="cpu"):
+    """Seeded dense bf16 q, k, v [B, N, H, D] ~ N(0, 1); K optionally plus a
+    per-(batch, head, channel) offset ~ N(0, k_channel_offset_var) added
+    before rounding.  Draw order: q, k, v, offset (CPU generator)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (batch, n, heads, head_dim)
+    q = torch.randn(shape, generator=g)
+    k = torch.randn(shape, generator=g)
+    v = torch.randn(shape, generator=g)
+    if k_channel_offset_var > 0:
+        k = k + torch.randn((batch, 1, heads, head_dim), generator=g) * math.sqrt(k_channel_offset_var)
+    return tuple(t.to(torch.bfloat16).to(device) for t in (q, k, v))
+
+
 WORKLOADS = {
     "tiny_mixed": tiny_mixed,
     "decode_batch": decode_batch,
