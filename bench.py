@@ -160,6 +160,27 @@ def run_quant(steps, warmup):
             "path": "quant (int8 QK, fp8 PV)"}
 
 
+def measured_traffic(kernel_files, profile_name):
+    """HBM bytes per launch of the dominant kernel from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary, each scaled by what the same
+    counter read for a plain 1 GiB copy.  None when no summary exists or the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    h = hashlib.sha1()
+    for f in kernel_files:
+        h.update(open(os.path.join(ROOT, "paged_kv_gqa_fwd_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != d.get("kernel_sources_sha1"):
+        return None
+    copy_kib = d["copy_bytes_per_dispatch"] / 1024.0
+    fetch = d["fetch_kib_per_dispatch"] * copy_kib / d["copy_fetch_kib_per_dispatch"]
+    write = d["write_kib_per_dispatch"] * copy_kib / d["copy_write_kib_per_dispatch"]
+    return round((fetch + write) * 1024.0)
+
+
 def summarize(res):
     name = res["workload"]
     if BOUND[name] == "hbm":
@@ -244,6 +265,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--path", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (torch copy_) five times: "
+                         "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -252,6 +276,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
+                          "bytes_written_per_launch": n, "launches": 5}), flush=True)
+        return
     torch.manual_seed(0)
     prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path)
     s = summarize(prim)
@@ -272,8 +306,12 @@ def main():
         torch.cuda.empty_cache()
     bound = BOUND[args.workload]
     if bound == "hbm":
+        traffic = None
+        if args.workload == "decode_batch" and "split" in prim["path"]:
+            traffic = measured_traffic(["decode_split.hip", "attn_device.h"],
+                                       "paged_decode_split_kernel__decode_batch.traffic.json")
         roof = {"bound": "hbm", "achieved": s["main_kernel_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(s["main_kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(s["main_kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "paged_decode_split_kernel" if "split" in prim["path"] else "paged_prefill_kernel",
                 "kernel_ms": s["main_kernel_ms"]}
     else:
