@@ -254,6 +254,48 @@ def _prefix_case(case, k):
                    q_lens=case.q_lens[:k], kv_lens=case.kv_lens[:k])
 
 
+def calibrate_gemm(n=16384, iters=20):
+    """Vendor GEMM throughput (hipBLASLt through torch) at n x n x n.  MFMA
+    power depends on the data: random operands run at a lower clock than
+    constant ones, so the random-data rate is the practical ceiling."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(2.0 * n ** 3 / (e0.elapsed_time(e1) / iters) / 1e9, 1)
+
+    res = {"calibration": "gemm", "n": n, "unit": "T(FL)OP/s"}
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    res["bf16_random"] = rate(lambda: a @ b)
+    c = torch.ones_like(a)
+    res["bf16_constant"] = rate(lambda: c @ c)
+    del c
+    try:
+        ai = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8, generator=g)
+        bi = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8, generator=g)
+        res["int8_random"] = rate(lambda: torch._int_mm(ai, bi))
+        del ai, bi
+    except Exception as e:  # the library may not cover this type on the platform
+        res["int8_random"] = "unavailable: %s" % type(e).__name__
+    try:
+        af = a.to(torch.float8_e4m3fn)
+        bf = b.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device="cuda")
+        res["fp8_random"] = rate(lambda: torch._scaled_mm(af, bf, one, one, out_dtype=torch.bfloat16))
+    except Exception as e:
+        res["fp8_random"] = "unavailable: %s" % type(e).__name__
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +310,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (torch copy_) five times: "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--calibrate-gemm", action="store_true",
+                    help="run only the vendor library's large GEMMs (bf16 on random and on constant "
+                         "data, int8, fp8) and print their throughput: the MFMA rate the chip "
+                         "sustains on real data, as context for the prefill and quantised rooflines")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -285,6 +331,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
                           "bytes_written_per_launch": n, "launches": 5}), flush=True)
+        return
+    if args.calibrate_gemm:
+        calibrate_gemm()
         return
     torch.manual_seed(0)
     prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path)

@@ -34,9 +34,14 @@ constexpr int kThreads = 256;  // 4 wave64 per workgroup
 #ifndef PA_DECODE_WAVES_256
 #define PA_DECODE_WAVES_256 1
 #endif
-// Packed query rows per prefill workgroup: 4 waves x 64 rows at D = 128,
-// 4 waves x 32 rows at D = 256.
+// Packed query rows per prefill workgroup: 8 waves x 32 rows (or 4 x 64)
+// at D = 128, 4 waves x 32 rows at D = 256.
 constexpr int prefill_rows(int d) { return d == 128 ? 256 : 128; }
+// Threads per prefill workgroup (two wave64 per SIMD at head_dim 128).
+#ifndef PA_PF_WAVES128
+#define PA_PF_WAVES128 8
+#endif
+constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 256; }
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
 constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
 

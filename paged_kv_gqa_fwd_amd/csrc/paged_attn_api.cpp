@@ -107,6 +107,7 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         const int64_t bm = pa::prefill_rows(d->head_dim);
         const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
+        plan->block_threads = pa::prefill_threads(d->head_dim);
         plan->pages_per_split = (int32_t)MP;
         plan->max_splits = 1;
         plan->grid_x = (int32_t)tiles;

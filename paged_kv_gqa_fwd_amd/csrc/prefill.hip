@@ -9,12 +9,17 @@
 // examples/decode.json manifest (buffers.kv).
 //
 // Design (MI355X):
-//  * One workgroup of 4 wave64 per (sequence, KV head, tile of 256 packed
-//    query rows).  Row r of a (sequence, KV head) is query token r / G,
-//    q head g*G + r % G, so the G heads sharing a KV head share every K/V
-//    tile.  Each wave owns 64 rows as two 32-row MFMA blocks, so every K or
-//    V operand read from LDS feeds two MFMAs: 64 FLOP per LDS byte, half of
-//    the LDS bandwidth the MFMA rate needs with 32 rows per wave.
+//  * One workgroup per (sequence, KV head, tile of packed query rows).  Row
+//    r of a (sequence, KV head) is query token r / G, q head g*G + r % G,
+//    so the G heads sharing a KV head share every K/V tile.  At D = 128 the
+//    workgroup is 8 wave64 (two per SIMD) of 32 rows each: the SIMD
+//    interleaves one wave's softmax VALU work and LDS waits with the other
+//    wave's MFMAs, which one wave per SIMD cannot do for itself.  Each K or
+//    V operand read from LDS then feeds one MFMA (32 FLOP per LDS byte, the
+//    LDS rate the full MFMA rate would need); the variant with 4 waves of
+//    64 rows (two MFMAs per operand, PA_PF_WAVES128=4) measured about 5%
+//    slower.  At D = 256, 4 waves of 32 rows (Q and O of a second block
+//    would not fit the registers).
 //  * K/V pages (64 keys) stream HBM -> LDS with direct 16-byte loads
 //    (global_load_lds_dwordx4), no register staging, through rings of K and
 //    V page buffers with one or two pages in flight beyond the next one.
@@ -36,20 +41,23 @@
 //  * Keys past the causal frontier of the workgroup's last row are never
 //    loaded; steps below the frontier of a wave's first row skip the mask.
 #include "attn_device.h"
+#include "lds_stream.h"
 
 namespace pa {
 
 template <int D>
 struct PfCfg {
-    static constexpr int WAVES = 4;
-    // 32-row MFMA blocks per wave: two at D = 128 (every LDS operand feeds
-    // two MFMAs); one at D = 256, where two blocks' Q and O would not fit
-    // the registers of a lane.
-    static constexpr int RB = D == 128 ? 2 : 1;
+    static constexpr int WAVES = D == 128 ? PA_PF_WAVES128 : 4;
+    static constexpr int THREADS = 64 * WAVES;
+    // 32-row MFMA blocks per wave: two when one wave runs per SIMD (every
+    // LDS operand feeds two MFMAs); one when two waves share a SIMD (their
+    // registers are halved) and at D = 256, where two blocks' Q and O would
+    // not fit the registers of a lane.
+    static constexpr int RB = (D == 128 && WAVES == 4) ? 2 : 1;
     static constexpr int BM = WAVES * RB * 32;      // packed query rows per workgroup
     static constexpr int CH = D / 8;                // 16-byte chunks per K or V row
     static constexpr int TILE = kPage * D;          // bf16 elements of one K (or V) page
-    static constexpr int LOADS = kPage * CH / kThreads;  // 16-byte loads per thread per K page
+    static constexpr int LOADS = kPage * CH / THREADS;  // 16-byte loads per thread per K page
     // Pages in flight beyond the next one, and the K / V ring depths that
     // allow it with the step pipeline below (K of page t+1 and V of page t
     // are read in the same step).
@@ -65,33 +73,8 @@ static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_r
 
 constexpr float kRescaleThreshold = 8.f;   // log2 units: P stays <= 256
 
-__device__ __forceinline__ float max_xor32(float x) {
-    // lanes l and l ^ 32 exchange values (v_permlane32_swap)
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// LDS byte address of a __shared__ pointer (the value M0 takes).
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// One direct 16-byte HBM -> LDS load per lane: lane l's 16 bytes at
-// base + voff land at LDS byte lds + 16 l.  Written as inline assembly so
-// the compiler does not serialise later LDS reads of other ring stages
-// behind it; completion is waited for explicitly (vmcnt) before the
-// barrier that publishes a stage.  M0 is not used for anything else here.
-__device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t voff_bytes) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff_bytes), "s"(base) : "memory");
-}
-
 // Direct HBM -> LDS loads of one page (K and V rows of one KV head).  LDS
-// position p = i*256 + tid of a tile holds key p / CH, physical chunk
+// position p = i*THREADS + tid of a tile holds key p / CH, physical chunk
 // p % CH.  The 16-byte chunks of a row are permuted so that the operand
 // reads hit 32 distinct 4-byte banks per LDS cycle: K chunk c of key k is
 // stored at c ^ (k & 7) (eight keys per b128 read cycle), V chunk c at
@@ -115,21 +98,14 @@ __device__ __forceinline__ void pf_load_page(uint16_t *lds_k, uint16_t *lds_v, c
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const bool ok = pl.key[i] < valid;
-        const int slot = (i * kThreads + w * 64) * 8;   // wave-uniform LDS element offset
+        const int slot = (i * C::THREADS + w * 64) * 8;   // wave-uniform LDS element offset
         dma16(lds_address(lds_k + slot), page_base, ok ? pl.kof[i] : pl.kof0[i]);
         dma16(lds_address(lds_v + slot), vbase, ok ? pl.vof[i] : pl.vof0[i]);
     }
 }
 
-// Page id j of a block-table row, read through the scalar cache (the id is
-// uniform across the workgroup).
-__device__ __forceinline__ int load_page_id(const int32_t *bt_row, int j) {
-    typedef __attribute__((address_space(4))) const int32_t const_i32;
-    return *((const_i32 *)bt_row + j);
-}
-
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(const AttnArgs a) {
     using C = PfCfg<D>;
     __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TILE];
@@ -202,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
     PageLoad<D> pl;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const int p = i * kThreads + tid;
+        const int p = i * C::THREADS + tid;
         const int key = p / C::CH;
         const int ck = (p % C::CH) ^ (key & 7);
         const int cv = (p % C::CH) ^ (2 * (key & 3));
@@ -469,7 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_prefill_kernel(const AttnAr
 
 template <int D>
 hipError_t launch_prefill(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL(paged_prefill_kernel<D>, grid, dim3(kThreads), 0, stream, a);
+    static_assert(PfCfg<D>::THREADS == prefill_threads(D), "workgroup size");
+    hipLaunchKernelGGL(paged_prefill_kernel<D>, grid, dim3(PfCfg<D>::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@
 //    (unit scales); l sums the unrounded 448 w.
 #include "attn_device.h"
 #include "quant_device.h"
+#include "lds_stream.h"
 
 namespace pa {
 
@@ -201,18 +202,6 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const QuantArgs a) {
 }
 
 // ---------------------------------------------------------------- attention
-// LDS byte address of a __shared__ pointer (the value M0 takes).
-__device__ __forceinline__ uint32_t q_lds_address(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-// One direct 16-byte HBM -> LDS load per lane (lane l lands at lds + 16 l);
-// completion is waited for explicitly (vmcnt) before the barrier that
-// publishes a stage.  M0 is not used for anything else in this kernel.
-__device__ __forceinline__ void q_dma16(uint32_t lds, const void *base, uint32_t voff_bytes) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff_bytes), "s"(base) : "memory");
-}
-
 // Wave-uniform f32 read through the scalar cache.
 __device__ __forceinline__ float load_scalar_f32(const float *p) {
     typedef __attribute__((address_space(4))) const float const_f32;
@@ -287,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
             const int slot = (i * 256 + w * 64) * 16;
             // keys past the end re-read key 0 of the tile (always valid)
             const uint32_t ko = kkey[i] < valid ? koff[i] : koff[i] - (uint32_t)(kkey[i] * a.h * D);
-            q_dma16(q_lds_address(&sk[st][slot]), kt, ko);
-            q_dma16(q_lds_address(&sv[st][slot]), vt, voff[i]);
+            dma16(lds_address(&sk[st][slot]), kt, ko);
+            dma16(lds_address(&sv[st][slot]), vt, voff[i]);
         }
     };
     int issued = -1;
@@ -358,10 +347,7 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
                 sf[kb][i] = s;
                 mx = fmaxf(mx, s);
             }
-        {
-            auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        }
+        mx = max_xor32(mx);
         const float f = fbase * load_scalar_f32(a.sk + ((int64_t)b * a.h + h) * a.blocks + t);
         const float mt = mx * f;   // -inf stays -inf (f > 0)
         const float m_new = fmaxf(m_run, mt);
@@ -400,11 +386,7 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
     }
 
     // out = O * s_v / (448 l) = O * s_v / l_part (l_part sums 448 w)
-    float l_row;
-    {
-        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-        l_row = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
+    const float l_row = sum_xor32(l_part);
     if (!row_ok) return;
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const float *svp = a.sv + ((int64_t)b * a.h + h) * D;
