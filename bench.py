@@ -128,7 +128,8 @@ def run_workload(name, steps, warmup, pps=0, path=0):
     res = {
         "workload": name, "case": case, "ms_per_step": step_ms,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
-        "path": "split_decode+combine" if plan.path == pa.PATH_SPLIT_DECODE else "prefill",
+        "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
+                 pa.PATH_PREFILL: "prefill"}[plan.path],
         "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
         "bytes": algorithmic_bytes(case), "flops": algorithmic_flops(case),
     }
@@ -347,7 +348,8 @@ def main():
             secondary.append(ss)
             torch.cuda.empty_cache()
             continue
-        r = run_workload(name, max(3, args.steps // 2), max(1, args.warmup // 2))
+        sec_path = args.path if args.path != 2 and BOUND[name] == "hbm" else 0   # 2 = prefill
+        r = run_workload(name, max(3, args.steps // 2), max(1, args.warmup // 2), path=sec_path)
         ss = summarize(r)
         log("[bench] %s" % json.dumps(ss))
         secondary.append(ss)

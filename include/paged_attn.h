@@ -89,12 +89,18 @@ typedef struct attn_paged_plan {
     int32_t grid_x, grid_y, grid_z;
     int32_t block_threads;
     size_t workspace_bytes;    /* bytes of workspace the call needs (0 if none) */
+    size_t counter_bytes;      /* leading workspace bytes holding merge counters (0 if none) */
 } attn_paged_plan;
 
 enum {
     ATTN_PATH_AUTO = 0,
     ATTN_PATH_SPLIT_DECODE = 1, /* split-KV partial kernel + log-sum-exp combine kernel */
-    ATTN_PATH_PREFILL = 2       /* q-tile kernel with causal tile skipping, one pass */
+    ATTN_PATH_PREFILL = 2,      /* q-tile kernel with causal tile skipping, one pass */
+    ATTN_PATH_SPLIT_FUSED = 3   /* split-KV kernel whose last split per (sequence, KV head)
+                                   merges the partials: one launch (decode.json's single
+                                   launch with an i32 counter scratch, ops.decode.impl).
+                                   Same bits as ATTN_PATH_SPLIT_DECODE; AUTO picks the
+                                   two-kernel form, which measured faster on MI355X. */
 };
 
 /*
@@ -137,7 +143,15 @@ int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int3
  *   causal       nonzero = bottom-right aligned causal mask.
  *   workspace    device buffer of >= attn_paged_workspace_bytes bytes,
  *                256-byte aligned (may be NULL when that size is 0); holds
- *                split-KV partials between the two kernels of the split path.
+ *                the split-KV partials and, on the fused split path, the
+ *                merge counters in its first plan.counter_bytes bytes.  Those
+ *                counter bytes must be zero when the call starts; every call
+ *                that runs to completion leaves them zero again.  A buffer
+ *                from a zeroing allocator, or one cleared once with
+ *                attn_workspace_clear, qualifies; after a call on another
+ *                path or a larger plan has used the same bytes for partials,
+ *                clear them again.  Calls that share a workspace must not
+ *                overlap in time.
  *   stream       hipStream_t to enqueue on (NULL = default stream).
  */
 int attn_paged_fwd(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
@@ -155,6 +169,16 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
                       float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream, int32_t path_hint,
                       int32_t pages_per_split);
+
+/*
+ * attn_workspace_clear -- enqueue a kernel that sets bytes [0, bytes) of a
+ * device workspace to zero (the merge counters of the fused split path must
+ * start at zero).  A kernel, not a memset node, so that graph capture of it
+ * replays correctly.  workspace: 4-byte aligned device pointer (NULL only
+ * with bytes == 0); bytes: a multiple of 4.  Returns ATTN_OK, ATTN_ERR_NULL,
+ * ATTN_ERR_ALIGN, ATTN_ERR_SHAPE (bytes not a multiple of 4) or ATTN_ERR_HIP.
+ */
+int attn_workspace_clear(void *workspace, size_t bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Quantised attention (int8 Q.K, fp8 P.V) over dense Q, K, V.

@@ -19,8 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 
 PATH_AUTO = 0
-PATH_SPLIT_DECODE = 1
+PATH_SPLIT_DECODE = 1   # split-KV kernel + combine kernel
 PATH_PREFILL = 2
+PATH_SPLIT_FUSED = 3    # split-KV kernel whose last split per (sequence, KV head) merges
 
 ATTN_OK = 0
 
@@ -81,6 +82,7 @@ class attn_paged_plan(ctypes.Structure):
         ("grid_z", ctypes.c_int32),
         ("block_threads", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("counter_bytes", ctypes.c_size_t),
     ]
 
 
@@ -106,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_make_plan.restype = ctypes.c_int
     lib.attn_paged_workspace_bytes.argtypes = [dims_p, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_paged_workspace_bytes.restype = ctypes.c_int
+    lib.attn_workspace_clear.argtypes = [p, sz, p]
+    lib.attn_workspace_clear.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_kernel_timing_enable.argtypes = [i32]
@@ -169,16 +173,35 @@ def make_plan(dims: attn_paged_dims, n_seqs: int, max_q: int, path: int = PATH_A
     return plan
 
 
+class _CachedWorkspace:
+    """One device workspace per device, grown on demand.  `clean` counts the
+    leading bytes known to be zero: the fused split path needs its counter
+    bytes zero on entry and leaves them zero, while partials written by any
+    split call dirty everything past that call's counter bytes."""
+
+    def __init__(self):
+        self.buf = None
+        self.clean = 0
+
+
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
+def _workspace(nbytes: int, device) -> _CachedWorkspace:
     key = (str(device),)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
-    return buf
+    ws = _ws_cache.setdefault(key, _CachedWorkspace())
+    if ws.buf is None or ws.buf.numel() < nbytes:
+        ws.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws.clean = ws.buf.numel()
+    return ws
+
+
+def workspace_clear(workspace: torch.Tensor, nbytes: int, stream=None) -> None:
+    """Zero the first ``nbytes`` of a workspace (``attn_workspace_clear``)."""
+    st = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    rc = load_library().attn_workspace_clear(workspace.data_ptr(), int(nbytes), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
 
 
 def _check_device_tensor(name, t, dtype):
@@ -198,7 +221,11 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
 
     q [T, Hq, D] bf16, kv_pool [NP, P, Hkv, 2, D] bf16 view, block_table
     [B, MP] int32, seq_lens [B] int32, cu_q [B+1] int32 (all on the GPU).
-    Returns ``out`` (allocated as zeros when not given).
+    Returns ``out`` (allocated as zeros when not given).  Without
+    ``workspace`` a cached per-device buffer is used (its merge counters are
+    kept zero); a caller-supplied ``workspace`` must have its first
+    ``plan.counter_bytes`` bytes zero on the fused split path (see
+    ``workspace_clear``).
     """
     lib = load_library()
     for name, t, dt in (("q", q, torch.bfloat16), ("kv_pool", kv_pool, torch.bfloat16),
@@ -215,12 +242,15 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
         raise ValueError("cu_q must have n_seqs + 1 entries and block_table >= n_seqs rows")
     dims = make_dims(q, kv_pool, block_table, out)
     plan = make_plan(dims, n_seqs, max_q, path, pages_per_split)
-    ws_ptr, ws_bytes = None, 0
+    ws_ptr, ws_bytes, cached = None, 0, None
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     if plan.workspace_bytes:
         if workspace is None:
-            workspace = _workspace(plan.workspace_bytes, q.device)
+            cached = _workspace(plan.workspace_bytes, q.device)
+            workspace = cached.buf
+            if cached.clean < plan.counter_bytes:
+                workspace_clear(workspace, plan.counter_bytes, st)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     rc = lib.attn_paged_fwd_ex(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(),
                                block_table.data_ptr(), seq_lens.data_ptr(), cu_q.data_ptr(),
                                n_seqs, int(max_q), float(scale), int(bool(causal)),
@@ -228,6 +258,8 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
                                int(path), int(pages_per_split))
     if rc != ATTN_OK:
         raise AttnError(rc)
+    if cached is not None:
+        cached.clean = plan.counter_bytes
     return out
 
 
@@ -327,7 +359,9 @@ def quant_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: fl
     dims = make_quant_dims(q, k, v, out)
     lay = quant_layout(dims)
     if workspace is None:
-        workspace = _workspace(lay.workspace_bytes, q.device)
+        cached = _workspace(lay.workspace_bytes, q.device)
+        cached.clean = 0   # the quantised intermediates overwrite it
+        workspace = cached.buf
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     rc = lib.attn_quant_fwd(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             ctypes.byref(dims), float(scale), int(bool(causal)), workspace.data_ptr(),

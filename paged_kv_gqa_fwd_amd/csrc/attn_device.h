@@ -55,6 +55,7 @@ struct AttnArgs {
     const int32_t *cu_q;        // [B + 1]
     float *part_o;              // f32 [T, Hq, S, D] split partials (unnormalised)
     float *part_ml;             // f32 [T, Hq, S, 2] split (max in log2 units, sum)
+    int32_t *counters;          // [B, Hkv] arrival counters of the in-kernel merge (zero between calls)
     int64_t q_st, q_sh, o_st, o_sh;
     int64_t kv_sp, kv_ss, kv_sh, kv_skv;
     int64_t bt_stride;
@@ -64,6 +65,7 @@ struct AttnArgs {
     float scale_log2;           // scale * log2(e): scores live in log2 units
     float scale_log2_pos;       // max(|scale| * log2(e), FLT_MIN) (prefill kernel)
     int32_t q_negate;           // scale < 0: the prefill kernel negates Q instead
+    int32_t fuse_merge;         // split path: the last split of each (sequence, KV head) merges
 };
 
 struct CombineArgs {

@@ -4,8 +4,10 @@
 // examples/decode.json manifest (ops.decode.impl.scratch: per-split partial
 // outputs and per-row (max, sum) statistics, grid.x = KV splits per
 // (KV head, sequence)) and the Mojo SM100MHA2Q docs (PartitionType: KV-cache
-// partition scheme; MaskType: causal or unmasked).  The pages' kernels fuse
-// the merge through a counter; here it is a second, separate kernel.
+// partition scheme; MaskType: causal or unmasked).  The splits are merged
+// either by a second, separate kernel or, like the manifest's single launch
+// with its i32 counter scratch (ops.decode.impl.scratch.counter), by the
+// last workgroup of each (sequence, KV head) to finish its split.
 //
 // Design (MI355X): one workgroup of 4 wave64 per (KV head, sequence, split).
 // The split's pages stream through LDS with 16-byte coalesced loads, staged
@@ -17,6 +19,14 @@
 #include "attn_device.h"
 
 namespace pa {
+
+// Device-scope (all XCDs) relaxed store / load of a float.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int D>
 struct DecodeCfg {
@@ -281,16 +291,71 @@ void paged_decode_split_kernel(const AttnArgs a) {
             // so the workspace scales with n_seqs * max_q
             const int64_t prow = (int64_t)b * a.max_q + ri;
             const int64_t slot = (prow * a.hq + rh) * a.max_splits + s;
-            a.part_o[slot * D + d] = osum;
-            if (d == 0) {
-                a.part_ml[slot * 2 + 0] = Mr;
-                a.part_ml[slot * 2 + 1] = lsum;
+            if (a.fuse_merge) {
+                // read by another workgroup of this launch: device-coherent
+                store_coherent(a.part_o + slot * D + d, osum);
+                if (d == 0) {
+                    store_coherent(a.part_ml + slot * 2 + 0, Mr);
+                    store_coherent(a.part_ml + slot * 2 + 1, lsum);
+                }
+            } else {
+                a.part_o[slot * D + d] = osum;
+                if (d == 0) {
+                    a.part_ml[slot * 2 + 0] = Mr;
+                    a.part_ml[slot * 2 + 1] = lsum;
+                }
             }
         } else {
             const float o = lsum > 0.f ? osum / lsum : 0.f;
             a.out[t * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(o);
         }
     }
+    if (!split || !a.fuse_merge) return;
+
+    // ---- in-kernel merge ---------------------------------------------------
+    // Every split of (b, g) that ran takes a ticket once its partials are
+    // visible device-wide; the one that draws the last ticket merges all of
+    // them in split order (the combine kernel's arithmetic, so both forms
+    // give the same bits) and returns the counter to zero for the next call.
+    // Nothing waits on another workgroup, so no ordering of workgroups can
+    // stall the grid.
+    //
+    // Visibility without cache-wide fences: the partials are written with
+    // device-scope stores (written through each XCD's L2 to the device
+    // coherence point) and read back with device-scope loads (served from
+    // that point, not from a stale L2 copy), so waiting for this workgroup's
+    // stores to complete before the ticket is taken is all the ordering the
+    // merge needs.  A device-scope fence would write back and invalidate the
+    // whole L2 of the XCD in every workgroup instead.
+    __shared__ int s_last;
+    const int ns = max(1, min(a.max_splits, (npages + a.pages_per_split - 1) / a.pages_per_split));
+    int32_t *counter = a.counters + (int64_t)b * a.hkv + g;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores completed
+    __syncthreads();                                    // ... and every wave's
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+    __syncthreads();
+    if (!s_last) return;
+    for (int r = tid / D; r < rows; r += RSTEP) {
+        const int ri = r / G;
+        const int rh = g * G + (r - ri * G);
+        const int64_t base = (((int64_t)b * a.max_q + ri) * a.hq + rh) * a.max_splits;
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, load_coherent(a.part_ml + (base + s2) * 2));
+        float acc = 0.f, lsum = 0.f;
+        if (M != -INFINITY) {
+            for (int s2 = 0; s2 < ns; ++s2) {
+                const float ms = load_coherent(a.part_ml + (base + s2) * 2);
+                const float ls = load_coherent(a.part_ml + (base + s2) * 2 + 1);
+                const float wgt = exp2_fast(ms - M);   // ms = -inf gives 0
+                lsum += wgt * ls;
+                acc += wgt * load_coherent(a.part_o + (base + s2) * D + d);
+            }
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        a.out[(q0 + ri) * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(acc * inv);
+    }
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Log-sum-exp merge of the split partials: per (token, q head) row,
@@ -350,6 +415,19 @@ template <int D>
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
     dim3 grid((a.hq + 3) / 4, a.max_q, a.n_seqs);
     hipLaunchKernelGGL(paged_combine_kernel<D>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Zero n 32-bit words (the merge counters of a workspace).
+__global__ __launch_bounds__(kThreads) void workspace_clear_kernel(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+        p[i] = 0u;
+}
+
+hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream) {
+    if (words == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((words + kThreads - 1) / kThreads, 1024);
+    hipLaunchKernelGGL(workspace_clear_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, words);
     return hipGetLastError();
 }
 

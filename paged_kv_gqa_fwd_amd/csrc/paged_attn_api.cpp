@@ -19,6 +19,7 @@
 namespace pa {
 hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
+hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream);
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_quant_prep(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_quant_attn(const QuantArgs &a, hipStream_t stream);
@@ -70,19 +71,23 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     int rc = validate_dims(d, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
     if (!plan) return ATTN_ERR_NULL;
-    if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_PREFILL) return ATTN_ERR_SHAPE;
+    if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_SPLIT_FUSED) return ATTN_ERR_SHAPE;
     if (pps < 0) return ATTN_ERR_SHAPE;
     const int G = d->num_q_heads / d->num_kv_heads;
     const int64_t mq = std::max<int32_t>(max_q, 1);
     int path = path_hint;
     if (path == ATTN_PATH_AUTO)
+        // The two-kernel split form measured faster than the single-launch
+        // merge on MI355X (the merge form makes every workgroup wait for its
+        // write-through partial stores and the ticket atomic before it ends).
         path = (mq * G <= kMaxDecodeRows) ? ATTN_PATH_SPLIT_DECODE : ATTN_PATH_PREFILL;
-    if (path == ATTN_PATH_SPLIT_DECODE && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
+    const bool split_path = path == ATTN_PATH_SPLIT_DECODE || path == ATTN_PATH_SPLIT_FUSED;
+    if (split_path && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
     *plan = attn_paged_plan{};
     plan->path = path;
     plan->block_threads = pa::kThreads;
     const int64_t MP = d->max_pages_per_seq;
-    if (path == ATTN_PATH_SPLIT_DECODE) {
+    if (split_path) {
         int64_t p = pps;
         if (p == 0) {
             // one workgroup per SIMD-wave slot: 4 waves = one per SIMD
@@ -101,7 +106,10 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         plan->grid_z = (int32_t)S;
         if (S > 1) {
             const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads * (size_t)S;
-            plan->workspace_bytes = align_up(rows * (size_t)d->head_dim * 4, kWsAlign) + align_up(rows * 8, kWsAlign);
+            if (path == ATTN_PATH_SPLIT_FUSED)
+                plan->counter_bytes = align_up((size_t)std::max<int32_t>(n_seqs, 1) * (size_t)d->num_kv_heads * 4, kWsAlign);
+            plan->workspace_bytes = plan->counter_bytes + align_up(rows * (size_t)d->head_dim * 4, kWsAlign) +
+                                    align_up(rows * 8, kWsAlign);
         }
     } else {
         const int64_t bm = pa::prefill_rows(d->head_dim);
@@ -195,9 +203,13 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
     a.scale_log2_pos = std::max((float)(std::fabs((double)scale) * 1.4426950408889634), FLT_MIN);
     a.q_negate = scale < 0.f ? 1 : 0;
     if (plan.workspace_bytes > 0) {
+        // [merge counters | partial O | partial (m, l)], each 256-byte aligned
         const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
-        a.part_o = static_cast<float *>(workspace);
-        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(rows * (size_t)D * 4, kWsAlign));
+        char *ws = static_cast<char *>(workspace);
+        a.counters = reinterpret_cast<int32_t *>(ws);
+        a.part_o = reinterpret_cast<float *>(ws + plan.counter_bytes);
+        a.part_ml = reinterpret_cast<float *>(ws + plan.counter_bytes + align_up(rows * (size_t)D * 4, kWsAlign));
+        a.fuse_merge = plan.path == ATTN_PATH_SPLIT_FUSED ? 1 : 0;
     }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -205,8 +217,8 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
     const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
     if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
-    hipError_t e = plan.path == ATTN_PATH_SPLIT_DECODE ? pa::launch_decode_split_any(D, a, grid, st)
-                                                      : pa::launch_prefill_any(D, a, grid, st);
+    hipError_t e = plan.path == ATTN_PATH_PREFILL ? pa::launch_prefill_any(D, a, grid, st)
+                                                 : pa::launch_decode_split_any(D, a, grid, st);
     if (e != hipSuccess) return ATTN_ERR_HIP;
     if (timing && record_event(&t_main.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
     const bool need_combine = plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1;
@@ -398,6 +410,17 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
     return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale,
                           causal, dims, workspace, workspace_bytes, stream, path_hint,
                           pages_per_split);
+}
+
+int attn_workspace_clear(void *workspace, size_t bytes, void *stream) {
+    if (bytes == 0) return ATTN_OK;
+    if (!workspace) return ATTN_ERR_NULL;
+    if (!aligned4(workspace)) return ATTN_ERR_ALIGN;
+    if (bytes % 4) return ATTN_ERR_SHAPE;
+    if (pa::launch_workspace_clear(static_cast<uint32_t *>(workspace), bytes / 4,
+                                   static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 int attn_kernel_timing_enable(int32_t enable) {

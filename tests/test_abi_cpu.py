@@ -35,7 +35,8 @@ def test_header_declares_entry_points():
     fns = header_functions()
     for name in ("attn_paged_fwd", "attn_paged_fwd_ex", "attn_paged_make_plan",
                  "attn_paged_workspace_bytes", "attn_status_string", "attn_quant_fwd",
-                 "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of"):
+                 "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of",
+                 "attn_workspace_clear"):
         assert name in fns
 
 
@@ -117,11 +118,12 @@ def test_forced_split_path_row_limit(pa):
 def test_workspace_checks(pa):
     import paged_kv_gqa_fwd_amd as mod
     d = dims(max_pages_per_seq=128, bt_stride=128)
-    plan = mod.make_plan(d, 64, 1)
-    assert plan.path == mod.PATH_SPLIT_DECODE and plan.max_splits > 1 and plan.workspace_bytes > 0
-    assert call(pa, d, n_seqs=64) == E_WS                                   # missing
-    assert call(pa, d, n_seqs=64, ws=FAKE + 16, ws_bytes=1 << 30) == E_WS   # misaligned
-    assert call(pa, d, n_seqs=64, ws=FAKE, ws_bytes=plan.workspace_bytes - 1) == E_WS
+    plan = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_FUSED)
+    assert plan.path == mod.PATH_SPLIT_FUSED and plan.max_splits > 1 and plan.workspace_bytes > 0
+    assert call(pa, d, n_seqs=64, path=3) == E_WS                           # missing
+    assert call(pa, d, n_seqs=64, path=3, ws=FAKE + 16, ws_bytes=1 << 30) == E_WS   # misaligned
+    assert call(pa, d, n_seqs=64, path=3, ws=FAKE, ws_bytes=plan.workspace_bytes - 1) == E_WS
+    assert call(pa, d, n_seqs=64) == E_WS             # the two-kernel split path needs one too
 
 
 def test_zero_sequences_is_noop(pa):
@@ -132,12 +134,22 @@ def test_plan_paths_and_sizes(pa):
     import paged_kv_gqa_fwd_amd as mod
     # decode batch: 64 seqs, G=4, MP=128 -> split decode
     d = dims(max_pages_per_seq=128, bt_stride=128)
-    p = mod.make_plan(d, 64, 1)
-    assert p.path == mod.PATH_SPLIT_DECODE
+    assert mod.make_plan(d, 64, 1).path == mod.PATH_SPLIT_DECODE
+    p = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_FUSED)
+    assert p.path == mod.PATH_SPLIT_FUSED
     assert p.grid_z == p.max_splits and p.grid_x == 8 and p.grid_y == 64
     assert p.max_splits == -(-128 // p.pages_per_split)
     rows = 64 * 1 * 32 * p.max_splits
-    assert p.workspace_bytes >= rows * 128 * 4 + rows * 8
+    # one i32 merge counter per (sequence, KV head), ahead of the partials
+    assert p.counter_bytes == 64 * 8 * 4
+    assert p.workspace_bytes >= p.counter_bytes + rows * 128 * 4 + rows * 8
+    # the two-kernel split path: same splits, no counters
+    pc = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE)
+    assert pc.path == mod.PATH_SPLIT_DECODE and pc.counter_bytes == 0
+    assert (pc.pages_per_split, pc.max_splits) == (p.pages_per_split, p.max_splits)
+    assert pc.workspace_bytes == p.workspace_bytes - p.counter_bytes
+    # counters round up to 256 bytes
+    assert mod.make_plan(d, 3, 1, mod.PATH_SPLIT_FUSED).counter_bytes == 256
     # many query rows -> prefill, no workspace
     d2 = dims(num_q_heads=24, num_kv_heads=4, head_dim=256, q_stride_token=24 * 256,
               q_stride_head=256, o_stride_token=24 * 256, o_stride_head=256, num_tokens=4096,
@@ -149,6 +161,8 @@ def test_plan_paths_and_sizes(pa):
     # forced split sizes are clamped to [1, MP]
     p3 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 1000)
     assert p3.pages_per_split == 128 and p3.max_splits == 1 and p3.workspace_bytes == 0
+    p3f = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_FUSED, 1000)
+    assert p3f.max_splits == 1 and p3f.workspace_bytes == 0 and p3f.counter_bytes == 0
     p4 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 3)
     assert p4.pages_per_split == 3 and p4.max_splits == 43
     # long decode: 128 seqs x 512 pages, 2 KV heads -> at least 16 splits' worth of workgroups
@@ -167,6 +181,14 @@ def test_workspace_bytes_query(pa):
     assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, ctypes.byref(n)) == OK
     assert n.value == pa.make_plan(d, 64, 1).workspace_bytes
     assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, None) == E_NULL
+
+
+def test_workspace_clear_validates(pa):
+    lib = pa.load_library()
+    assert lib.attn_workspace_clear(None, 0, None) == OK          # nothing to do
+    assert lib.attn_workspace_clear(None, 256, None) == E_NULL
+    assert lib.attn_workspace_clear(0x1002, 256, None) == E_ALIGN
+    assert lib.attn_workspace_clear(0x1000, 6, None) == E_SHAPE
 
 
 def test_status_strings(pa):
