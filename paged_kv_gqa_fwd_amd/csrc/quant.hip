@@ -333,20 +333,26 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
         }
         // scores (raw, f32) with the mask; sacc[kb][i] is key 64t + 32kb + 8(i/4) + 4hi + i%4
         float sf[2][16];
-        const bool need_mask = (t + 1) * kQuantBlock > w_full;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sf[kb][i] = (float)sacc[kb][i];
+        // Only the diagonal and tail tiles need the mask: one wave-uniform
+        // branch around the whole loop, so that the other tiles do not pay
+        // for it (a per-element select costs three VALU instructions a score).
+        if ((t + 1) * kQuantBlock > w_full) {
+            const int lim = vis - (t * kQuantBlock + 4 * hi);   // key offset o is visible iff o < lim
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    sf[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3)) < lim ? sf[kb][i] : -INFINITY;
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (float)sacc[kb][i];
-                if (need_mask) {
-                    const int key = t * kQuantBlock + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    s = key < vis ? s : -INFINITY;
-                }
-                sf[kb][i] = s;
-                mx = fmaxf(mx, s);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sf[kb][i]);
         mx = max_xor32(mx);
         const float f = fbase * load_scalar_f32(a.sk + ((int64_t)b * a.h + h) * a.blocks + t);
         const float mt = mx * f;   // -inf stays -inf (f > 0)
