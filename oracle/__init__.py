@@ -7,7 +7,7 @@ next to this file is compiled by ``gcc`` on its own.
 
 ``paged_attn`` is masked softmax attention written out as its definition
 (see the header of ``paged_attn_oracle.c`` for the formula and the pages it
-follows).  ``quant_prep`` / ``quant_attn`` emulate the int8 Q.K / fp8 P.V
+follows); ``kv_write`` is the cache write that precedes it, a plain scatter.  ``quant_prep`` / ``quant_attn`` emulate the int8 Q.K / fp8 P.V
 quantised variant step by step (``quant_oracle.c``); the rounding of the
 softmax weights to fp8 inside the fused loop is "parity unpinned": the page
 names that step but not its arithmetic.
@@ -108,6 +108,37 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
     if rc != 0:
         raise RuntimeError("oracle_paged_attn failed with status %d" % rc)
     return (out, lse) if return_lse else out
+
+
+def kv_write(kv_pool, k_new, v_new, block_table, seq_lens, cu_q):
+    """The KV-cache write that runs just before attention (metrale blueprint
+    graph.json: node l3.attn.kv_write precedes l3.attn.attend), into the paged
+    layout of kern-kernels examples/decode.json (buffers kv / table / seq /
+    cuq).  Returns a new pool; the input pool is not modified.
+
+    For sequence b with n = cu_q[b+1] - cu_q[b] new tokens and L = seq_lens[b]
+    keys in all (the new ones included), new token i (row t = cu_q[b] + i) is
+    key position pos = L - n + i: its K row k_new[t, g, :] and V row
+    v_new[t, g, :] of every KV head g go to page block_table[b][pos // P],
+    slot pos % P.  Tokens with pos < 0 (more new tokens than keys) have no
+    place in the cache and are not written.
+
+    kv_pool: bf16 [NP, P, Hkv, 2, D] CPU view; k_new, v_new: bf16 [T, Hkv, D].
+    """
+    pool = kv_pool.clone()
+    P = pool.shape[1]
+    bt = block_table.to(torch.int64)
+    for b in range(seq_lens.numel()):
+        t0, t1, L = int(cu_q[b]), int(cu_q[b + 1]), int(seq_lens[b])
+        n = t1 - t0
+        for i in range(n):
+            pos = L - n + i
+            if pos < 0:
+                continue
+            page, slot = int(bt[b, pos // P]), pos % P
+            pool[page, slot, :, 0, :] = k_new[t0 + i]
+            pool[page, slot, :, 1, :] = v_new[t0 + i]
+    return pool
 
 
 QBLOCK = 64  # tokens per int8 scale block

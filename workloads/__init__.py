@@ -270,6 +270,25 @@ def dit_self_attn(device="cpu", seed: int = 105, n_tokens: int = 37810, heads: i
                      causal=False, k_channel_offset_var=2.0, device=device)
 
 
+def new_kv_tokens(case: PagedCase, seed: int, layout: str = "separate"):
+    """Seeded K and V rows for the step's new tokens: bf16 [T, Hkv, D] each
+    (T = the q rows of the case).  layout "separate" gives two contiguous
+    tensors; "fused_qkv" gives strided views into one [T, Hq + 2 Hkv, D]
+    projection output (q heads first, then K heads, then V heads), as a fused
+    QKV projection would leave them."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    T, hq, d = case.q.shape
+    hkv = case.num_kv_heads
+    dev = case.q.device
+    if layout == "separate":
+        k = _randn_bf16((T, hkv, d), gen, "cpu")
+        v = _randn_bf16((T, hkv, d), gen, "cpu")
+        return k.to(dev), v.to(dev)
+    assert layout == "fused_qkv"
+    qkv = _randn_bf16((T, hq + 2 * hkv, d), gen, "cpu").to(dev)
+    return qkv[:, hq:hq + hkv, :], qkv[:, hq + hkv:, :]
+
+
 def dense_from_case(case: PagedCase):
     """Dense [1, N, H, D] views (q, k, v) of a one-sequence self-attention case
     (n = L): the pages are gathered in block-table order, K and V stay
