@@ -136,6 +136,33 @@ def run_workload(name, steps, warmup, pps=0, path=0):
     return res
 
 
+def run_write(name, steps, warmup):
+    """The KV-cache write followed by attention in one call
+    (attn_paged_fwd_write) on a workload's shape, with seeded new K/V rows
+    for every query token.  The line's value is the write kernel's rate:
+    every new K/V byte read once and written once."""
+    import paged_kv_gqa_fwd_amd as pa
+    log("[bench] generating %s (with KV-cache write)" % name)
+    case = workloads.WORKLOADS[name](device="cuda")
+    k_new, v_new = workloads.new_kv_tokens(case, case.seed + 1000)
+    out = torch.empty_like(case.q)
+
+    def step():
+        pa.paged_attention_write(case.q, k_new, v_new, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                 max(case.max_q, 1), case.scale, case.causal, out=out)
+
+    for _ in range(warmup):
+        step()
+    step_ms = _time_steps(step, steps)
+    main_ms, comb_ms, write_ms = _kernel_times(step, steps)
+    written = sum(min(n, L) for n, L in zip(case.q_lens, case.kv_lens))
+    wbytes = 2 * written * case.num_kv_heads * 2 * case.head_dim * 2
+    return {"workload": name + "+kv_write", "value": round(wbytes / (write_ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s (write kernel)", "write_bytes": wbytes, "write_kernel_ms": round(write_ms, 4),
+            "ms_per_step": round(step_ms, 4), "attention_ms": round(main_ms + comb_ms, 4),
+            "path": "kv_write + attention"}
+
+
 def run_quant(steps, warmup):
     """The quantised path (attn_quant_fwd: preparation + fused int8/fp8 loop)
     on the video-DiT shape, same seeded Q/K/V as the bf16 DiT workload."""
@@ -303,7 +330,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant",
+    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant,"
+                                           "decode_batch+kv_write,chunked_prefill+kv_write",
                     help="comma list of extra workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
@@ -342,6 +370,12 @@ def main():
     log("[bench] %s" % json.dumps(s))
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        if name.endswith("+kv_write"):
+            ss = run_write(name[:-len("+kv_write")], max(3, args.steps // 2), max(1, args.warmup // 2))
+            log("[bench] %s" % json.dumps(ss))
+            secondary.append(ss)
+            torch.cuda.empty_cache()
+            continue
         if name == "dit_quant":
             ss = run_quant(max(3, args.steps // 2), max(1, args.warmup // 2))
             log("[bench] %s" % json.dumps(ss))

@@ -170,6 +170,54 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
                       size_t workspace_bytes, void *stream, int32_t path_hint,
                       int32_t pages_per_split);
 
+/* ---------------------------------------------------------------------------
+ * KV-cache write: the step's new K and V rows into the paged pool, the step
+ * that runs just before attention (metrale blueprint graph.json: node
+ * l3.attn.kv_write precedes l3.attn.attend; page layout of kern-kernels
+ * examples/decode.json, buffers kv / table / seq / cuq).
+ *
+ * For sequence b with n_b = cu_q[b+1] - cu_q[b] new tokens and L_b =
+ * seq_lens[b] keys in all (the new ones included), new token i (row
+ * t = cu_q[b] + i) is key position pos = L_b - n_b + i: k_new[t, g, :] and
+ * v_new[t, g, :] of every KV head g are written to the K and V rows of page
+ * block_table[b, pos / P], slot pos % P.  Tokens with pos < 0 (n_b > L_b) are
+ * not written.  Nothing else in the pool changes.
+ */
+typedef struct attn_kv_new_dims {
+    int64_t k_stride_token;    /* k_new[t, g, d] at k_new + t*k_stride_token + g*k_stride_head + d */
+    int64_t k_stride_head;
+    int64_t v_stride_token;    /* v_new likewise */
+    int64_t v_stride_head;
+} attn_kv_new_dims;
+
+/*
+ * attn_paged_kv_write -- the cache write alone.
+ *   kv_pool        bf16 pool, written (addressed through dims' kv strides).
+ *   k_new, v_new   bf16 [num_tokens, Hkv, D] (strides in new_dims; each a
+ *                  multiple of 8, head stride >= D, token stride >= Hkv *
+ *                  head stride), 16-byte aligned.  Views into a fused QKV
+ *                  projection output qualify.
+ *   block_table, seq_lens, cu_q, n_seqs, max_q, dims: as for attn_paged_fwd
+ *                  (dims' q / out strides are checked, not used).
+ * Pages written by two sequences at once, or a slot shared with a page that
+ * another sequence reads, are the caller's race.  Returns ATTN_OK or a
+ * validation error; nothing is launched on error.
+ */
+int attn_paged_kv_write(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
+                        const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                        const attn_paged_dims *dims, const attn_kv_new_dims *new_dims, void *stream);
+
+/*
+ * attn_paged_fwd_write -- the cache write followed by attn_paged_fwd in one
+ * call (two launches in stream order; the attention sees the written rows).
+ * Every argument of both steps is validated before either is launched.
+ */
+int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void *v_new, void *kv_pool,
+                         const int32_t *block_table, const int32_t *seq_lens, const int32_t *cu_q,
+                         int32_t n_seqs, int32_t max_q, float scale, int32_t causal,
+                         const attn_paged_dims *dims, const attn_kv_new_dims *new_dims, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /*
  * attn_workspace_clear -- enqueue a kernel that sets bytes [0, bytes) of a
  * device workspace to zero (the merge counters of the fused split path must
@@ -250,8 +298,9 @@ int attn_quant_fwd(void *out, const void *q, const void *k, const void *v,
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * launch is bracketed by HIP events recorded on the launch stream; elapsed
  * times are summed per kind: the main attention kernel (split-KV partials,
- * prefill or the quantised loop), the split-KV combine kernel, and the
- * quantised path's preparation kernels.  attn_kernel_timing_read
+ * prefill or the quantised loop), the split-KV combine kernel, and the work
+ * before the main kernel (the quantised path's preparation kernels, the
+ * KV-cache write).  attn_kernel_timing_read
  * synchronises on the recorded events, returns the totals (milliseconds)
  * and launch counts (any pointer may be NULL), and resets them.  Returns
  * ATTN_ERR_HIP if an event call fails.

@@ -86,6 +86,15 @@ class attn_paged_plan(ctypes.Structure):
     ]
 
 
+class attn_kv_new_dims(ctypes.Structure):
+    _fields_ = [
+        ("k_stride_token", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -108,6 +117,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_make_plan.restype = ctypes.c_int
     lib.attn_paged_workspace_bytes.argtypes = [dims_p, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_paged_workspace_bytes.restype = ctypes.c_int
+    nd_p = ctypes.POINTER(attn_kv_new_dims)
+    lib.attn_paged_kv_write.argtypes = [p, p, p, p, p, p, i32, i32, dims_p, nd_p, p]
+    lib.attn_paged_kv_write.restype = ctypes.c_int
+    lib.attn_paged_fwd_write.argtypes = [p, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, nd_p,
+                                         p, sz, p]
+    lib.attn_paged_fwd_write.restype = ctypes.c_int
     lib.attn_workspace_clear.argtypes = [p, sz, p]
     lib.attn_workspace_clear.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -256,6 +271,74 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
                                n_seqs, int(max_q), float(scale), int(bool(causal)),
                                ctypes.byref(dims), ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream),
                                int(path), int(pages_per_split))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    if cached is not None:
+        cached.clean = plan.counter_bytes
+    return out
+
+
+def _new_kv_dims(k_new: torch.Tensor, v_new: torch.Tensor) -> attn_kv_new_dims:
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _check_device_tensor(name, t, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("%s must be [T, Hkv, D] with D contiguous" % name)
+    return attn_kv_new_dims(k_new.stride(0), k_new.stride(1), v_new.stride(0), v_new.stride(1))
+
+
+def kv_write(kv_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
+             seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int, q_like: Optional[torch.Tensor] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> None:
+    """The KV-cache write (``attn_paged_kv_write``): the new K/V rows
+    k_new / v_new [T, Hkv, D] go to key positions L - n .. L - 1 of each
+    sequence.  ``q_like`` ([T, Hq, D]) supplies the q-head count and row
+    count of the dims (a zero-stride stand-in is used when absent)."""
+    lib = load_library()
+    if q_like is not None:
+        dims = make_dims(q_like, kv_pool, block_table, q_like)
+    else:
+        # no q: describe packed [T, Hkv, D] rows with one q head per KV head
+        T, hkv, d = k_new.shape
+        s = kv_pool.stride()
+        dims = attn_paged_dims(
+            num_q_heads=hkv, num_kv_heads=kv_pool.shape[2], head_dim=d, page_size=kv_pool.shape[1],
+            num_pages=kv_pool.shape[0], max_pages_per_seq=block_table.shape[1], num_tokens=T,
+            q_stride_token=hkv * d, q_stride_head=d, o_stride_token=hkv * d, o_stride_head=d,
+            kv_stride_page=s[0], kv_stride_slot=s[1], kv_stride_head=s[2], kv_stride_kv=s[3],
+            bt_stride=block_table.stride(0))
+    nd = _new_kv_dims(k_new, v_new)
+    st = stream if stream is not None else torch.cuda.current_stream(kv_pool.device)
+    rc = lib.attn_paged_kv_write(kv_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(),
+                                 seq_lens.data_ptr(), cu_q.data_ptr(), seq_lens.numel(), int(max_q),
+                                 ctypes.byref(dims), ctypes.byref(nd), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+
+
+def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kv_pool: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int,
+                          scale: float, causal: bool = True, out: Optional[torch.Tensor] = None,
+                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The cache write then attention in one call (``attn_paged_fwd_write``)."""
+    lib = load_library()
+    _check_device_tensor("q", q, torch.bfloat16)
+    if out is None:
+        out = torch.zeros_like(q)
+    dims = make_dims(q, kv_pool, block_table, out)
+    nd = _new_kv_dims(k_new, v_new)
+    plan = make_plan(dims, seq_lens.numel(), max_q)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    ws_ptr, ws_bytes, cached = None, 0, None
+    if plan.workspace_bytes:
+        cached = _workspace(plan.workspace_bytes, q.device)
+        if cached.clean < plan.counter_bytes:
+            workspace_clear(cached.buf, plan.counter_bytes, st)
+        ws_ptr, ws_bytes = cached.buf.data_ptr(), cached.buf.numel()
+    rc = lib.attn_paged_fwd_write(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                  kv_pool.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                  cu_q.data_ptr(), seq_lens.numel(), int(max_q), float(scale),
+                                  int(bool(causal)), ctypes.byref(dims), ctypes.byref(nd), ws_ptr, ws_bytes,
+                                  ctypes.c_void_p(st.cuda_stream))
     if rc != ATTN_OK:
         raise AttnError(rc)
     if cached is not None:

@@ -15,6 +15,7 @@
 #include "attn_device.h"
 #include "paged_attn.h"
 #include "quant_device.h"
+#include "kv_write.h"
 
 namespace pa {
 hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
@@ -23,6 +24,7 @@ hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream)
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_quant_prep(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_quant_attn(const QuantArgs &a, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
 }  // namespace pa
 
 namespace {
@@ -151,11 +153,12 @@ void timing_push(const TimedLaunch &t) {
     g_timed.push_back(t);
 }
 
-int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
-                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
-                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
-                   size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps) {
-    attn_paged_plan plan;
+// Validate an attention call and build its kernel arguments (no launch).
+int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                  const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                  float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                  size_t workspace_bytes, int32_t path_hint, int32_t pps, attn_paged_plan &plan,
+                  pa::AttnArgs &a) {
     int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, &plan);
     if (rc != ATTN_OK) return rc;
     if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
@@ -171,7 +174,7 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
 
     const int D = dims->head_dim;
     const int G = dims->num_q_heads / dims->num_kv_heads;
-    pa::AttnArgs a{};
+    a = pa::AttnArgs{};
     a.out = static_cast<uint16_t *>(out);
     a.q = static_cast<const uint16_t *>(q);
     a.kv = static_cast<const uint16_t *>(kv_pool);
@@ -211,8 +214,11 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
         a.part_ml = reinterpret_cast<float *>(ws + plan.counter_bytes + align_up(rows * (size_t)D * 4, kWsAlign));
         a.fuse_merge = plan.path == ATTN_PATH_SPLIT_FUSED ? 1 : 0;
     }
+    return ATTN_OK;
+}
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
+// Launch a prepared attention call (split kernel + combine, or prefill).
+int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipStream_t st) {
     const dim3 grid(plan.grid_x, plan.grid_y, plan.grid_z);
     const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
@@ -227,12 +233,12 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
         c.out = a.out;
         c.part_o = a.part_o;
         c.part_ml = a.part_ml;
-        c.seq_lens = seq_lens;
-        c.cu_q = cu_q;
+        c.seq_lens = a.seq_lens;
+        c.cu_q = a.cu_q;
         c.o_st = a.o_st;
         c.o_sh = a.o_sh;
-        c.n_seqs = n_seqs;
-        c.max_q = max_q;
+        c.n_seqs = a.n_seqs;
+        c.max_q = a.max_q;
         c.hq = a.hq;
         c.pages_per_split = plan.pages_per_split;
         c.max_splits = plan.max_splits;
@@ -253,6 +259,71 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
 }
 
 // ---- quantised path -------------------------------------------------------
+int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
+                   size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps) {
+    attn_paged_plan plan;
+    pa::AttnArgs a;
+    int rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal,
+                           dims, workspace, workspace_bytes, path_hint, pps, plan, a);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    return paged_launch(plan, a, dims->head_dim, static_cast<hipStream_t>(stream));
+}
+
+// Validate a KV-cache write and build its kernel arguments (no launch).
+int kv_write_prepare(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
+                     const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                     const attn_paged_dims *dims, const attn_kv_new_dims *nd, pa::KvWriteArgs &w) {
+    int rc = validate_dims(dims, n_seqs, max_q);
+    if (rc != ATTN_OK) return rc;
+    if (!nd) return ATTN_ERR_NULL;
+    const int64_t D = dims->head_dim, hkv = dims->num_kv_heads;
+    const int64_t strides[] = {nd->k_stride_token, nd->k_stride_head, nd->v_stride_token, nd->v_stride_head};
+    for (int64_t st : strides)
+        if (st <= 0 || (st & 7) != 0) return ATTN_ERR_STRIDE;
+    if (nd->k_stride_head < D || nd->k_stride_token < hkv * nd->k_stride_head) return ATTN_ERR_STRIDE;
+    if (nd->v_stride_head < D || nd->v_stride_token < hkv * nd->v_stride_head) return ATTN_ERR_STRIDE;
+    if (n_seqs == 0) return ATTN_OK;
+    if (!kv_pool || !k_new || !v_new || !block_table || !seq_lens || !cu_q) return ATTN_ERR_NULL;
+    if (!aligned16(kv_pool) || !aligned16(k_new) || !aligned16(v_new)) return ATTN_ERR_ALIGN;
+    if (!aligned4(block_table) || !aligned4(seq_lens) || !aligned4(cu_q)) return ATTN_ERR_ALIGN;
+    w = pa::KvWriteArgs{};
+    w.kv = static_cast<uint16_t *>(kv_pool);
+    w.k_new = static_cast<const uint16_t *>(k_new);
+    w.v_new = static_cast<const uint16_t *>(v_new);
+    w.block_table = block_table;
+    w.seq_lens = seq_lens;
+    w.cu_q = cu_q;
+    w.kv_sp = dims->kv_stride_page;
+    w.kv_ss = dims->kv_stride_slot;
+    w.kv_sh = dims->kv_stride_head;
+    w.kv_skv = dims->kv_stride_kv;
+    w.bt_stride = dims->bt_stride;
+    w.k_st = nd->k_stride_token;
+    w.k_sh = nd->k_stride_head;
+    w.v_st = nd->v_stride_token;
+    w.v_sh = nd->v_stride_head;
+    w.n_seqs = n_seqs;
+    w.max_q = max_q;
+    w.hkv = dims->num_kv_heads;
+    w.d = dims->head_dim;
+    return ATTN_OK;
+}
+
+int kv_write_launch(const pa::KvWriteArgs &w, hipStream_t st) {
+    const bool timing = timing_enabled();
+    TimedLaunch tl{};
+    if (timing && record_event(&tl.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+    if (pa::launch_kv_write(w, st) != hipSuccess) return ATTN_ERR_HIP;
+    if (timing) {
+        if (record_event(&tl.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+        tl.kind = kTimedPrep;
+        timing_push(tl);
+    }
+    return ATTN_OK;
+}
+
 int quant_layout(const attn_quant_dims *d, attn_quant_layout *lay) {
     if (!d || !lay) return ATTN_ERR_NULL;
     if (d->head_dim != pa::kQuantD) return ATTN_ERR_UNSUPPORTED;
@@ -410,6 +481,37 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
     return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale,
                           causal, dims, workspace, workspace_bytes, stream, path_hint,
                           pages_per_split);
+}
+
+int attn_paged_kv_write(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
+                        const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                        const attn_paged_dims *dims, const attn_kv_new_dims *new_dims, void *stream) {
+    pa::KvWriteArgs w;
+    int rc = kv_write_prepare(kv_pool, k_new, v_new, block_table, seq_lens, cu_q, n_seqs, max_q, dims,
+                              new_dims, w);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    return kv_write_launch(w, static_cast<hipStream_t>(stream));
+}
+
+int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void *v_new, void *kv_pool,
+                         const int32_t *block_table, const int32_t *seq_lens, const int32_t *cu_q,
+                         int32_t n_seqs, int32_t max_q, float scale, int32_t causal,
+                         const attn_paged_dims *dims, const attn_kv_new_dims *new_dims, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    // every argument of both steps is checked before anything is launched
+    pa::KvWriteArgs w;
+    int rc = kv_write_prepare(kv_pool, k_new, v_new, block_table, seq_lens, cu_q, n_seqs, max_q, dims,
+                              new_dims, w);
+    if (rc != ATTN_OK) return rc;
+    attn_paged_plan plan;
+    pa::AttnArgs a;
+    rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
+                       workspace, workspace_bytes, ATTN_PATH_AUTO, 0, plan, a);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = kv_write_launch(w, st);
+    if (rc != ATTN_OK) return rc;
+    return paged_launch(plan, a, dims->head_dim, st);
 }
 
 int attn_workspace_clear(void *workspace, size_t bytes, void *stream) {

@@ -36,7 +36,7 @@ def test_header_declares_entry_points():
     for name in ("attn_paged_fwd", "attn_paged_fwd_ex", "attn_paged_make_plan",
                  "attn_paged_workspace_bytes", "attn_status_string", "attn_quant_fwd",
                  "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of",
-                 "attn_workspace_clear"):
+                 "attn_workspace_clear", "attn_paged_kv_write", "attn_paged_fwd_write"):
         assert name in fns
 
 
@@ -181,6 +181,43 @@ def test_workspace_bytes_query(pa):
     assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, ctypes.byref(n)) == OK
     assert n.value == pa.make_plan(d, 64, 1).workspace_bytes
     assert lib.attn_paged_workspace_bytes(ctypes.byref(d), 64, 1, None) == E_NULL
+
+
+def _nd(pa, ks=(8 * 128, 128), vs=(8 * 128, 128)):
+    import paged_kv_gqa_fwd_amd as mod
+    return mod.attn_kv_new_dims(ks[0], ks[1], vs[0], vs[1])
+
+
+def test_kv_write_validates_before_launch(pa):
+    lib = pa.load_library()
+    d = dims()   # 32 q / 8 KV heads, D 128
+    F = FAKE
+
+    def w(nd, n_seqs=4, kv=F, k=F, v=F, max_q=1):
+        return lib.attn_paged_kv_write(kv, k, v, F, F, F, n_seqs, max_q, ctypes.byref(d),
+                                       ctypes.byref(nd) if nd is not None else None, None)
+    assert w(None) == E_NULL
+    assert w(_nd(pa, ks=(8 * 128, 100))) == E_STRIDE         # head stride not a multiple of 8
+    assert w(_nd(pa, ks=(8 * 128, 64))) == E_STRIDE          # rows shorter than D
+    assert w(_nd(pa, vs=(4 * 128, 128))) == E_STRIDE         # heads of a token overlap the next token
+    assert w(_nd(pa), k=None) == E_NULL
+    assert w(_nd(pa), v=F + 8) == E_ALIGN
+    assert w(_nd(pa), max_q=0) == E_SHAPE
+    assert w(_nd(pa), n_seqs=0, kv=None, k=None, v=None) == OK   # nothing to write
+
+
+def test_fwd_write_validates_both_steps(pa):
+    lib = pa.load_library()
+    d = dims()
+    F = FAKE
+
+    def fw(nd, scale=0.1, out=F, ws=None, ws_bytes=0, n_seqs=4):
+        return lib.attn_paged_fwd_write(out, F, F, F, F, F, F, F, n_seqs, 1, scale, 1, ctypes.byref(d),
+                                        ctypes.byref(nd) if nd is not None else None, ws, ws_bytes, None)
+    assert fw(None) == E_NULL                       # write step
+    assert fw(_nd(pa), scale=float("nan")) == E_SHAPE   # attention step
+    assert fw(_nd(pa), out=None) == E_NULL
+    assert fw(_nd(pa), out=F + 2) == E_ALIGN
 
 
 def test_workspace_clear_validates(pa):
