@@ -50,6 +50,8 @@ def _load():
         lib.oracle_paged_attn.argtypes = [
             p, p, p, i64, i64, p, i64, i64, i64, i64, p, i64, p, p,
             i32, i32, i32, i32, i32, f64, i32, p, i64, i32]
+        lib.oracle_paged_attn_ex.restype = ctypes.c_int
+        lib.oracle_paged_attn_ex.argtypes = lib.oracle_paged_attn.argtypes + [p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_quant_prep.restype = ctypes.c_int
         lib.oracle_quant_prep.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p, p, p, p, p, i32]
@@ -72,8 +74,12 @@ def _ptr(t: torch.Tensor) -> int:
 
 
 def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bool,
-               row_mask=None, chunk_keys: int = 0, nthreads: int = 0, return_lse: bool = False):
+               row_mask=None, chunk_keys: int = 0, nthreads: int = 0, return_lse: bool = False,
+               sinks=None, window: int = 0):
     """fp64 masked softmax attention over a paged KV cache.
+
+    sinks : optional per-q-head sink logits [Hq] (joins the normalisation,
+            no value row); window : W > 0 keeps only keys j >= pos - W + 1.
 
     q         : bf16 [T, Hq, D] CPU tensor (D contiguous, other strides free)
     kv_pool   : bf16 [NP, P, Hkv, 2, D] CPU tensor view (index 3: 0 = K, 1 = V)
@@ -100,11 +106,16 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
         rm = np.ascontiguousarray(np.asarray(row_mask, dtype=np.uint8))
         assert rm.shape == (T,)
     st = kv_pool.stride()
-    rc = lib.oracle_paged_attn(
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float64))
+        assert sk.shape == (hq,)
+    rc = lib.oracle_paged_attn_ex(
         out.ctypes.data, lse.ctypes.data, _ptr(q), q.stride(0), q.stride(1),
         _ptr(kv_pool), st[0], st[1], st[2], st[3], _ptr(bt), bt.stride(0), _ptr(sl), _ptr(cq),
         n_seqs, hq, hkv, d, P, float(scale), int(bool(causal)),
-        rm.ctypes.data if rm is not None else None, int(chunk_keys), int(nthreads))
+        rm.ctypes.data if rm is not None else None, int(chunk_keys), int(nthreads),
+        sk.ctypes.data if sk is not None else None, int(window))
     if rc != 0:
         raise RuntimeError("oracle_paged_attn failed with status %d" % rc)
     return (out, lse) if return_lse else out

@@ -34,6 +34,17 @@
  * design notes): seq_lens counts the step's own tokens; causal alignment is
  * bottom-right (queries sit at the tail of the sequence); q head h uses KV
  * head h / G.
+ *
+ * Optional variants (oracle_paged_attn_ex):
+ *  - attention sinks (Mojo SM100MHA2Q, SinkType: an optional pointer to
+ *    attention-sink weights).  Reading: one logit per q head, in the units of
+ *    the scaled scores, that joins the softmax normalisation and carries no
+ *    value row:  out = sum_j e^{s_j} V_j / (e^{sink_h} + sum_j e^{s_j}),
+ *    lse = log(e^{sink_h} + sum_j e^{s_j}).  A -inf sink changes nothing.
+ *  - a sliding window (decode.json's parameter pack holds an INT32_MAX field,
+ *    read as "window disabled").  Reading: with window W > 0 a query at
+ *    position pos sees only keys j >= pos - W + 1 (besides the causal or
+ *    length bound); W <= 0 means no window.
  */
 #include <math.h>
 #include <stdint.h>
@@ -121,6 +132,7 @@ static int64_t visible_keys(int64_t L, int64_t n, int64_t i, int causal)
 
 /*
  * out  : fp64 [num_tokens, hq, d] (rows outside [0, cu_q[n_seqs]) untouched)
+ * sinks: fp64 [hq] sink logits, or NULL;  window: W > 0, or <= 0 for none
  * lse  : fp64 [num_tokens, hq] natural-log log-sum-exp, or NULL
  * row_mask : optional uint8 [num_tokens]; when given only rows with a nonzero
  *            entry are computed (sampled checks at large sizes)
@@ -130,12 +142,12 @@ static int64_t visible_keys(int64_t L, int64_t n, int64_t i, int causal)
  *            log-sum-exp rule -- the split-KV reading, used for the
  *            "split + combine equals one pass" invariant.
  */
-int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_stride_token,
-                      int64_t q_stride_head, const uint16_t *pool, int64_t s_page, int64_t s_slot,
-                      int64_t s_head, int64_t s_kv, const int32_t *block_table, int64_t bt_stride,
-                      const int32_t *seq_lens, const int32_t *cu_q, int n_seqs, int hq, int hkv,
-                      int d, int page_size, double scale, int causal, const uint8_t *row_mask,
-                      int64_t chunk_keys, int nthreads)
+int oracle_paged_attn_ex(double *out, double *lse, const uint16_t *q, int64_t q_stride_token,
+                         int64_t q_stride_head, const uint16_t *pool, int64_t s_page, int64_t s_slot,
+                         int64_t s_head, int64_t s_kv, const int32_t *block_table, int64_t bt_stride,
+                         const int32_t *seq_lens, const int32_t *cu_q, int n_seqs, int hq, int hkv,
+                         int d, int page_size, double scale, int causal, const uint8_t *row_mask,
+                         int64_t chunk_keys, int nthreads, const double *sinks, int64_t window)
 {
     if (hkv <= 0 || hq % hkv != 0 || d <= 0 || page_size <= 0 || n_seqs < 0) return -1;
     oracle_ctx c = {q, q_stride_token, q_stride_head, pool, s_page, s_slot, s_head, s_kv,
@@ -169,14 +181,19 @@ int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_str
                     const int64_t i = t - cu_q[b];
                     const int64_t L = seq_lens[b];
                     const int64_t vis = visible_keys(L, n, i, causal);
+                    int64_t lo = 0;                       /* first key inside the window */
+                    if (window > 0) {
+                        lo = L - n + i - window + 1;
+                        if (lo < 0) lo = 0;
+                    }
                     double *dst = out + (t * hq + h) * (int64_t)d;
                     double m = -INFINITY, l = 0.0;
                     if (chunk_keys <= 0) {
-                        attend_range(&c, b, t, h, 0, vis, scores, &m, &l, acc);
+                        attend_range(&c, b, t, h, lo, vis, scores, &m, &l, acc);
                     } else {
                         /* merge partial triples chunk by chunk (log-sum-exp rule) */
                         for (int e = 0; e < d; ++e) acc[e] = 0.0;
-                        for (int64_t j0 = 0; j0 < vis; j0 += chunk_keys) {
+                        for (int64_t j0 = lo; j0 < vis; j0 += chunk_keys) {
                             int64_t j1 = j0 + chunk_keys < vis ? j0 + chunk_keys : vis;
                             double ms, ls;
                             attend_range(&c, b, t, h, j0, j1, scores, &ms, &ls, part);
@@ -187,6 +204,15 @@ int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_str
                             for (int e = 0; e < d; ++e) acc[e] = acc[e] * a_old + part[e] * a_new;
                             m = mn;
                         }
+                    }
+                    if (sinks && sinks[h] != -INFINITY) {
+                        /* the sink joins the normalisation with no value row */
+                        const double sk = sinks[h];
+                        const double mn = sk > m ? sk : m;
+                        const double a = (m == -INFINITY) ? 0.0 : exp(m - mn);
+                        l = l * a + exp(sk - mn);
+                        for (int e = 0; e < d; ++e) acc[e] *= a;
+                        m = mn;
                     }
                     if (l > 0.0) {
                         for (int e = 0; e < d; ++e) dst[e] = acc[e] / l;
@@ -203,6 +229,18 @@ int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_str
         free(part);
     }
     return status;
+}
+
+int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_stride_token,
+                      int64_t q_stride_head, const uint16_t *pool, int64_t s_page, int64_t s_slot,
+                      int64_t s_head, int64_t s_kv, const int32_t *block_table, int64_t bt_stride,
+                      const int32_t *seq_lens, const int32_t *cu_q, int n_seqs, int hq, int hkv,
+                      int d, int page_size, double scale, int causal, const uint8_t *row_mask,
+                      int64_t chunk_keys, int nthreads)
+{
+    return oracle_paged_attn_ex(out, lse, q, q_stride_token, q_stride_head, pool, s_page, s_slot, s_head,
+                                s_kv, block_table, bt_stride, seq_lens, cu_q, n_seqs, hq, hkv, d, page_size,
+                                scale, causal, row_mask, chunk_keys, nthreads, NULL, 0);
 }
 
 int oracle_num_threads(void)
