@@ -171,6 +171,43 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
                       int32_t pages_per_split);
 
 /* ---------------------------------------------------------------------------
+ * Options of the paged call: attention sinks and a sliding window.
+ *
+ *   sinks   device f32 [Hq], 4-byte aligned, or NULL: one logit per q head in
+ *           the units of the scaled scores (scale * q.k) that joins the softmax
+ *           normalisation and carries no value row (Mojo SM100MHA2Q docs,
+ *           SinkType: an optional pointer to attention-sink weights):
+ *             out[t, h] = sum_j e^{s_j} V_j / (e^{sinks[h]} + sum_j e^{s_j}).
+ *           -inf entries mean no sink for that head.
+ *   window  0 = none; W > 0: a query at position pos sees only keys
+ *           j >= pos - W + 1, besides the causal / length bound (decode.json's
+ *           parameter pack carries an INT32_MAX field, read as "window
+ *           disabled"; any W >= max_pages_per_seq * page_size changes
+ *           nothing).  Negative values are a shape error.
+ *   path_hint, pages_per_split: as for attn_paged_fwd_ex.
+ * With a window the split path plans and reads only the pages from row 0's
+ * window start on; rows with neither a visible key nor a sink give zeros, and
+ * rows with only a sink give zeros too (all weight on the sink).
+ */
+typedef struct attn_paged_options {
+    const float *sinks;
+    int32_t window;
+    int32_t path_hint;
+    int32_t pages_per_split;
+} attn_paged_options;
+
+/* attn_paged_make_plan with options (the window shrinks the split plan). */
+int attn_paged_make_plan_opt(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                             const attn_paged_options *opt, attn_paged_plan *plan);
+
+/* attn_paged_fwd with options; the workspace must hold the workspace_bytes of
+ * attn_paged_make_plan_opt for the same options. */
+int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                       const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                       float scale, int32_t causal, const attn_paged_dims *dims, const attn_paged_options *opt,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * KV-cache write: the step's new K and V rows into the paged pool, the step
  * that runs just before attention (metrale blueprint graph.json: node
  * l3.attn.kv_write precedes l3.attn.attend; page layout of kern-kernels

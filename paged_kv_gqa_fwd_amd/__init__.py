@@ -86,6 +86,15 @@ class attn_paged_plan(ctypes.Structure):
     ]
 
 
+class attn_paged_options(ctypes.Structure):
+    _fields_ = [
+        ("sinks", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
+        ("path_hint", ctypes.c_int32),
+        ("pages_per_split", ctypes.c_int32),
+    ]
+
+
 class attn_kv_new_dims(ctypes.Structure):
     _fields_ = [
         ("k_stride_token", ctypes.c_int64),
@@ -114,6 +123,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_fwd_ex.argtypes = fwd_args + [i32, i32]
     lib.attn_paged_fwd_ex.restype = ctypes.c_int
     lib.attn_paged_make_plan.argtypes = [dims_p, i32, i32, i32, i32, ctypes.POINTER(attn_paged_plan)]
+    opt_p = ctypes.POINTER(attn_paged_options)
+    lib.attn_paged_make_plan_opt.argtypes = [dims_p, i32, i32, opt_p, ctypes.POINTER(attn_paged_plan)]
+    lib.attn_paged_make_plan_opt.restype = ctypes.c_int
+    lib.attn_paged_fwd_opt.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, opt_p, p, sz, p]
+    lib.attn_paged_fwd_opt.restype = ctypes.c_int
     lib.attn_paged_make_plan.restype = ctypes.c_int
     lib.attn_paged_workspace_bytes.argtypes = [dims_p, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_paged_workspace_bytes.restype = ctypes.c_int
@@ -179,10 +193,11 @@ def make_dims(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.Tensor,
 
 
 def make_plan(dims: attn_paged_dims, n_seqs: int, max_q: int, path: int = PATH_AUTO,
-              pages_per_split: int = 0) -> attn_paged_plan:
+              pages_per_split: int = 0, window: int = 0) -> attn_paged_plan:
     plan = attn_paged_plan()
-    rc = load_library().attn_paged_make_plan(ctypes.byref(dims), n_seqs, max_q, path,
-                                             pages_per_split, ctypes.byref(plan))
+    opt = attn_paged_options(None, int(window), int(path), int(pages_per_split))
+    rc = load_library().attn_paged_make_plan_opt(ctypes.byref(dims), n_seqs, max_q, ctypes.byref(opt),
+                                                 ctypes.byref(plan))
     if rc != ATTN_OK:
         raise AttnError(rc)
     return plan
@@ -231,8 +246,12 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
                     causal: bool = True, out: Optional[torch.Tensor] = None,
                     path: int = PATH_AUTO, pages_per_split: int = 0,
                     workspace: Optional[torch.Tensor] = None,
-                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Paged GQA attention forward through ``attn_paged_fwd_ex``.
+                    stream: Optional[torch.cuda.Stream] = None,
+                    sinks: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
+    """Paged GQA attention forward through ``attn_paged_fwd_opt``.
+
+    sinks: optional f32 [Hq] GPU tensor of per-q-head sink logits; window:
+    0 = none, W > 0 = each query sees only its last W key positions.
 
     q [T, Hq, D] bf16, kv_pool [NP, P, Hkv, 2, D] bf16 view, block_table
     [B, MP] int32, seq_lens [B] int32, cu_q [B+1] int32 (all on the GPU).
@@ -256,7 +275,14 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
     if cu_q.numel() != n_seqs + 1 or block_table.shape[0] < n_seqs:
         raise ValueError("cu_q must have n_seqs + 1 entries and block_table >= n_seqs rows")
     dims = make_dims(q, kv_pool, block_table, out)
-    plan = make_plan(dims, n_seqs, max_q, path, pages_per_split)
+    plan = make_plan(dims, n_seqs, max_q, path, pages_per_split, window)
+    sinks_ptr = None
+    if sinks is not None:
+        _check_device_tensor("sinks", sinks, torch.float32)
+        if sinks.numel() != q.shape[1] or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous f32 tensor with one entry per q head")
+        sinks_ptr = sinks.data_ptr()
+    opt = attn_paged_options(sinks_ptr, int(window), int(path), int(pages_per_split))
     ws_ptr, ws_bytes, cached = None, 0, None
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     if plan.workspace_bytes:
@@ -266,11 +292,11 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
             if cached.clean < plan.counter_bytes:
                 workspace_clear(workspace, plan.counter_bytes, st)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    rc = lib.attn_paged_fwd_ex(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(),
-                               block_table.data_ptr(), seq_lens.data_ptr(), cu_q.data_ptr(),
-                               n_seqs, int(max_q), float(scale), int(bool(causal)),
-                               ctypes.byref(dims), ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream),
-                               int(path), int(pages_per_split))
+    rc = lib.attn_paged_fwd_opt(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(),
+                                block_table.data_ptr(), seq_lens.data_ptr(), cu_q.data_ptr(),
+                                n_seqs, int(max_q), float(scale), int(bool(causal)),
+                                ctypes.byref(dims), ctypes.byref(opt), ws_ptr, ws_bytes,
+                                ctypes.c_void_p(st.cuda_stream))
     if rc != ATTN_OK:
         raise AttnError(rc)
     if cached is not None:

@@ -66,6 +66,8 @@ struct AttnArgs {
     float scale_log2_pos;       // max(|scale| * log2(e), FLT_MIN) (prefill kernel)
     int32_t q_negate;           // scale < 0: the prefill kernel negates Q instead
     int32_t fuse_merge;         // split path: the last split of each (sequence, KV head) merges
+    const float *sinks;         // [Hq] sink logits (units of the scaled scores), or null
+    int32_t window;             // > 0: a query at pos sees only keys >= pos - window + 1; 0: no window
 };
 
 struct CombineArgs {
@@ -74,8 +76,9 @@ struct CombineArgs {
     const float *part_ml;
     const int32_t *seq_lens;
     const int32_t *cu_q;
+    const float *sinks;
     int64_t o_st, o_sh;
-    int32_t n_seqs, max_q, hq, pages_per_split, max_splits;
+    int32_t n_seqs, max_q, hq, pages_per_split, max_splits, window;
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -91,6 +94,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// First key a query at position pos may see under a left window of w keys
+// (w > 0); 0 without a window.
+__device__ __forceinline__ int window_start(int pos, int w) {
+    if (w <= 0) return 0;
+    const int64_t lo = (int64_t)pos - w + 1;
+    return lo > 0 ? (int)lo : 0;
+}
+
+// Split-KV layout of one sequence: splits cover its pages from the first one
+// inside row 0's window (row 0 has the earliest window) in runs of pps pages.
+__device__ __forceinline__ int split_first_page(int L, int n, int w) { return window_start(L - n, w) / kPage; }
+__device__ __forceinline__ int split_count(int npages, int p_lo, int pps, int max_splits) {
+    const int ns = (npages - p_lo + pps - 1) / pps;
+    return ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
 }
 
 // Number of keys visible to query i of a sequence with n queries and L keys

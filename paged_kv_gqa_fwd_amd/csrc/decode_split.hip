@@ -103,7 +103,10 @@ void paged_decode_split_kernel(const AttnArgs a) {
     int n = a.cu_q[b + 1] - q0;
     if (n > a.max_q) n = a.max_q;  // caller contract: n_b <= max_q
     const int npages = (L + kPage - 1) / kPage;
-    const int p_begin = s * a.pages_per_split;
+    // Splits start at the first page inside row 0's window (page 0 without a
+    // window), so pages no row can see are neither planned nor read.
+    const int p_lo = split_first_page(L, n, a.window);
+    const int p_begin = p_lo + s * a.pages_per_split;
     // Uniform across the workgroup.  A split past the sequence's last page
     // writes nothing (the combine never reads it); without splitting, an
     // empty sequence still runs the epilogue so its rows are written as zeros.
@@ -119,6 +122,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
     const int qi = row / G;
     const int h = g * G + (row - qi * G);
     const int vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
+    const int lo = row_ok ? window_start(L - n + qi, a.window) : 0;   // first key inside the window
 
     // Q^T as the B operand of v_mfma_f32_16x16x32_bf16: lane holds
     // q[row, 32*kk + 8*(lane/16) .. +7] for kk = 0 .. D/32-1.
@@ -160,7 +164,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sv[i] = (key0 + i < vis) ? sacc[i] * a.scale_log2 : -INFINITY;
+            sv[i] = (key0 + i < vis && key0 + i >= lo) ? sacc[i] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[i]);
         }
         mx = fmaxf(mx, shfl_xor_f32(mx, 16));
@@ -306,6 +310,11 @@ void paged_decode_split_kernel(const AttnArgs a) {
                 }
             }
         } else {
+            if (a.sinks) {
+                // the row's sink logit joins the normaliser (no value row)
+                const float sink2 = a.sinks[rh] * kLog2e;
+                if (sink2 != -INFINITY) lsum += exp2_fast(sink2 - Mr_use);
+            }
             const float o = lsum > 0.f ? osum / lsum : 0.f;
             a.out[t * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(o);
         }
@@ -328,7 +337,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
     // merge needs.  A device-scope fence would write back and invalidate the
     // whole L2 of the XCD in every workgroup instead.
     __shared__ int s_last;
-    const int ns = max(1, min(a.max_splits, (npages + a.pages_per_split - 1) / a.pages_per_split));
+    const int ns = split_count(npages, p_lo, a.pages_per_split, a.max_splits);
     int32_t *counter = a.counters + (int64_t)b * a.hkv + g;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores completed
     __syncthreads();                                    // ... and every wave's
@@ -342,6 +351,8 @@ void paged_decode_split_kernel(const AttnArgs a) {
         const int64_t base = (((int64_t)b * a.max_q + ri) * a.hq + rh) * a.max_splits;
         float M = -INFINITY;
         for (int s2 = 0; s2 < ns; ++s2) M = fmaxf(M, load_coherent(a.part_ml + (base + s2) * 2));
+        const float sink2 = a.sinks ? a.sinks[rh] * kLog2e : -INFINITY;
+        M = fmaxf(M, sink2);
         float acc = 0.f, lsum = 0.f;
         if (M != -INFINITY) {
             for (int s2 = 0; s2 < ns; ++s2) {
@@ -351,6 +362,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
                 lsum += wgt * ls;
                 acc += wgt * load_coherent(a.part_o + (base + s2) * D + d);
             }
+            if (sink2 != -INFINITY) lsum += exp2_fast(sink2 - M);
         }
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         a.out[(q0 + ri) * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(acc * inv);
@@ -359,7 +371,8 @@ void paged_decode_split_kernel(const AttnArgs a) {
 }
 
 // Log-sum-exp merge of the split partials: per (token, q head) row,
-// M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s.
+// M = max(max_s m_s, sink), w_s = 2^(m_s - M),
+// out = sum_s w_s O_s / (sum_s w_s l_s + 2^(sink - M)); no sink = -inf.
 // One wave64 per row; splits that hold no page of the sequence are skipped.
 template <int D>
 __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineArgs a) {
@@ -374,8 +387,7 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     if (i >= n) return;
     const int L = a.seq_lens[b];
     const int npages = (L + kPage - 1) / kPage;
-    int ns = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    if (ns > a.max_splits) ns = a.max_splits;
+    const int ns = split_count(npages, split_first_page(L, n, a.window), a.pages_per_split, a.max_splits);
     const int64_t t = q0 + i;
     const int64_t base = (((int64_t)b * a.max_q + i) * a.hq + h) * a.max_splits;
 
@@ -383,6 +395,9 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_ml[(base + s) * 2]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    // the row's sink logit (log2 units) joins the normaliser, with no value row
+    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+    M = fmaxf(M, sink2);
     constexpr int PER = D / 64;
     float acc[PER];
 #pragma unroll
@@ -398,6 +413,7 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
 #pragma unroll
             for (int e = 0; e < PER; ++e) acc[e] += wgt * po[lane + 64 * e];
         }
+        if (sink2 != -INFINITY) lsum += exp2_fast(sink2 - M);
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     uint16_t *op = a.out + t * a.o_st + (int64_t)h * a.o_sh;

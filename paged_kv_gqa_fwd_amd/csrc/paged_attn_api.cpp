@@ -68,13 +68,19 @@ int validate_dims(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q) {
     return ATTN_OK;
 }
 
+// A window that reaches past every key a table can hold changes nothing.
+int32_t effective_window(const attn_paged_dims *d, int32_t window) {
+    return (int64_t)window >= (int64_t)d->max_pages_per_seq * pa::kPage ? 0 : window;
+}
+
 int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
-              int32_t pps, attn_paged_plan *plan) {
+              int32_t pps, int32_t window, attn_paged_plan *plan) {
     int rc = validate_dims(d, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
     if (!plan) return ATTN_ERR_NULL;
     if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_SPLIT_FUSED) return ATTN_ERR_SHAPE;
-    if (pps < 0) return ATTN_ERR_SHAPE;
+    if (pps < 0 || window < 0) return ATTN_ERR_SHAPE;
+    window = effective_window(d, window);
     const int G = d->num_q_heads / d->num_kv_heads;
     const int64_t mq = std::max<int32_t>(max_q, 1);
     int path = path_hint;
@@ -88,7 +94,10 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     *plan = attn_paged_plan{};
     plan->path = path;
     plan->block_threads = pa::kThreads;
-    const int64_t MP = d->max_pages_per_seq;
+    // Pages the split path may have to read per sequence: all of them, or
+    // with a window those from row 0's window start to the last key.
+    int64_t MP = d->max_pages_per_seq;
+    if (split_path && window > 0) MP = std::min<int64_t>(MP, (window + mq + 62) / pa::kPage + 1);
     if (split_path) {
         int64_t p = pps;
         if (p == 0) {
@@ -157,15 +166,16 @@ void timing_push(const TimedLaunch &t) {
 int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
-                  size_t workspace_bytes, int32_t path_hint, int32_t pps, attn_paged_plan &plan,
-                  pa::AttnArgs &a) {
-    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, &plan);
+                  size_t workspace_bytes, int32_t path_hint, int32_t pps, const float *sinks,
+                  int32_t window, attn_paged_plan &plan, pa::AttnArgs &a) {
+    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan);
     if (rc != ATTN_OK) return rc;
     if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
     if (n_seqs == 0) return ATTN_OK;
     if (!out || !q || !kv_pool || !block_table || !seq_lens || !cu_q) return ATTN_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return ATTN_ERR_ALIGN;
     if (!aligned4(block_table) || !aligned4(seq_lens) || !aligned4(cu_q)) return ATTN_ERR_ALIGN;
+    if (sinks && !aligned4(sinks)) return ATTN_ERR_ALIGN;
     if (plan.workspace_bytes > 0) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0)
             return ATTN_ERR_WORKSPACE;
@@ -205,6 +215,8 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     // (every weight is then exactly 1 unless |q.k| exceeds about 1e30).
     a.scale_log2_pos = std::max((float)(std::fabs((double)scale) * 1.4426950408889634), FLT_MIN);
     a.q_negate = scale < 0.f ? 1 : 0;
+    a.sinks = sinks;
+    a.window = effective_window(dims, window);
     if (plan.workspace_bytes > 0) {
         // [merge counters | partial O | partial (m, l)], each 256-byte aligned
         const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
@@ -242,6 +254,8 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
         c.hq = a.hq;
         c.pages_per_split = plan.pages_per_split;
         c.max_splits = plan.max_splits;
+        c.sinks = a.sinks;
+        c.window = a.window;
         if (timing && record_event(&t_comb.start, st) != ATTN_OK) return ATTN_ERR_HIP;
         e = pa::launch_combine_any(D, c, st);
         if (e != hipSuccess) return ATTN_ERR_HIP;
@@ -262,11 +276,12 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
 int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
                    const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
                    float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
-                   size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps) {
+                   size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps,
+                   const float *sinks = nullptr, int32_t window = 0) {
     attn_paged_plan plan;
     pa::AttnArgs a;
     int rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal,
-                           dims, workspace, workspace_bytes, path_hint, pps, plan, a);
+                           dims, workspace, workspace_bytes, path_hint, pps, sinks, window, plan, a);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     return paged_launch(plan, a, dims->head_dim, static_cast<hipStream_t>(stream));
 }
@@ -452,14 +467,14 @@ extern "C" {
 
 int attn_paged_make_plan(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
                          int32_t path_hint, int32_t pages_per_split, attn_paged_plan *plan) {
-    return make_plan(dims, n_seqs, max_q, path_hint, pages_per_split, plan);
+    return make_plan(dims, n_seqs, max_q, path_hint, pages_per_split, 0, plan);
 }
 
 int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
                                size_t *bytes) {
     if (!bytes) return ATTN_ERR_NULL;
     attn_paged_plan plan;
-    int rc = make_plan(dims, n_seqs, max_q, ATTN_PATH_AUTO, 0, &plan);
+    int rc = make_plan(dims, n_seqs, max_q, ATTN_PATH_AUTO, 0, 0, &plan);
     if (rc != ATTN_OK) return rc;
     *bytes = plan.workspace_bytes;
     return ATTN_OK;
@@ -481,6 +496,22 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
     return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale,
                           causal, dims, workspace, workspace_bytes, stream, path_hint,
                           pages_per_split);
+}
+
+int attn_paged_make_plan_opt(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
+                             const attn_paged_options *opt, attn_paged_plan *plan) {
+    if (!opt) return ATTN_ERR_NULL;
+    return make_plan(dims, n_seqs, max_q, opt->path_hint, opt->pages_per_split, opt->window, plan);
+}
+
+int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                       const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                       float scale, int32_t causal, const attn_paged_dims *dims, const attn_paged_options *opt,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!opt) return ATTN_ERR_NULL;
+    return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
+                          workspace, workspace_bytes, stream, opt->path_hint, opt->pages_per_split, opt->sinks,
+                          opt->window);
 }
 
 int attn_paged_kv_write(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
@@ -506,7 +537,7 @@ int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void
     attn_paged_plan plan;
     pa::AttnArgs a;
     rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
-                       workspace, workspace_bytes, ATTN_PATH_AUTO, 0, plan, a);
+                       workspace, workspace_bytes, ATTN_PATH_AUTO, 0, nullptr, 0, plan, a);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     rc = kv_write_launch(w, st);

@@ -128,8 +128,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     const int r0 = tile * C::BM;
     if (r0 >= R) return;
 
-    // This lane's rows: one per 32-row block.
-    int vis[C::RB];
+    // This lane's rows: one per 32-row block.  Row keys are [lo, vis).
+    int vis[C::RB], lo[C::RB];
     bool row_ok[C::RB];
     int qi_[C::RB], h_[C::RB];
 #pragma unroll
@@ -139,11 +139,18 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         qi_[rb] = r / G;
         h_[rb] = g * G + (r - qi_[rb] * G);
         vis[rb] = row_ok[rb] ? visible_keys(L, n, qi_[rb], a.causal) : 0;
+        lo[rb] = row_ok[rb] ? window_start(L - n + qi_[rb], a.window) : 0;
     }
     const int r_last = min(R, r0 + C::BM) - 1;
     const int kv_end = visible_keys(L, n, r_last / G, a.causal);   // max over the workgroup's rows
     // keys below this wave's first row's frontier are visible to all its rows
     const int w_full = visible_keys(L, n, min(R - 1, r0 + 32 * C::RB * w) / G, a.causal);
+    // keys at or above the window start of this wave's last row are inside
+    // every row's window; pages below the workgroup's first row's window
+    // start are never loaded (0 and page 0 without a window)
+    const int w_lo = window_start(L - n + min(R - 1, r0 + 32 * C::RB * (w + 1) - 1) / G, a.window);
+    const int t0 = window_start(L - n + r0 / G, a.window) / kPage;
+    const int j0 = 2 * t0;                     // first 32-key step
     const int nsteps = (kv_end + 31) / 32;     // 32-key softmax steps
     const int ntiles = (nsteps + 1) / 2;       // 64-key pages
 
@@ -207,10 +214,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     };
 
 #pragma unroll
-    for (int t = 0; t <= C::LEAD; ++t)
-        if (t < ntiles) {
-            issue_page(t);
-            issued = t;
+    for (int tt = 0; tt <= C::LEAD; ++tt)
+        if (t0 + tt < ntiles) {
+            issue_page(t0 + tt);
+            issued = t0 + tt;
         }
 
     f32x16 oacc[C::RB][D / 32];
@@ -295,24 +302,24 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     for (int rb = 0; rb < C::RB; ++rb) pb[rb][0] = pb[rb][1] = bf16x8{};
     // One pipelined step: scur holds S_j on entry; snext receives S_{j+1}.
     auto step = [&](int j, f32x16 (&scur)[C::RB], f32x16 (&snext)[C::RB]) {
-        // ---- mask (diagonal and tail steps only)
-        if (32 * j + 32 > w_full) {
+        // ---- mask (diagonal, tail and window-edge steps only)
+        if (32 * j + 32 > w_full || 32 * j < w_lo) {
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = 32 * j + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    scur[rb][i] = key < vis[rb] ? scur[rb][i] : -INFINITY;
+                    scur[rb][i] = (key < vis[rb] && key >= lo[rb]) ? scur[rb][i] : -INFINITY;
                 }
         }
         // ---- A(j): P_{j-1} V_{j-1} on the MFMA pipe, two V operands
-        // ahead, with the row max of S_j on the VALU.  At j = 0, P is zero
-        // and page 0's V (landed) is read.
+        // ahead, with the row max of S_j on the VALU.  At the first step P
+        // is zero and the first page's V (landed) is read.
         float mx[C::RB];
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) mx[rb] = -INFINITY;
         {
-            const uint16_t *vt = vstage(j > 0 ? j - 1 : 0);
+            const uint16_t *vt = vstage(j > j0 ? j - 1 : j0);
             bf16x8 vop[PF + 1];
 #pragma unroll
             for (int k = 0; k < PF; ++k) vop[k] = vread(vt, k);
@@ -405,27 +412,41 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 }
             }
 #pragma unroll
-            for (int rb = 0; rb < C::RB; ++rb) l_part[rb] += psum[rb];
+            for (int rb = 0; rb < C::RB; ++rb) {
+                l_part[rb] += psum[rb];
+                // An empty use of the weights here keeps their VALU work in
+                // this block, interleaved with the Q.K MFMAs above: otherwise
+                // the compiler may sink it below the loop's branch, after the
+                // MFMAs, where nothing overlaps it.
+                asm volatile("" ::"v"(pb[rb][0]), "v"(pb[rb][1]), "v"(l_part[rb]));
+            }
         }
     };
 
-    wait_page(0);
-    __builtin_amdgcn_s_barrier();
     f32x16 sA[C::RB], sB[C::RB];
-    qk(0, sA);
-    // Two steps per page; the S registers alternate roles between them.
-    for (int t = 0; t < ntiles; ++t) {
-        step(2 * t, sA, sB);
-        if (2 * t + 1 < nsteps) step(2 * t + 1, sB, sA);
+    if (j0 < nsteps) {
+        wait_page(t0);
+        __builtin_amdgcn_s_barrier();
+        qk(j0, sA);
+        // Two steps per page; the S registers alternate roles between them.
+        for (int t = t0; t < ntiles; ++t) {
+            step(2 * t, sA, sB);
+            if (2 * t + 1 < nsteps) step(2 * t + 1, sB, sA);
+        }
+        pv(nsteps - 1, pb);
     }
-    if (nsteps > 0) pv(nsteps - 1, pb);
 
     // Epilogue: out = O / l, rounded to bf16.  oacc[rb][db][i] holds
     // d = 32db + 8(i/4) + 4hi + i%4 of this lane's row in block rb.
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
-        const float l_row = sum_xor32(l_part[rb]);
+        float l_row = sum_xor32(l_part[rb]);
         if (!row_ok[rb]) continue;
+        if (a.sinks && l_row > 0.f) {
+            // the row's sink logit joins the normaliser (no value row)
+            const float sink2 = a.sinks[h_[rb]] * kLog2e;
+            if (sink2 != -INFINITY) l_row += exp2_fast(sink2 - m_ref[rb]);
+        }
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
         uint16_t *op = a.out + (int64_t)(q0 + qi_[rb]) * a.o_st + (int64_t)h_[rb] * a.o_sh;
 #pragma unroll

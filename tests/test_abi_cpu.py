@@ -36,7 +36,8 @@ def test_header_declares_entry_points():
     for name in ("attn_paged_fwd", "attn_paged_fwd_ex", "attn_paged_make_plan",
                  "attn_paged_workspace_bytes", "attn_status_string", "attn_quant_fwd",
                  "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of",
-                 "attn_workspace_clear", "attn_paged_kv_write", "attn_paged_fwd_write"):
+                 "attn_workspace_clear", "attn_paged_kv_write", "attn_paged_fwd_write",
+                 "attn_paged_fwd_opt", "attn_paged_make_plan_opt"):
         assert name in fns
 
 
@@ -218,6 +219,33 @@ def test_fwd_write_validates_both_steps(pa):
     assert fw(_nd(pa), scale=float("nan")) == E_SHAPE   # attention step
     assert fw(_nd(pa), out=None) == E_NULL
     assert fw(_nd(pa), out=F + 2) == E_ALIGN
+
+
+def test_options_validate_and_shrink_the_split_plan(pa):
+    import paged_kv_gqa_fwd_amd as mod
+    lib = pa.load_library()
+    d = dims(max_pages_per_seq=128, bt_stride=128)
+    plan = mod.attn_paged_plan()
+
+    def opt(sinks=None, window=0, path=0, pps=0):
+        return mod.attn_paged_options(sinks, window, path, pps)
+
+    def fo(o, ws=None, ws_bytes=0):
+        return lib.attn_paged_fwd_opt(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1, 0.1, 1, ctypes.byref(d),
+                                      ctypes.byref(o) if o is not None else None, ws, ws_bytes, None)
+    assert fo(None) == E_NULL
+    assert lib.attn_paged_make_plan_opt(ctypes.byref(d), 64, 1, None, ctypes.byref(plan)) == E_NULL
+    assert fo(opt(window=-1)) == E_SHAPE
+    assert fo(opt(sinks=FAKE + 2), ws=FAKE, ws_bytes=1 << 30) == E_ALIGN
+    # a window shrinks the pages each sequence's splits must cover
+    full = mod.make_plan(d, 64, 1)
+    win = mod.make_plan(d, 64, 1, window=256)     # rows see <= 256 keys: <= 5 pages from row 0's start
+    assert win.max_splits * win.pages_per_split >= 5 and win.max_splits * win.pages_per_split < 128
+    assert win.workspace_bytes < full.workspace_bytes
+    # windows that reach past every key a table can hold change nothing
+    same = mod.make_plan(d, 64, 1, window=128 * 64)
+    assert (same.pages_per_split, same.max_splits, same.workspace_bytes) == \
+        (full.pages_per_split, full.max_splits, full.workspace_bytes)
 
 
 def test_workspace_clear_validates(pa):
