@@ -67,10 +67,12 @@ def visible_pairs(case) -> int:
     return tot
 
 
-def algorithmic_bytes(case) -> int:
-    """K and V of every visible key once per KV head, Q read once, out written once."""
+def algorithmic_bytes(case, window: int = 0) -> int:
+    """K and V of every visible key once per KV head, Q read once, out written once.
+    With a window only keys from row 0's window start on are needed."""
     d, hq, hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
-    kv = sum(case.kv_lens) * hkv * 2 * d * 2
+    keys = sum(L if window <= 0 else min(L, L - max(0, L - n - window + 1)) for n, L in zip(case.q_lens, case.kv_lens))
+    kv = keys * hkv * 2 * d * 2
     T = sum(case.q_lens)
     return kv + 2 * T * hq * d * 2
 
@@ -108,30 +110,30 @@ def _kernel_times(fn, steps):
     return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
 
 
-def run_workload(name, steps, warmup, pps=0, path=0):
+def run_workload(name, steps, warmup, pps=0, path=0, window=0):
     import paged_kv_gqa_fwd_amd as pa
-    log("[bench] generating %s" % name)
+    log("[bench] generating %s%s" % (name, " (window %d)" % window if window else ""))
     case = workloads.WORKLOADS[name](device="cuda")
     out = torch.empty_like(case.q)
     args = (case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, max(case.max_q, 1),
             case.scale, case.causal)
     dims = pa.make_dims(case.q, case.kv, case.block_table, out)
-    plan = pa.make_plan(dims, case.n_seqs, max(case.max_q, 1), path, pps)
+    plan = pa.make_plan(dims, case.n_seqs, max(case.max_q, 1), path, pps, window)
 
     def step():
-        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps)
+        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps, window=window)
 
     for _ in range(warmup):
         step()
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, _ = _kernel_times(step, steps)
     res = {
-        "workload": name, "case": case, "ms_per_step": step_ms,
+        "workload": name + ("+window%d" % window if window else ""), "case": case, "ms_per_step": step_ms,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
                  pa.PATH_PREFILL: "prefill"}[plan.path],
         "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
-        "bytes": algorithmic_bytes(case), "flops": algorithmic_flops(case),
+        "bytes": algorithmic_bytes(case, window), "flops": algorithmic_flops(case),
     }
     return res
 
@@ -211,7 +213,7 @@ def measured_traffic(kernel_files, profile_name):
 
 def summarize(res):
     name = res["workload"]
-    if BOUND[name] == "hbm":
+    if BOUND[name.split("+")[0]] == "hbm":
         val = res["bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
         kern = res["bytes"] / (res["main_kernel_ms"] * 1e-3) / 1e9
         return {"workload": name, "value": round(val, 2), "unit": "GB/s",
@@ -331,7 +333,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant,"
-                                           "decode_batch+kv_write,chunked_prefill+kv_write",
+                                           "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096",
                     help="comma list of extra workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
@@ -370,6 +372,15 @@ def main():
     log("[bench] %s" % json.dumps(s))
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        if "+window" in name:
+            base, w = name.split("+window")
+            r = run_workload(base, max(3, args.steps // 2), max(1, args.warmup // 2), window=int(w))
+            ss = summarize(r)
+            log("[bench] %s" % json.dumps(ss))
+            secondary.append(ss)
+            del r
+            torch.cuda.empty_cache()
+            continue
         if name.endswith("+kv_write"):
             ss = run_write(name[:-len("+kv_write")], max(3, args.steps // 2), max(1, args.warmup // 2))
             log("[bench] %s" % json.dumps(ss))
