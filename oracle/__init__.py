@@ -51,7 +51,7 @@ def _load():
             p, p, p, i64, i64, p, i64, i64, i64, i64, p, i64, p, p,
             i32, i32, i32, i32, i32, f64, i32, p, i64, i32]
         lib.oracle_paged_attn_ex.restype = ctypes.c_int
-        lib.oracle_paged_attn_ex.argtypes = lib.oracle_paged_attn.argtypes + [p, i64]
+        lib.oracle_paged_attn_ex.argtypes = lib.oracle_paged_attn.argtypes + [p, i64, i32, f64, f64]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_quant_prep.restype = ctypes.c_int
         lib.oracle_quant_prep.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p, p, p, p, p, i32]
@@ -75,11 +75,13 @@ def _ptr(t: torch.Tensor) -> int:
 
 def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bool,
                row_mask=None, chunk_keys: int = 0, nthreads: int = 0, return_lse: bool = False,
-               sinks=None, window: int = 0):
+               sinks=None, window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
     """fp64 masked softmax attention over a paged KV cache.
 
     sinks : optional per-q-head sink logits [Hq] (joins the normalisation,
             no value row); window : W > 0 keeps only keys j >= pos - W + 1.
+    A uint8 kv_pool holds OCP e4m3 codes: K = k_scale * e4m3(code),
+    V = v_scale * e4m3(code).
 
     q         : bf16 [T, Hq, D] CPU tensor (D contiguous, other strides free)
     kv_pool   : bf16 [NP, P, Hkv, 2, D] CPU tensor view (index 3: 0 = K, 1 = V)
@@ -88,7 +90,8 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
     the natural-log lse [T, Hq] when ``return_lse``.
     """
     lib = _load()
-    assert q.dtype == torch.bfloat16 and kv_pool.dtype == torch.bfloat16
+    assert q.dtype == torch.bfloat16 and kv_pool.dtype in (torch.bfloat16, torch.uint8)
+    kv_fp8 = kv_pool.dtype == torch.uint8
     assert q.device.type == "cpu" and kv_pool.device.type == "cpu"
     assert q.dim() == 3 and q.stride(2) == 1
     assert kv_pool.dim() == 5 and kv_pool.stride(4) == 1 and kv_pool.shape[3] == 2
@@ -115,7 +118,7 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
         _ptr(kv_pool), st[0], st[1], st[2], st[3], _ptr(bt), bt.stride(0), _ptr(sl), _ptr(cq),
         n_seqs, hq, hkv, d, P, float(scale), int(bool(causal)),
         rm.ctypes.data if rm is not None else None, int(chunk_keys), int(nthreads),
-        sk.ctypes.data if sk is not None else None, int(window))
+        sk.ctypes.data if sk is not None else None, int(window), int(kv_fp8), float(k_scale), float(v_scale))
     if rc != 0:
         raise RuntimeError("oracle_paged_attn failed with status %d" % rc)
     return (out, lse) if return_lse else out

@@ -45,6 +45,10 @@
  *    read as "window disabled").  Reading: with window W > 0 a query at
  *    position pos sees only keys j >= pos - W + 1 (besides the causal or
  *    length bound); W <= 0 means no window.
+ *  - an fp8 KV cache (the Mojo SM100MHA2Q docs carry fp8 branches of the KV
+ *    dtype): pool elements are OCP e4m3 codes with one scale for K and one
+ *    for V, K_j = k_scale * e4m3(code), V_j = v_scale * e4m3(code), decoded
+ *    exactly to fp64 by this oracle's own decoder (quant_oracle.c).
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,6 +57,8 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+double oracle_e4m3_decode(uint8_t c);   /* quant_oracle.c */
 
 static double bf16_bits_to_f64(uint16_t bits)
 {
@@ -71,15 +77,25 @@ typedef struct {
     int64_t bt_stride;
     int hq, hkv, d, page_size;
     double scale;
+    int kv_fp8;                 /* pool elements: 0 = bf16, 1 = e4m3 codes */
+    double k_scale, v_scale;    /* fp8 pool only */
 } oracle_ctx;
 
-/* Address of element 0 of key/value row j of sequence b, KV head g. */
-static const uint16_t *kv_row(const oracle_ctx *c, int b, int64_t j, int g, int which)
+/* Key (which = 0) or value (which = 1) row j of sequence b, KV head g,
+   widened to fp64 into row[0 .. d). */
+static void kv_row(const oracle_ctx *c, int b, int64_t j, int g, int which, double *row)
 {
     int64_t page = c->block_table[(int64_t)b * c->bt_stride + j / c->page_size];
     int64_t slot = j % c->page_size;
-    return c->pool + page * c->s_page + slot * c->s_slot + (int64_t)g * c->s_head
-           + (int64_t)which * c->s_kv;
+    int64_t off = page * c->s_page + slot * c->s_slot + (int64_t)g * c->s_head + (int64_t)which * c->s_kv;
+    if (!c->kv_fp8) {
+        const uint16_t *p = c->pool + off;
+        for (int e = 0; e < c->d; ++e) row[e] = bf16_bits_to_f64(p[e]);
+    } else {
+        const uint8_t *p = (const uint8_t *)c->pool + off;   /* strides count bytes */
+        const double sc = which ? c->v_scale : c->k_scale;
+        for (int e = 0; e < c->d; ++e) row[e] = sc * oracle_e4m3_decode(p[e]);
+    }
 }
 
 /*
@@ -89,7 +105,7 @@ static const uint16_t *kv_row(const oracle_ctx *c, int b, int64_t j, int g, int 
  * An empty range gives m = -inf, l = 0, o = 0.
  */
 static void attend_range(const oracle_ctx *c, int b, int64_t t, int h, int64_t j0, int64_t j1,
-                         double *scores, double *m_out, double *l_out, double *o)
+                         double *scores, double *m_out, double *l_out, double *o, double *row)
 {
     const int d = c->d;
     const int g = h / (c->hq / c->hkv);
@@ -102,9 +118,9 @@ static void attend_range(const oracle_ctx *c, int b, int64_t t, int h, int64_t j
     }
     double m = -INFINITY;
     for (int64_t j = j0; j < j1; ++j) {
-        const uint16_t *k = kv_row(c, b, j, g, 0);
+        kv_row(c, b, j, g, 0, row);
         double dot = 0.0;
-        for (int e = 0; e < d; ++e) dot += bf16_bits_to_f64(qrow[e]) * bf16_bits_to_f64(k[e]);
+        for (int e = 0; e < d; ++e) dot += bf16_bits_to_f64(qrow[e]) * row[e];
         double s = c->scale * dot;
         scores[j - j0] = s;
         if (s > m) m = s;
@@ -113,8 +129,8 @@ static void attend_range(const oracle_ctx *c, int b, int64_t t, int h, int64_t j
     for (int64_t j = j0; j < j1; ++j) {
         double w = exp(scores[j - j0] - m);
         l += w;
-        const uint16_t *v = kv_row(c, b, j, g, 1);
-        for (int e = 0; e < d; ++e) o[e] += w * bf16_bits_to_f64(v[e]);
+        kv_row(c, b, j, g, 1, row);
+        for (int e = 0; e < d; ++e) o[e] += w * row[e];
     }
     *m_out = m;
     *l_out = l;
@@ -147,11 +163,12 @@ int oracle_paged_attn_ex(double *out, double *lse, const uint16_t *q, int64_t q_
                          int64_t s_head, int64_t s_kv, const int32_t *block_table, int64_t bt_stride,
                          const int32_t *seq_lens, const int32_t *cu_q, int n_seqs, int hq, int hkv,
                          int d, int page_size, double scale, int causal, const uint8_t *row_mask,
-                         int64_t chunk_keys, int nthreads, const double *sinks, int64_t window)
+                         int64_t chunk_keys, int nthreads, const double *sinks, int64_t window,
+                         int kv_fp8, double k_scale, double v_scale)
 {
     if (hkv <= 0 || hq % hkv != 0 || d <= 0 || page_size <= 0 || n_seqs < 0) return -1;
     oracle_ctx c = {q, q_stride_token, q_stride_head, pool, s_page, s_slot, s_head, s_kv,
-                    block_table, bt_stride, hq, hkv, d, page_size, scale};
+                    block_table, bt_stride, hq, hkv, d, page_size, scale, kv_fp8, k_scale, v_scale};
     int64_t max_l = 0;
     for (int b = 0; b < n_seqs; ++b)
         if (seq_lens[b] > max_l) max_l = seq_lens[b];
@@ -167,7 +184,8 @@ int oracle_paged_attn_ex(double *out, double *lse, const uint16_t *q, int64_t q_
         double *scores = (double *)malloc(sizeof(double) * (size_t)(max_l > 0 ? max_l : 1));
         double *acc = (double *)malloc(sizeof(double) * (size_t)d);
         double *part = (double *)malloc(sizeof(double) * (size_t)d);
-        if (!scores || !acc || !part) {
+        double *row = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!scores || !acc || !part || !row) {
 #pragma omp atomic write
             status = -2;
         } else {
@@ -189,14 +207,14 @@ int oracle_paged_attn_ex(double *out, double *lse, const uint16_t *q, int64_t q_
                     double *dst = out + (t * hq + h) * (int64_t)d;
                     double m = -INFINITY, l = 0.0;
                     if (chunk_keys <= 0) {
-                        attend_range(&c, b, t, h, lo, vis, scores, &m, &l, acc);
+                        attend_range(&c, b, t, h, lo, vis, scores, &m, &l, acc, row);
                     } else {
                         /* merge partial triples chunk by chunk (log-sum-exp rule) */
                         for (int e = 0; e < d; ++e) acc[e] = 0.0;
                         for (int64_t j0 = lo; j0 < vis; j0 += chunk_keys) {
                             int64_t j1 = j0 + chunk_keys < vis ? j0 + chunk_keys : vis;
                             double ms, ls;
-                            attend_range(&c, b, t, h, j0, j1, scores, &ms, &ls, part);
+                            attend_range(&c, b, t, h, j0, j1, scores, &ms, &ls, part, row);
                             double mn = ms > m ? ms : m;
                             double a_old = (m == -INFINITY) ? 0.0 : exp(m - mn);
                             double a_new = (ms == -INFINITY) ? 0.0 : exp(ms - mn);
@@ -227,6 +245,7 @@ int oracle_paged_attn_ex(double *out, double *lse, const uint16_t *q, int64_t q_
         free(scores);
         free(acc);
         free(part);
+        free(row);
     }
     return status;
 }
@@ -240,7 +259,7 @@ int oracle_paged_attn(double *out, double *lse, const uint16_t *q, int64_t q_str
 {
     return oracle_paged_attn_ex(out, lse, q, q_stride_token, q_stride_head, pool, s_page, s_slot, s_head,
                                 s_kv, block_table, bt_stride, seq_lens, cu_q, n_seqs, hq, hkv, d, page_size,
-                                scale, causal, row_mask, chunk_keys, nthreads, NULL, 0);
+                                scale, causal, row_mask, chunk_keys, nthreads, NULL, 0, 0, 1.0, 1.0);
 }
 
 int oracle_num_threads(void)

@@ -289,6 +289,18 @@ def new_kv_tokens(case: PagedCase, seed: int, layout: str = "separate"):
     return qkv[:, hq:hq + hkv, :], qkv[:, hq + hkv:, :]
 
 
+def fp8_pool_case(case: PagedCase, mult: float = 2.0) -> PagedCase:
+    """The same case over an fp8 KV cache: every pool element (bf16 x) becomes
+    the OCP e4m3 code of mult * x (torch's float8_e4m3fn conversion; poisoned
+    NaN slots stay NaN codes), stored as uint8 with the pool's layout and
+    element strides.  The cache then holds K = k_scale * e4m3(code) with
+    k_scale chosen by the caller (1 / mult keeps the bf16 case's scale)."""
+    storage = (case.pool_storage.float() * mult).to(torch.float8_e4m3fn).view(torch.uint8)
+    kv = storage.as_strided(case.kv.shape, case.kv.stride(),
+                            case.kv.storage_offset() - case.pool_storage.storage_offset())
+    return dataclasses.replace(case, name=case.name + "-fp8", pool_storage=storage, kv=kv)
+
+
 def dense_from_case(case: PagedCase):
     """Dense [1, N, H, D] views (q, k, v) of a one-sequence self-attention case
     (n = L): the pages are gathered in block-table order, K and V stay
