@@ -69,10 +69,11 @@ def visible_pairs(case) -> int:
 
 def algorithmic_bytes(case, window: int = 0) -> int:
     """K and V of every visible key once per KV head, Q read once, out written once.
-    With a window only keys from row 0's window start on are needed."""
+    With a window only keys from row 0's window start on are needed; an fp8
+    cache holds one byte per element."""
     d, hq, hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
     keys = sum(L if window <= 0 else min(L, L - max(0, L - n - window + 1)) for n, L in zip(case.q_lens, case.kv_lens))
-    kv = keys * hkv * 2 * d * 2
+    kv = keys * hkv * 2 * d * case.kv.element_size()
     T = sum(case.q_lens)
     return kv + 2 * T * hq * d * 2
 
@@ -110,10 +111,15 @@ def _kernel_times(fn, steps):
     return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
 
 
-def run_workload(name, steps, warmup, pps=0, path=0, window=0):
+def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
     import paged_kv_gqa_fwd_amd as pa
-    log("[bench] generating %s%s" % (name, " (window %d)" % window if window else ""))
+    log("[bench] generating %s%s%s" % (name, " (window %d)" % window if window else "", " (fp8 cache)" if fp8 else ""))
     case = workloads.WORKLOADS[name](device="cuda")
+    kscale = 1.0
+    if fp8:
+        # e4m3 codes of 2x the bf16 pool values; scales 1/2 keep the values
+        case = workloads.fp8_pool_case(case, mult=2.0)
+        kscale = 0.5
     out = torch.empty_like(case.q)
     args = (case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, max(case.max_q, 1),
             case.scale, case.causal)
@@ -121,14 +127,16 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0):
     plan = pa.make_plan(dims, case.n_seqs, max(case.max_q, 1), path, pps, window)
 
     def step():
-        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps, window=window)
+        pa.paged_attention(*args, out=out, path=path, pages_per_split=pps, window=window, k_scale=kscale,
+                           v_scale=kscale)
 
     for _ in range(warmup):
         step()
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, _ = _kernel_times(step, steps)
     res = {
-        "workload": name + ("+window%d" % window if window else ""), "case": case, "ms_per_step": step_ms,
+        "workload": name + ("+window%d" % window if window else "") + ("+fp8" if fp8 else ""), "case": case,
+        "ms_per_step": step_ms,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
                  pa.PATH_PREFILL: "prefill"}[plan.path],
@@ -333,7 +341,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant,"
-                                           "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096",
+                                           "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096,"
+                                           "decode_batch+fp8,long_decode+fp8",
                     help="comma list of extra workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
@@ -372,6 +381,14 @@ def main():
     log("[bench] %s" % json.dumps(s))
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        if name.endswith("+fp8"):
+            r = run_workload(name[:-len("+fp8")], max(3, args.steps // 2), max(1, args.warmup // 2), fp8=True)
+            ss = summarize(r)
+            log("[bench] %s" % json.dumps(ss))
+            secondary.append(ss)
+            del r
+            torch.cuda.empty_cache()
+            continue
         if "+window" in name:
             base, w = name.split("+window")
             r = run_workload(base, max(3, args.steps // 2), max(1, args.warmup // 2), window=int(w))

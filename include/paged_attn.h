@@ -194,7 +194,21 @@ typedef struct attn_paged_options {
     int32_t window;
     int32_t path_hint;
     int32_t pages_per_split;
+    int32_t kv_dtype;          /* ATTN_KV_BF16 (0) or ATTN_KV_FP8_E4M3 (1) */
+    float k_scale, v_scale;    /* fp8 cache: K = k_scale * e4m3(code), V = v_scale * e4m3(code);
+                                  ignored for a bf16 cache */
 } attn_paged_options;
+
+/*
+ * KV-cache element types.  ATTN_KV_FP8_E4M3: the pool holds OCP e4m3 codes
+ * (1 byte; dims' kv strides then count bytes and must be multiples of 16),
+ * with one scale for all of K and one for all of V (the Mojo SM100MHA2Q docs
+ * carry fp8 branches of the KV dtype; per-tensor scales are the reading taken
+ * here).  Supported on the split-decode paths (packed rows G * max_q <= 16);
+ * a call that would take the prefill path returns ATTN_ERR_UNSUPPORTED.
+ * Scales must be finite.
+ */
+enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3 = 1 };
 
 /* attn_paged_make_plan with options (the window shrinks the split plan). */
 int attn_paged_make_plan_opt(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,

@@ -22,6 +22,8 @@ PATH_AUTO = 0
 PATH_SPLIT_DECODE = 1   # split-KV kernel + combine kernel
 PATH_PREFILL = 2
 PATH_SPLIT_FUSED = 3    # split-KV kernel whose last split per (sequence, KV head) merges
+KV_BF16 = 0
+KV_FP8_E4M3 = 1         # OCP e4m3 codes with per-tensor K and V scales
 
 ATTN_OK = 0
 
@@ -92,6 +94,9 @@ class attn_paged_options(ctypes.Structure):
         ("window", ctypes.c_int32),
         ("path_hint", ctypes.c_int32),
         ("pages_per_split", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -193,9 +198,9 @@ def make_dims(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.Tensor,
 
 
 def make_plan(dims: attn_paged_dims, n_seqs: int, max_q: int, path: int = PATH_AUTO,
-              pages_per_split: int = 0, window: int = 0) -> attn_paged_plan:
+              pages_per_split: int = 0, window: int = 0, kv_dtype: int = 0) -> attn_paged_plan:
     plan = attn_paged_plan()
-    opt = attn_paged_options(None, int(window), int(path), int(pages_per_split))
+    opt = attn_paged_options(None, int(window), int(path), int(pages_per_split), int(kv_dtype), 1.0, 1.0)
     rc = load_library().attn_paged_make_plan_opt(ctypes.byref(dims), n_seqs, max_q, ctypes.byref(opt),
                                                  ctypes.byref(plan))
     if rc != ATTN_OK:
@@ -247,11 +252,13 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
                     path: int = PATH_AUTO, pages_per_split: int = 0,
                     workspace: Optional[torch.Tensor] = None,
                     stream: Optional[torch.cuda.Stream] = None,
-                    sinks: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
+                    sinks: Optional[torch.Tensor] = None, window: int = 0,
+                    k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """Paged GQA attention forward through ``attn_paged_fwd_opt``.
 
     sinks: optional f32 [Hq] GPU tensor of per-q-head sink logits; window:
-    0 = none, W > 0 = each query sees only its last W key positions.
+    0 = none, W > 0 = each query sees only its last W key positions.  A uint8
+    kv_pool is an fp8 (OCP e4m3) cache: K = k_scale * e4m3, V = v_scale * e4m3.
 
     q [T, Hq, D] bf16, kv_pool [NP, P, Hkv, 2, D] bf16 view, block_table
     [B, MP] int32, seq_lens [B] int32, cu_q [B+1] int32 (all on the GPU).
@@ -262,7 +269,8 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
     ``workspace_clear``).
     """
     lib = load_library()
-    for name, t, dt in (("q", q, torch.bfloat16), ("kv_pool", kv_pool, torch.bfloat16),
+    kv_dtype = KV_FP8_E4M3 if kv_pool.dtype == torch.uint8 else KV_BF16
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv_pool", kv_pool, torch.uint8 if kv_dtype else torch.bfloat16),
                         ("block_table", block_table, torch.int32), ("seq_lens", seq_lens, torch.int32),
                         ("cu_q", cu_q, torch.int32)):
         _check_device_tensor(name, t, dt)
@@ -275,14 +283,15 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
     if cu_q.numel() != n_seqs + 1 or block_table.shape[0] < n_seqs:
         raise ValueError("cu_q must have n_seqs + 1 entries and block_table >= n_seqs rows")
     dims = make_dims(q, kv_pool, block_table, out)
-    plan = make_plan(dims, n_seqs, max_q, path, pages_per_split, window)
+    plan = make_plan(dims, n_seqs, max_q, path, pages_per_split, window, kv_dtype)
     sinks_ptr = None
     if sinks is not None:
         _check_device_tensor("sinks", sinks, torch.float32)
         if sinks.numel() != q.shape[1] or not sinks.is_contiguous():
             raise ValueError("sinks must be a contiguous f32 tensor with one entry per q head")
         sinks_ptr = sinks.data_ptr()
-    opt = attn_paged_options(sinks_ptr, int(window), int(path), int(pages_per_split))
+    opt = attn_paged_options(sinks_ptr, int(window), int(path), int(pages_per_split), kv_dtype, float(k_scale),
+                             float(v_scale))
     ws_ptr, ws_bytes, cached = None, 0, None
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     if plan.workspace_bytes:
@@ -320,6 +329,7 @@ def kv_write(kv_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, bl
     sequence.  ``q_like`` ([T, Hq, D]) supplies the q-head count and row
     count of the dims (a zero-stride stand-in is used when absent)."""
     lib = load_library()
+    _check_device_tensor("kv_pool", kv_pool, torch.bfloat16)
     if q_like is not None:
         dims = make_dims(q_like, kv_pool, block_table, q_like)
     else:
@@ -348,6 +358,7 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
     """The cache write then attention in one call (``attn_paged_fwd_write``)."""
     lib = load_library()
     _check_device_tensor("q", q, torch.bfloat16)
+    _check_device_tensor("kv_pool", kv_pool, torch.bfloat16)
     if out is None:
         out = torch.zeros_like(q)
     dims = make_dims(q, kv_pool, block_table, out)

@@ -68,6 +68,8 @@ struct AttnArgs {
     int32_t fuse_merge;         // split path: the last split of each (sequence, KV head) merges
     const float *sinks;         // [Hq] sink logits (units of the scaled scores), or null
     int32_t window;             // > 0: a query at pos sees only keys >= pos - window + 1; 0: no window
+    int32_t kv_fp8;             // pool holds OCP e4m3 codes (split path only); strides count bytes
+    float v_scale;              // V = v_scale * e4m3(code) (1 for a bf16 pool); k_scale is in scale_log2
 };
 
 struct CombineArgs {

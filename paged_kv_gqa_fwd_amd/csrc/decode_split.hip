@@ -28,60 +28,85 @@ __device__ __forceinline__ float load_coherent(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
+template <int D, bool F8>
 struct DecodeCfg {
     static constexpr int STAGES = decode_stages(D);
     static constexpr int WAVES_PER_SIMD = decode_waves_per_simd(D);
     static constexpr int KROW = D + 8;    // bf16 per LDS K row (16 B pad: conflict-free b128 reads)
     static constexpr int VROW = D + 16;   // bf16 per LDS V row (32 B pad: conflict-free tr reads)
-    static constexpr int CHUNKS = 2 * kPage * D / 8;          // 16-byte chunks per K+V page
-    static constexpr int CH_PER_THREAD = CHUNKS / kThreads;   // D/16
+    static constexpr int EB = F8 ? 1 : 2;                    // bytes per pool element
+    static constexpr int EPC = 16 / EB;                      // pool elements per 16-byte chunk
+    static constexpr int DC = D / EPC;                       // chunks per K or V row
+    static constexpr int CHUNKS = 2 * kPage * DC;            // 16-byte chunks per K+V page
+    static constexpr int CH_PER_THREAD = CHUNKS / kThreads;  // D/16 (bf16) or D/32 (fp8)
     static constexpr int LDS_ELEMS = kPage * (KROW + VROW);
 };
 
 // Issue the 16-byte loads of one page (K and V rows of one KV head) into
-// registers.  Chunk c -> key = c / (D/4), kv = (c / (D/8)) % 2, dc = c % (D/8):
+// registers.  Chunk c -> key = c / (2 DC), kv = (c / DC) % 2, dc = c % DC:
 // consecutive threads read consecutive 16 bytes of one key's K row then V row.
 // Slots at or past `valid` (the tail of a sequence's last page) are not read
 // and stage as zeros: their memory may hold anything, and a non-finite V
 // would turn the zero softmax weight of a masked key into NaN in P.V.
-template <int D>
-__device__ __forceinline__ void load_page(u32x4 (&stage)[DecodeCfg<D>::CH_PER_THREAD],
-                                          const uint16_t *head_base, int64_t page_off,
+// `head_base` and the strides address pool elements (bf16 or fp8 bytes).
+template <int D, bool F8>
+__device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
+                                          const char *head_base, int64_t page_off,
                                           int64_t kv_ss, int64_t kv_skv, int tid, int valid) {
-    constexpr int DC = D / 8;
+    using C = DecodeCfg<D, F8>;
 #pragma unroll
-    for (int it = 0; it < DecodeCfg<D>::CH_PER_THREAD; ++it) {
+    for (int it = 0; it < C::CH_PER_THREAD; ++it) {
         const int c = it * kThreads + tid;
-        const int dc = c % DC;
-        const int kv = (c / DC) & 1;
-        const int key = c / (2 * DC);
-        const uint16_t *src = head_base + page_off + (int64_t)key * kv_ss + kv * kv_skv + dc * 8;
+        const int dc = c % C::DC;
+        const int kv = (c / C::DC) & 1;
+        const int key = c / (2 * C::DC);
+        const char *src = head_base + (page_off + (int64_t)key * kv_ss + kv * kv_skv) * C::EB + dc * 16;
         stage[it] = key < valid ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_page(const u32x4 (&stage)[DecodeCfg<D>::CH_PER_THREAD],
+// Four OCP e4m3 codes (one 32-bit word) to four bf16 (two words), exactly:
+// every e4m3 value is a bf16 value.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);   // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);    // bytes 2, 3
+    const bf16x2_t pa = {(__bf16)a[0], (__bf16)a[1]};
+    const bf16x2_t pb = {(__bf16)b[0], (__bf16)b[1]};
+    lo = __builtin_bit_cast(uint32_t, pa);
+    hi = __builtin_bit_cast(uint32_t, pb);
+}
+
+template <int D, bool F8>
+__device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
                                            uint16_t *ks, uint16_t *vs, int tid) {
-    constexpr int DC = D / 8;
+    using C = DecodeCfg<D, F8>;
 #pragma unroll
-    for (int it = 0; it < DecodeCfg<D>::CH_PER_THREAD; ++it) {
+    for (int it = 0; it < C::CH_PER_THREAD; ++it) {
         const int c = it * kThreads + tid;
-        const int dc = c % DC;
-        const int kv = (c / DC) & 1;
-        const int key = c / (2 * DC);
-        uint16_t *dst = kv ? (vs + key * DecodeCfg<D>::VROW + dc * 8)
-                           : (ks + key * DecodeCfg<D>::KROW + dc * 8);
-        *reinterpret_cast<u32x4 *>(dst) = stage[it];
+        const int dc = c % C::DC;
+        const int kv = (c / C::DC) & 1;
+        const int key = c / (2 * C::DC);
+        uint16_t *dst = kv ? (vs + key * C::VROW + dc * C::EPC) : (ks + key * C::KROW + dc * C::EPC);
+        if constexpr (!F8) {
+            *reinterpret_cast<u32x4 *>(dst) = stage[it];
+        } else {
+            // 16 codes -> 16 bf16 (dequantised; the scales are applied to
+            // the scores and the output)
+            uint32_t o[8];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) e4m3x4_to_bf16x4(stage[it][q4], o[2 * q4], o[2 * q4 + 1]);
+            *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{o[4], o[5], o[6], o[7]};
+        }
     }
 }
 
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DecodeCfg<D>::WAVES_PER_SIMD)))
+__attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
 void paged_decode_split_kernel(const AttnArgs a) {
-    using C = DecodeCfg<D>;
+    using C = DecodeCfg<D, F8>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
     __shared__ float red_m[4][16];
     __shared__ float red_l[4][16];
@@ -137,7 +162,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
         }
     }
 
-    const uint16_t *head_base = a.kv + (int64_t)g * a.kv_sh;
+    const char *head_base = reinterpret_cast<const char *>(a.kv) + (int64_t)g * a.kv_sh * C::EB;
     const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
 
     f32x4 oacc[D / 16];
@@ -203,27 +228,27 @@ void paged_decode_split_kernel(const AttnArgs a) {
         // issue, so the block-table latency stays off the critical path.
         u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
         if (p_begin < p_end)
-            load_page<D>(stA, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
+            load_page<D, F8>(stA, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
                          L - p_begin * kPage);
         if (p_begin + 1 < p_end)
-            load_page<D>(stB, head_base, (int64_t)bt_row[p_begin + 1] * sp, a.kv_ss, a.kv_skv, tid,
+            load_page<D, F8>(stB, head_base, (int64_t)bt_row[p_begin + 1] * sp, a.kv_ss, a.kv_skv, tid,
                          L - (p_begin + 1) * kPage);
         int pid_a = (p_begin + 2 < p_end) ? bt_row[p_begin + 2] : 0;
         for (int p = p_begin; p < p_end; p += 2) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D>(stA, ks, vs, tid);
+            store_page<D, F8>(stA, ks, vs, tid);
             __syncthreads();
             if (p + 2 < p_end)
-                load_page<D>(stA, head_base, (int64_t)pid_a * sp, a.kv_ss, a.kv_skv, tid,
+                load_page<D, F8>(stA, head_base, (int64_t)pid_a * sp, a.kv_ss, a.kv_skv, tid,
                              L - (p + 2) * kPage);
             const int pid_b = (p + 3 < p_end) ? bt_row[p + 3] : 0;
             compute_page(p);
             if (p + 1 >= p_end) break;       // uniform across the workgroup
             __syncthreads();
-            store_page<D>(stB, ks, vs, tid);
+            store_page<D, F8>(stB, ks, vs, tid);
             __syncthreads();
             if (p + 3 < p_end)
-                load_page<D>(stB, head_base, (int64_t)pid_b * sp, a.kv_ss, a.kv_skv, tid,
+                load_page<D, F8>(stB, head_base, (int64_t)pid_b * sp, a.kv_ss, a.kv_skv, tid,
                              L - (p + 3) * kPage);
             pid_a = (p + 4 < p_end) ? bt_row[p + 4] : 0;
             compute_page(p + 1);
@@ -232,15 +257,15 @@ void paged_decode_split_kernel(const AttnArgs a) {
         // One page in flight per workgroup; several workgroups per CU overlap.
         u32x4 st[C::CH_PER_THREAD];
         if (p_begin < p_end)
-            load_page<D>(st, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
+            load_page<D, F8>(st, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
                          L - p_begin * kPage);
         int pid = (p_begin + 1 < p_end) ? bt_row[p_begin + 1] : 0;
         for (int p = p_begin; p < p_end; ++p) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D>(st, ks, vs, tid);
+            store_page<D, F8>(st, ks, vs, tid);
             __syncthreads();
             if (p + 1 < p_end)
-                load_page<D>(st, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid,
+                load_page<D, F8>(st, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid,
                              L - (p + 1) * kPage);
             pid = (p + 2 < p_end) ? bt_row[p + 2] : 0;
             compute_page(p);
@@ -287,6 +312,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
             lsum += red_l[ww][r] * exp2_fast(red_m[ww][r] - Mr_use);
             osum += ored[(ww * 16 + r) * D + d];
         }
+        if constexpr (F8) osum *= a.v_scale;   // V = v_scale * e4m3(code)
         const int ri = r / G;
         const int rh = g * G + (r - ri * G);
         const int64_t t = q0 + ri;
@@ -423,7 +449,10 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
 
 template <int D>
 hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL(paged_decode_split_kernel<D>, grid, dim3(kThreads), 0, stream, a);
+    if (a.kv_fp8)
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

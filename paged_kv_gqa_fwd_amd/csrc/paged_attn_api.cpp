@@ -74,9 +74,16 @@ int32_t effective_window(const attn_paged_dims *d, int32_t window) {
 }
 
 int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
-              int32_t pps, int32_t window, attn_paged_plan *plan) {
+              int32_t pps, int32_t window, attn_paged_plan *plan, int32_t kv_dtype = ATTN_KV_BF16) {
     int rc = validate_dims(d, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
+    if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    if (kv_dtype == ATTN_KV_FP8_E4M3) {
+        // 16-byte aligned rows of D one-byte codes
+        const int64_t kvs[] = {d->kv_stride_page, d->kv_stride_slot, d->kv_stride_head, d->kv_stride_kv};
+        for (int64_t st : kvs)
+            if ((st & 15) != 0) return ATTN_ERR_STRIDE;
+    }
     if (!plan) return ATTN_ERR_NULL;
     if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_SPLIT_FUSED) return ATTN_ERR_SHAPE;
     if (pps < 0 || window < 0) return ATTN_ERR_SHAPE;
@@ -91,6 +98,7 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         path = (mq * G <= kMaxDecodeRows) ? ATTN_PATH_SPLIT_DECODE : ATTN_PATH_PREFILL;
     const bool split_path = path == ATTN_PATH_SPLIT_DECODE || path == ATTN_PATH_SPLIT_FUSED;
     if (split_path && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
+    if (!split_path && kv_dtype != ATTN_KV_BF16) return ATTN_ERR_UNSUPPORTED;   // prefill reads bf16 only
     *plan = attn_paged_plan{};
     plan->path = path;
     plan->block_threads = pa::kThreads;
@@ -167,10 +175,13 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
                   const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
                   size_t workspace_bytes, int32_t path_hint, int32_t pps, const float *sinks,
-                  int32_t window, attn_paged_plan &plan, pa::AttnArgs &a) {
-    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan);
+                  int32_t window, attn_paged_plan &plan, pa::AttnArgs &a, int32_t kv_dtype = ATTN_KV_BF16,
+                  float k_scale = 1.f, float v_scale = 1.f) {
+    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan, kv_dtype);
     if (rc != ATTN_OK) return rc;
     if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
+    if (kv_dtype == ATTN_KV_BF16) k_scale = v_scale = 1.f;   // the scales belong to an fp8 cache only
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale)) return ATTN_ERR_SHAPE;
     if (n_seqs == 0) return ATTN_OK;
     if (!out || !q || !kv_pool || !block_table || !seq_lens || !cu_q) return ATTN_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return ATTN_ERR_ALIGN;
@@ -208,7 +219,9 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     a.pages_per_split = plan.pages_per_split;
     a.max_splits = plan.max_splits;
     a.causal = causal ? 1 : 0;
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)k_scale);
+    a.kv_fp8 = kv_dtype == ATTN_KV_FP8_E4M3 ? 1 : 0;
+    a.v_scale = v_scale;
     // The prefill kernel takes the maximum of raw scores and applies the
     // scale afterwards, which needs a positive scale: a negative one is
     // applied by negating Q (exact), and zero as the smallest normal float
@@ -277,11 +290,13 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
                    const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
                    float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
                    size_t workspace_bytes, void *stream, int32_t path_hint, int32_t pps,
-                   const float *sinks = nullptr, int32_t window = 0) {
+                   const float *sinks = nullptr, int32_t window = 0, int32_t kv_dtype = ATTN_KV_BF16,
+                   float k_scale = 1.f, float v_scale = 1.f) {
     attn_paged_plan plan;
     pa::AttnArgs a;
     int rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal,
-                           dims, workspace, workspace_bytes, path_hint, pps, sinks, window, plan, a);
+                           dims, workspace, workspace_bytes, path_hint, pps, sinks, window, plan, a, kv_dtype,
+                           k_scale, v_scale);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     return paged_launch(plan, a, dims->head_dim, static_cast<hipStream_t>(stream));
 }
@@ -501,7 +516,7 @@ int attn_paged_fwd_ex(void *out, const void *q, const void *kv_pool, const int32
 int attn_paged_make_plan_opt(const attn_paged_dims *dims, int32_t n_seqs, int32_t max_q,
                              const attn_paged_options *opt, attn_paged_plan *plan) {
     if (!opt) return ATTN_ERR_NULL;
-    return make_plan(dims, n_seqs, max_q, opt->path_hint, opt->pages_per_split, opt->window, plan);
+    return make_plan(dims, n_seqs, max_q, opt->path_hint, opt->pages_per_split, opt->window, plan, opt->kv_dtype);
 }
 
 int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
@@ -511,7 +526,7 @@ int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int3
     if (!opt) return ATTN_ERR_NULL;
     return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
                           workspace, workspace_bytes, stream, opt->path_hint, opt->pages_per_split, opt->sinks,
-                          opt->window);
+                          opt->window, opt->kv_dtype, opt->k_scale, opt->v_scale);
 }
 
 int attn_paged_kv_write(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,

@@ -248,6 +248,32 @@ def test_options_validate_and_shrink_the_split_plan(pa):
         (full.pages_per_split, full.max_splits, full.workspace_bytes)
 
 
+def test_fp8_cache_options_validate(pa):
+    import paged_kv_gqa_fwd_amd as mod
+    lib = pa.load_library()
+    d = dims(max_pages_per_seq=128, bt_stride=128)   # kv strides: multiples of 16
+    plan = mod.attn_paged_plan()
+
+    def mp(o, dd=d, max_q=1):
+        return lib.attn_paged_make_plan_opt(ctypes.byref(dd), 64, max_q, ctypes.byref(o), ctypes.byref(plan))
+
+    def fo(o):
+        return lib.attn_paged_fwd_opt(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1, 0.1, 1, ctypes.byref(d),
+                                      ctypes.byref(o), FAKE, 1 << 30, None)
+    f8 = lambda **kw: mod.attn_paged_options(kw.get("sinks"), kw.get("window", 0), kw.get("path", 0),
+                                             kw.get("pps", 0), kw.get("dtype", 1), kw.get("ks", 1.0),
+                                             kw.get("vs", 1.0))
+    assert mp(f8()) == OK and plan.path == mod.PATH_SPLIT_DECODE
+    assert mp(f8(dtype=2)) == E_UNSUP
+    assert mp(f8(path=2)) == E_UNSUP                        # the prefill kernel reads bf16 only
+    assert mp(f8(), max_q=5) == E_UNSUP                     # 20 packed rows: prefill would be needed
+    assert mp(f8(), dd=dims(max_pages_per_seq=128, bt_stride=128, kv_stride_kv=136)) == E_STRIDE
+    assert fo(f8(ks=float("inf"))) == E_SHAPE
+    assert fo(f8(vs=float("nan"))) == E_SHAPE
+    # a bf16 cache ignores the scales (a zeroed options struct stays valid)
+    assert mp(mod.attn_paged_options(None, 0, 0, 0, 0, 0.0, 0.0)) == OK
+
+
 def test_workspace_clear_validates(pa):
     lib = pa.load_library()
     assert lib.attn_workspace_clear(None, 0, None) == OK          # nothing to do

@@ -1,0 +1,96 @@
+"""GPU parity of decode over an fp8 (OCP e4m3) paged KV cache against the
+fp64 oracle (same codes, same per-tensor scales), through the C ABI.
+
+Tolerance: the bf16 bar (max-abs 2e-2, rel-RMS 5e-3).  The dequantisation
+is exact (every e4m3 value is a bf16 value; the scales enter the scores and
+the output in f32), so the error budget is the bf16 path's.
+"""
+import math
+
+import pytest
+import torch
+
+import workloads
+from parity_util import compare, log
+
+pytestmark = pytest.mark.gpu
+
+PATH_AUTO, PATH_SPLIT, PATH_PREFILL, PATH_FUSED = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_gqa_fwd_amd as pa
+    pa.load_library()
+
+
+def _check(oracle_mod, case8, ks, vs, what, path=PATH_AUTO, pps=0, window=0, sinks=None):
+    import paged_kv_gqa_fwd_amd as pa
+    ref = oracle_mod.paged_attn(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, case8.scale,
+                                case8.causal, k_scale=ks, v_scale=vs, window=window,
+                                sinks=None if sinks is None else sinks.double().numpy())
+    g = case8.to("cuda")
+    log("  gpu fp8 call: %s path=%d pps=%d W=%d" % (what, path, pps, window))
+    out = pa.paged_attention(g.q, g.kv, g.block_table, g.seq_lens, g.cu_q, max(case8.max_q, 1), case8.scale,
+                             case8.causal, path=path, pages_per_split=pps, window=window, k_scale=ks, v_scale=vs,
+                             sinks=None if sinks is None else sinks.cuda())
+    torch.cuda.synchronize()
+    compare(out, ref, what=what)
+    return out
+
+
+@pytest.mark.parametrize("path,pps", [(PATH_AUTO, 0), (PATH_SPLIT, 1), (PATH_SPLIT, 1000), (PATH_FUSED, 3)])
+def test_decode_batch_fp8(oracle_mod, path, pps):
+    case8 = workloads.fp8_pool_case(workloads.decode_batch(n_seqs=12, seed=821))
+    _check(oracle_mod, case8, 0.5, 0.5, "decode fp8 path=%d pps=%d" % (path, pps), path, pps)
+
+
+def test_long_decode_fp8_d256(oracle_mod):
+    case8 = workloads.fp8_pool_case(workloads.long_decode(n_seqs=4, ctx=8192, seed=822), mult=8.0)
+    _check(oracle_mod, case8, 0.125, 0.125, "long decode fp8 D256")
+
+
+def test_tiny_mixed_rows_fp8(oracle_mod):
+    """Several query rows per sequence (6 heads x 2 tokens = 12 packed rows), the
+    two-layer pool, poisoned tails, another K scale (V kept at unit size, the
+    scale the absolute tolerance is stated for)."""
+    base = workloads.make_case("f8-multi", 823, [2, 1, 2], [130, 64, 1], 24, 4, 256, causal=True, poison=True,
+                               layers=2, layer=1)
+    case8 = workloads.fp8_pool_case(base)
+    _check(oracle_mod, case8, 0.3, 0.5, "fp8 multi-row")
+
+
+def test_fp8_with_window_and_sinks(oracle_mod):
+    case8 = workloads.fp8_pool_case(workloads.decode_batch(n_seqs=6, seed=824))
+    sinks = torch.linspace(-1.0, 3.0, 32)
+    sinks[0] = -math.inf
+    _check(oracle_mod, case8, 0.5, 0.5, "fp8 W=700 sinks", window=700, sinks=sinks)
+
+
+def test_fp8_equals_bf16_on_exact_values():
+    """With power-of-two scales the dequantised cache is exactly a bf16 cache:
+    the fp8 kernel must give the bf16 kernel's bits."""
+    import dataclasses
+    import paged_kv_gqa_fwd_amd as pa
+    case8 = workloads.fp8_pool_case(workloads.decode_batch(n_seqs=8, seed=825)).to("cuda")
+    vals = case8.pool_storage.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    kvb = vals.as_strided(case8.kv.shape, case8.kv.stride(), case8.kv.storage_offset())
+    kvb[:, :, :, 0] *= 0.5
+    kvb[:, :, :, 1] *= 0.25
+    caseb = dataclasses.replace(case8, pool_storage=vals, kv=kvb)
+    a = pa.paged_attention(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, 1, case8.scale, True,
+                           k_scale=0.5, v_scale=0.25)
+    b = pa.paged_attention(caseb.q, caseb.kv, caseb.block_table, caseb.seq_lens, caseb.cu_q, 1, caseb.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_prefill_is_unsupported():
+    import paged_kv_gqa_fwd_amd as pa
+    case8 = workloads.fp8_pool_case(workloads.chunked_prefill(n_seqs=2, q_lo=100, q_hi=200, ctx_hi=300,
+                                                              seed=826)).to("cuda")
+    with pytest.raises(pa.AttnError):
+        pa.paged_attention(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, case8.max_q,
+                           case8.scale, True, k_scale=1.0, v_scale=1.0)
