@@ -43,6 +43,19 @@ constexpr int prefill_rows(int d) { return d == 128 ? 256 : 128; }
 #endif
 constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 256; }
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
+// Pages in flight per workgroup over an fp8 cache: a page carries half the
+// bytes, so more of them keep the same bytes in flight in the same registers.
+#ifndef PA_DECODE_F8_STAGES_128
+#define PA_DECODE_F8_STAGES_128 4
+#endif
+#ifndef PA_DECODE_F8_STAGES_256
+#define PA_DECODE_F8_STAGES_256 2
+#endif
+constexpr int decode_stages_f8(int d) { return d == 128 ? PA_DECODE_F8_STAGES_128 : PA_DECODE_F8_STAGES_256; }
+#ifndef PA_DECODE_F8_WAVES_128
+#define PA_DECODE_F8_WAVES_128 2
+#endif
+constexpr int decode_waves_per_simd_f8(int d) { return d == 128 ? PA_DECODE_F8_WAVES_128 : PA_DECODE_WAVES_256; }
 constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
 
 // Arguments shared by the split-KV decode kernel and the prefill kernel.

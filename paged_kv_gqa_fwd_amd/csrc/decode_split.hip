@@ -30,8 +30,8 @@ __device__ __forceinline__ float load_coherent(const float *p) {
 
 template <int D, bool F8>
 struct DecodeCfg {
-    static constexpr int STAGES = decode_stages(D);
-    static constexpr int WAVES_PER_SIMD = decode_waves_per_simd(D);
+    static constexpr int STAGES = F8 ? decode_stages_f8(D) : decode_stages(D);
+    static constexpr int WAVES_PER_SIMD = F8 ? decode_waves_per_simd_f8(D) : decode_waves_per_simd(D);
     static constexpr int KROW = D + 8;    // bf16 per LDS K row (16 B pad: conflict-free b128 reads)
     static constexpr int VROW = D + 16;   // bf16 per LDS V row (32 B pad: conflict-free tr reads)
     static constexpr int EB = F8 ? 1 : 2;                    // bytes per pool element
@@ -66,15 +66,11 @@ __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_P
 }
 
 // Four OCP e4m3 codes (one 32-bit word) to four bf16 (two words), exactly:
-// every e4m3 value is a bf16 value.
+// every e4m3 value is a bf16 value (one conversion instruction per pair,
+// with a unit scale).
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);   // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);    // bytes 2, 3
-    const bf16x2_t pa = {(__bf16)a[0], (__bf16)a[1]};
-    const bf16x2_t pb = {(__bf16)b[0], (__bf16)b[1]};
-    lo = __builtin_bit_cast(uint32_t, pa);
-    hi = __builtin_bit_cast(uint32_t, pb);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));  // bytes 0, 1
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));   // bytes 2, 3
 }
 
 template <int D, bool F8>
@@ -222,7 +218,33 @@ void paged_decode_split_kernel(const AttnArgs a) {
     };
 
     const int64_t sp = a.kv_sp;
-    if constexpr (C::STAGES == 2) {
+    if constexpr (C::STAGES >= 3) {
+        // A ring of STAGES pages in flight: page p stages in slot (p - p_begin)
+        // % STAGES, and its slot is refilled with page p + STAGES once the
+        // page is in LDS.  Each page id is read before the LDS store so its
+        // latency overlaps it.
+        u32x4 st[C::STAGES][C::CH_PER_THREAD];
+#pragma unroll
+        for (int k = 0; k < C::STAGES; ++k)
+            if (p_begin + k < p_end)
+                load_page<D, F8>(st[k], head_base, (int64_t)bt_row[p_begin + k] * sp, a.kv_ss, a.kv_skv, tid,
+                                 L - (p_begin + k) * kPage);
+        for (int p0 = p_begin; p0 < p_end; p0 += C::STAGES) {
+#pragma unroll
+            for (int k = 0; k < C::STAGES; ++k) {
+                const int p = p0 + k;
+                if (p >= p_end) break;           // uniform across the workgroup
+                const int pn = p + C::STAGES;
+                const int pid = pn < p_end ? bt_row[pn] : 0;
+                __syncthreads();                 // the previous page is fully consumed
+                store_page<D, F8>(st[k], ks, vs, tid);
+                __syncthreads();
+                if (pn < p_end)
+                    load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid, L - pn * kPage);
+                compute_page(p);
+            }
+        }
+    } else if constexpr (C::STAGES == 2) {
         // Two pages in flight: stage A holds even pages of the split, stage B
         // odd ones.  Each page id is read one compute phase before its loads
         // issue, so the block-table latency stays off the critical path.

@@ -87,6 +87,29 @@ def test_fp8_equals_bf16_on_exact_values():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_every_code_decodes_exactly():
+    """Each sequence has one key, so out = its V row: the 254 non-NaN codes
+    (NaN codes replaced by 0) must come out as torch's e4m3 decoding, exactly
+    (as values: the code of -0 comes out as +0, the sum P.V starting at +0)."""
+    import paged_kv_gqa_fwd_amd as pa
+    case = workloads.make_case("f8-codes", 827, [1, 1], [1, 1], 2, 2, 128, causal=True)
+    case8 = workloads.fp8_pool_case(case)
+    codes = torch.arange(256, dtype=torch.int32)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    for b in range(2):
+        pg = int(case8.block_table[b, 0])
+        for g in range(2):
+            case8.kv[pg, 0, g, 1] = codes[128 * b:128 * b + 128].to(torch.uint8)
+    g8 = case8.to("cuda")
+    out = pa.paged_attention(g8.q, g8.kv, g8.block_table, g8.seq_lens, g8.cu_q, 1, case8.scale, True,
+                             k_scale=1.0, v_scale=1.0)
+    torch.cuda.synchronize()
+    expect = codes.to(torch.uint8).view(torch.float8_e4m3fn).to(torch.bfloat16).view(2, 128)
+    for b in range(2):
+        for h in range(2):
+            assert torch.equal(out[b, h].cpu().float(), expect[b].float()), (b, h)
+
+
 def test_fp8_prefill_is_unsupported():
     import paged_kv_gqa_fwd_amd as pa
     case8 = workloads.fp8_pool_case(workloads.chunked_prefill(n_seqs=2, q_lo=100, q_hi=200, ctx_hi=300,
