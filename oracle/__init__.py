@@ -59,6 +59,8 @@ def _load():
         lib.oracle_quant_attn.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, f64, i32, i32, p, p, i32]
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_e4m3_encode.argtypes = [f64]
+        lib.oracle_e4m3_encode_array.restype = None
+        lib.oracle_e4m3_encode_array.argtypes = [p, p, i64]
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         _lib = lib
@@ -124,7 +126,18 @@ def paged_attn(q, kv_pool, block_table, seq_lens, cu_q, scale: float, causal: bo
     return (out, lse) if return_lse else out
 
 
-def kv_write(kv_pool, k_new, v_new, block_table, seq_lens, cu_q):
+def e4m3_quantize(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """uint8 OCP e4m3 codes of x * (1 / scale), the reciprocal and the product
+    rounded to f32 (the quantised path's reading of "value / scale"), then the
+    encoder above (round to nearest even, saturating at +-448)."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = np.ascontiguousarray((x.float().numpy() * inv).astype(np.float32))
+    out = np.zeros(y.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_array(y.ctypes.data, out.ctypes.data, y.size)
+    return torch.from_numpy(out)
+
+
+def kv_write(kv_pool, k_new, v_new, block_table, seq_lens, cu_q, k_scale=None, v_scale=None):
     """The KV-cache write that runs just before attention (metrale blueprint
     graph.json: node l3.attn.kv_write precedes l3.attn.attend), into the paged
     layout of kern-kernels examples/decode.json (buffers kv / table / seq /
@@ -138,8 +151,13 @@ def kv_write(kv_pool, k_new, v_new, block_table, seq_lens, cu_q):
     place in the cache and are not written.
 
     kv_pool: bf16 [NP, P, Hkv, 2, D] CPU view; k_new, v_new: bf16 [T, Hkv, D].
+    A uint8 pool is an fp8 cache: the rows are stored as e4m3_quantize(row,
+    k_scale) and e4m3_quantize(row, v_scale).
     """
     pool = kv_pool.clone()
+    if pool.dtype == torch.uint8:
+        k_new = e4m3_quantize(k_new, k_scale)
+        v_new = e4m3_quantize(v_new, v_scale)
     P = pool.shape[1]
     bt = block_table.to(torch.int64)
     for b in range(seq_lens.numel()):

@@ -105,6 +105,12 @@ uint8_t oracle_e4m3_encode(double x)
     return sign | (uint8_t)((ub << 3) | mant);
 }
 
+/* Codes of n f32 values (the encoder above, element by element). */
+void oracle_e4m3_encode_array(const float *x, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode((double)x[i]);
+}
+
 double oracle_e4m3_decode(uint8_t c)
 {
     const int s = c >> 7, ub = (c >> 3) & 15, m = c & 7;

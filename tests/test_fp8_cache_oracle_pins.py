@@ -75,3 +75,39 @@ def test_brute_force_over_torch_decoding(oracle_mod):
                 w = torch.softmax(s, dim=0)
                 np.testing.assert_allclose(got[t0 + i, h], (w @ V[:vis, h // 2]).numpy(), rtol=0, atol=1e-12)
         t0 += n
+
+
+def test_quantize_matches_torch_e4m3(oracle_mod):
+    """e4m3_quantize(x, s) equals torch's float8_e4m3fn conversion of the f32
+    product x * (1/s) wherever that product is inside [-448, 448] (torch has no
+    saturation; the oracle saturates, pinned by the encoder's own pins)."""
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(4096, generator=g) * 3).to(torch.bfloat16)
+    for s in (1.0, 0.25, 0.037, 3.0):
+        got = oracle_mod.e4m3_quantize(x, s)
+        y = x.float() * (torch.tensor(1.0, dtype=torch.float32) / torch.tensor(s, dtype=torch.float32))
+        inside = y.abs() <= 448
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        assert torch.equal(got[inside], ref[inside]), s
+
+
+def test_fp8_write_then_attend_is_quantised_attention(oracle_mod):
+    """The fp8 write stores the quantised new rows: attention over the written
+    fp8 cache equals attention over a bf16 cache that holds the dequantised
+    rows (power-of-two scales keep every dequantised value a bf16 value)."""
+    import dataclasses
+    base = workloads.make_case("f8w", 743, [1, 3], [70, 129], 8, 2, 32, causal=True, scale=0.3)
+    case8 = workloads.fp8_pool_case(base)
+    k_new, v_new = workloads.new_kv_tokens(base, 44)
+    ks, vs = 0.5, 0.25
+    w8 = oracle_mod.kv_write(case8.kv, k_new, v_new, case8.block_table, case8.seq_lens, case8.cu_q,
+                             k_scale=ks, v_scale=vs)
+    got = oracle_mod.paged_attn(case8.q, w8, case8.block_table, case8.seq_lens, case8.cu_q, case8.scale, True,
+                                k_scale=ks, v_scale=vs)
+    kq = oracle_mod.e4m3_quantize(k_new, ks).view(torch.float8_e4m3fn).float() * ks
+    vq = oracle_mod.e4m3_quantize(v_new, vs).view(torch.float8_e4m3fn).float() * vs
+    cb = _decoded_bf16_case(case8, ks, vs)
+    wb = oracle_mod.kv_write(cb.kv, kq.to(torch.bfloat16), vq.to(torch.bfloat16), cb.block_table, cb.seq_lens,
+                             cb.cu_q)
+    ref = oracle_mod.paged_attn(cb.q, wb, cb.block_table, cb.seq_lens, cb.cu_q, cb.scale, True)
+    assert np.array_equal(got, ref)
