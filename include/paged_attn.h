@@ -270,6 +270,26 @@ int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void
                          size_t workspace_bytes, void *stream);
 
 /*
+ * attn_paged_kv_write_opt / attn_paged_fwd_write_opt -- the same calls with
+ * options (attn_paged_options above; the write uses kv_dtype, k_scale and
+ * v_scale, the attention all of them).  Into an fp8 cache the new rows are
+ * stored as OCP e4m3 codes of x * (1 / scale), with the reciprocal and the
+ * product in f32, rounded to nearest even and saturating at +-448 (the
+ * quantised path's reading of "value / scale"); the scales must be finite
+ * and nonzero.
+ */
+int attn_paged_kv_write_opt(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
+                            const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                            const attn_paged_dims *dims, const attn_kv_new_dims *new_dims,
+                            const attn_paged_options *opt, void *stream);
+int attn_paged_fwd_write_opt(void *out, const void *q, const void *k_new, const void *v_new, void *kv_pool,
+                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *cu_q,
+                             int32_t n_seqs, int32_t max_q, float scale, int32_t causal,
+                             const attn_paged_dims *dims, const attn_kv_new_dims *new_dims,
+                             const attn_paged_options *opt, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * attn_workspace_clear -- enqueue a kernel that sets bytes [0, bytes) of a
  * device workspace to zero (the merge counters of the fused split path must
  * start at zero).  A kernel, not a memset node, so that graph capture of it

@@ -142,6 +142,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_fwd_write.argtypes = [p, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, nd_p,
                                          p, sz, p]
     lib.attn_paged_fwd_write.restype = ctypes.c_int
+    lib.attn_paged_kv_write_opt.argtypes = [p, p, p, p, p, p, i32, i32, dims_p, nd_p, ctypes.POINTER(attn_paged_options), p]
+    lib.attn_paged_kv_write_opt.restype = ctypes.c_int
+    lib.attn_paged_fwd_write_opt.argtypes = [p, p, p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, nd_p,
+                                             ctypes.POINTER(attn_paged_options), p, sz, p]
+    lib.attn_paged_fwd_write_opt.restype = ctypes.c_int
     lib.attn_workspace_clear.argtypes = [p, sz, p]
     lib.attn_workspace_clear.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -321,15 +326,23 @@ def _new_kv_dims(k_new: torch.Tensor, v_new: torch.Tensor) -> attn_kv_new_dims:
     return attn_kv_new_dims(k_new.stride(0), k_new.stride(1), v_new.stride(0), v_new.stride(1))
 
 
+def _pool_dtype(kv_pool: torch.Tensor) -> int:
+    if kv_pool.dtype == torch.uint8:
+        return KV_FP8_E4M3
+    _check_device_tensor("kv_pool", kv_pool, torch.bfloat16)
+    return KV_BF16
+
+
 def kv_write(kv_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
              seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int, q_like: Optional[torch.Tensor] = None,
-             stream: Optional[torch.cuda.Stream] = None) -> None:
-    """The KV-cache write (``attn_paged_kv_write``): the new K/V rows
+             stream: Optional[torch.cuda.Stream] = None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """The KV-cache write (``attn_paged_kv_write_opt``): the new K/V rows
     k_new / v_new [T, Hkv, D] go to key positions L - n .. L - 1 of each
-    sequence.  ``q_like`` ([T, Hq, D]) supplies the q-head count and row
-    count of the dims (a zero-stride stand-in is used when absent)."""
+    sequence (as e4m3 codes of x / scale into a uint8 fp8 cache).  ``q_like``
+    ([T, Hq, D]) supplies the q-head count of the dims (one q head per KV
+    head is described when absent)."""
     lib = load_library()
-    _check_device_tensor("kv_pool", kv_pool, torch.bfloat16)
+    kv_dtype = _pool_dtype(kv_pool)
     if q_like is not None:
         dims = make_dims(q_like, kv_pool, block_table, q_like)
     else:
@@ -343,10 +356,12 @@ def kv_write(kv_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, bl
             kv_stride_page=s[0], kv_stride_slot=s[1], kv_stride_head=s[2], kv_stride_kv=s[3],
             bt_stride=block_table.stride(0))
     nd = _new_kv_dims(k_new, v_new)
+    opt = attn_paged_options(None, 0, 0, 0, kv_dtype, float(k_scale), float(v_scale))
     st = stream if stream is not None else torch.cuda.current_stream(kv_pool.device)
-    rc = lib.attn_paged_kv_write(kv_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(),
-                                 seq_lens.data_ptr(), cu_q.data_ptr(), seq_lens.numel(), int(max_q),
-                                 ctypes.byref(dims), ctypes.byref(nd), ctypes.c_void_p(st.cuda_stream))
+    rc = lib.attn_paged_kv_write_opt(kv_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), block_table.data_ptr(),
+                                     seq_lens.data_ptr(), cu_q.data_ptr(), seq_lens.numel(), int(max_q),
+                                     ctypes.byref(dims), ctypes.byref(nd), ctypes.byref(opt),
+                                     ctypes.c_void_p(st.cuda_stream))
     if rc != ATTN_OK:
         raise AttnError(rc)
 
@@ -354,16 +369,18 @@ def kv_write(kv_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, bl
 def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kv_pool: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int,
                           scale: float, causal: bool = True, out: Optional[torch.Tensor] = None,
-                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """The cache write then attention in one call (``attn_paged_fwd_write``)."""
+                          stream: Optional[torch.cuda.Stream] = None, k_scale: float = 1.0,
+                          v_scale: float = 1.0) -> torch.Tensor:
+    """The cache write then attention in one call (``attn_paged_fwd_write_opt``)."""
     lib = load_library()
     _check_device_tensor("q", q, torch.bfloat16)
-    _check_device_tensor("kv_pool", kv_pool, torch.bfloat16)
+    kv_dtype = _pool_dtype(kv_pool)
     if out is None:
         out = torch.zeros_like(q)
     dims = make_dims(q, kv_pool, block_table, out)
     nd = _new_kv_dims(k_new, v_new)
-    plan = make_plan(dims, seq_lens.numel(), max_q)
+    plan = make_plan(dims, seq_lens.numel(), max_q, kv_dtype=kv_dtype)
+    opt = attn_paged_options(None, 0, 0, 0, kv_dtype, float(k_scale), float(v_scale))
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     ws_ptr, ws_bytes, cached = None, 0, None
     if plan.workspace_bytes:
@@ -371,11 +388,11 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
         if cached.clean < plan.counter_bytes:
             workspace_clear(cached.buf, plan.counter_bytes, st)
         ws_ptr, ws_bytes = cached.buf.data_ptr(), cached.buf.numel()
-    rc = lib.attn_paged_fwd_write(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-                                  kv_pool.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
-                                  cu_q.data_ptr(), seq_lens.numel(), int(max_q), float(scale),
-                                  int(bool(causal)), ctypes.byref(dims), ctypes.byref(nd), ws_ptr, ws_bytes,
-                                  ctypes.c_void_p(st.cuda_stream))
+    rc = lib.attn_paged_fwd_write_opt(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                      kv_pool.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                      cu_q.data_ptr(), seq_lens.numel(), int(max_q), float(scale),
+                                      int(bool(causal)), ctypes.byref(dims), ctypes.byref(nd), ctypes.byref(opt),
+                                      ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream))
     if rc != ATTN_OK:
         raise AttnError(rc)
     if cached is not None:

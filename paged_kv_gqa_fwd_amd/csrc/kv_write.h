@@ -15,6 +15,8 @@ struct KvWriteArgs {
     int64_t bt_stride;
     int64_t k_st, k_sh, v_st, v_sh;
     int32_t n_seqs, max_q, hkv, d;
+    int32_t fp8;                 // pool holds OCP e4m3 codes (strides count bytes)
+    float k_inv, v_inv;          // fp8: code = e4m3(x * (1 / scale)), product in f32
 };
 
 }  // namespace pa

@@ -8,12 +8,16 @@
 // every KV head go to page block_table[b][pos / 64], slot pos % 64.  Tokens
 // with pos < 0 (more new tokens than keys) have no slot and are skipped.
 //
+// Into an fp8 cache the rows are stored as OCP e4m3 codes of x * (1/scale)
+// (one scale for K, one for V; the product in f32, round to nearest even,
+// saturating), the quantised path's reading of "value / scale".
+//
 // Design (MI355X): one workgroup of 256 threads per (sequence, group of
-// kWriteTok new tokens).  A token's rows are 2 * Hkv * D bf16; thread c moves
-// 16-byte chunk c (chunk fastest, then K/V, then KV head, then token), so
-// consecutive lanes read consecutive bytes of the new rows and write whole
-// 16-byte runs of one slot.  HBM-bound: every new byte is read once and
-// written once.
+// kWriteTok new tokens).  A token's rows are 2 * Hkv * D elements; thread c
+// writes 16-byte output chunk c (chunk fastest, then K/V, then KV head, then
+// token), so consecutive lanes read consecutive bytes of the new rows and
+// write whole 16-byte runs of one slot.  HBM-bound: every new byte is read
+// once and written once.
 #include "attn_device.h"
 #include "kv_write.h"
 
@@ -21,6 +25,33 @@ namespace pa {
 
 constexpr int kWriteTok = 4;   // new tokens per workgroup
 
+// |y| > 448 becomes +-448 (the largest e4m3 value); NaN stays NaN.  The
+// conversion instruction alone does not saturate out-of-range inputs.
+__device__ __forceinline__ float e4m3_saturate(float y) {
+    return fabsf(y) > 448.f ? copysignf(448.f, y) : y;
+}
+
+// Sixteen bf16 (two 16-byte words) to sixteen e4m3 codes of x * inv: the
+// product in f32, saturated to +-448, then v_cvt_pk_fp8_f32 (round to
+// nearest even).
+__device__ __forceinline__ u32x4 bf16x16_to_e4m3(const u32x4 a, const u32x4 b, float inv) {
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const u32x4 &src = w < 2 ? a : b;
+        const uint32_t x0 = src[2 * (w & 1)], x1 = src[2 * (w & 1) + 1];
+        const float f0 = e4m3_saturate(__uint_as_float(x0 << 16) * inv);
+        const float f1 = e4m3_saturate(__uint_as_float(x0 & 0xFFFF0000u) * inv);
+        const float f2 = e4m3_saturate(__uint_as_float(x1 << 16) * inv);
+        const float f3 = e4m3_saturate(__uint_as_float(x1 & 0xFFFF0000u) * inv);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, word, true);
+        r[w] = (uint32_t)word;
+    }
+    return r;
+}
+
+template <bool F8>
 __global__ __launch_bounds__(kThreads) void paged_kv_write_kernel(const KvWriteArgs a) {
     const int b = blockIdx.y;
     const int i0 = blockIdx.x * kWriteTok;
@@ -29,7 +60,8 @@ __global__ __launch_bounds__(kThreads) void paged_kv_write_kernel(const KvWriteA
     if (n > a.max_q) n = a.max_q;   // caller contract: n_b <= max_q
     if (i0 >= n) return;
     const int L = a.seq_lens[b];
-    const int chunks = a.d / 8;                  // 16-byte chunks per row
+    constexpr int EPC = F8 ? 16 : 8;             // pool elements per 16-byte output chunk
+    const int chunks = a.d / EPC;                // output chunks per row
     const int per_head = 2 * chunks;             // K row then V row
     const int per_tok = a.hkv * per_head;
     const int total = (min(n, i0 + kWriteTok) - i0) * per_tok;
@@ -45,19 +77,29 @@ __global__ __launch_bounds__(kThreads) void paged_kv_write_kernel(const KvWriteA
         const int kv = r2 / chunks;              // 0 = K, 1 = V
         const int ch = r2 - kv * chunks;
         const int64_t t = q0 + i;
-        const uint16_t *src = kv ? a.v_new + t * a.v_st + (int64_t)g * a.v_sh
-                                 : a.k_new + t * a.k_st + (int64_t)g * a.k_sh;
+        const uint16_t *src = (kv ? a.v_new + t * a.v_st + (int64_t)g * a.v_sh
+                                  : a.k_new + t * a.k_st + (int64_t)g * a.k_sh) + EPC * ch;
         const int64_t page = bt_row[pos / kPage];
-        uint16_t *dst = a.kv + page * a.kv_sp + (int64_t)(pos % kPage) * a.kv_ss + (int64_t)g * a.kv_sh +
-                        kv * a.kv_skv;
-        *reinterpret_cast<u32x4 *>(dst + 8 * ch) = *reinterpret_cast<const u32x4 *>(src + 8 * ch);
+        const int64_t off = page * a.kv_sp + (int64_t)(pos % kPage) * a.kv_ss + (int64_t)g * a.kv_sh +
+                            kv * a.kv_skv + EPC * ch;   // pool elements
+        if constexpr (!F8) {
+            *reinterpret_cast<u32x4 *>(a.kv + off) = *reinterpret_cast<const u32x4 *>(src);
+        } else {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(src + 8);
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.kv) + off) =
+                bf16x16_to_e4m3(lo, hi, kv ? a.v_inv : a.k_inv);
+        }
     }
 }
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream) {
     if (a.n_seqs == 0 || a.max_q == 0) return hipSuccess;
     const dim3 grid((a.max_q + kWriteTok - 1) / kWriteTok, a.n_seqs);
-    hipLaunchKernelGGL(paged_kv_write_kernel, grid, dim3(kThreads), 0, stream, a);
+    if (a.fp8)
+        hipLaunchKernelGGL(paged_kv_write_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(paged_kv_write_kernel<false>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -304,10 +304,20 @@ int paged_fwd_impl(void *out, const void *q, const void *kv_pool, const int32_t 
 // Validate a KV-cache write and build its kernel arguments (no launch).
 int kv_write_prepare(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
                      const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
-                     const attn_paged_dims *dims, const attn_kv_new_dims *nd, pa::KvWriteArgs &w) {
+                     const attn_paged_dims *dims, const attn_kv_new_dims *nd, pa::KvWriteArgs &w,
+                     int32_t kv_dtype = ATTN_KV_BF16, float k_scale = 1.f, float v_scale = 1.f) {
     int rc = validate_dims(dims, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
     if (!nd) return ATTN_ERR_NULL;
+    if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+    if (kv_dtype == ATTN_KV_FP8_E4M3) {
+        const int64_t kvs[] = {dims->kv_stride_page, dims->kv_stride_slot, dims->kv_stride_head, dims->kv_stride_kv};
+        for (int64_t st : kvs)
+            if ((st & 15) != 0) return ATTN_ERR_STRIDE;
+        // finite, nonzero scales (the codes are x * (1 / scale))
+        if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale == 0.f || v_scale == 0.f)
+            return ATTN_ERR_SHAPE;
+    }
     const int64_t D = dims->head_dim, hkv = dims->num_kv_heads;
     const int64_t strides[] = {nd->k_stride_token, nd->k_stride_head, nd->v_stride_token, nd->v_stride_head};
     for (int64_t st : strides)
@@ -338,6 +348,9 @@ int kv_write_prepare(void *kv_pool, const void *k_new, const void *v_new, const 
     w.max_q = max_q;
     w.hkv = dims->num_kv_heads;
     w.d = dims->head_dim;
+    w.fp8 = kv_dtype == ATTN_KV_FP8_E4M3 ? 1 : 0;
+    w.k_inv = w.fp8 ? 1.f / k_scale : 1.f;
+    w.v_inv = w.fp8 ? 1.f / v_scale : 1.f;
     return ATTN_OK;
 }
 
@@ -553,6 +566,41 @@ int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void
     pa::AttnArgs a;
     rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
                        workspace, workspace_bytes, ATTN_PATH_AUTO, 0, nullptr, 0, plan, a);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    rc = kv_write_launch(w, st);
+    if (rc != ATTN_OK) return rc;
+    return paged_launch(plan, a, dims->head_dim, st);
+}
+
+int attn_paged_kv_write_opt(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,
+                            const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                            const attn_paged_dims *dims, const attn_kv_new_dims *new_dims,
+                            const attn_paged_options *opt, void *stream) {
+    if (!opt) return ATTN_ERR_NULL;
+    pa::KvWriteArgs w;
+    int rc = kv_write_prepare(kv_pool, k_new, v_new, block_table, seq_lens, cu_q, n_seqs, max_q, dims,
+                              new_dims, w, opt->kv_dtype, opt->k_scale, opt->v_scale);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    return kv_write_launch(w, static_cast<hipStream_t>(stream));
+}
+
+int attn_paged_fwd_write_opt(void *out, const void *q, const void *k_new, const void *v_new, void *kv_pool,
+                             const int32_t *block_table, const int32_t *seq_lens, const int32_t *cu_q,
+                             int32_t n_seqs, int32_t max_q, float scale, int32_t causal,
+                             const attn_paged_dims *dims, const attn_kv_new_dims *new_dims,
+                             const attn_paged_options *opt, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    if (!opt) return ATTN_ERR_NULL;
+    pa::KvWriteArgs w;
+    int rc = kv_write_prepare(kv_pool, k_new, v_new, block_table, seq_lens, cu_q, n_seqs, max_q, dims,
+                              new_dims, w, opt->kv_dtype, opt->k_scale, opt->v_scale);
+    if (rc != ATTN_OK) return rc;
+    attn_paged_plan plan;
+    pa::AttnArgs a;
+    rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
+                       workspace, workspace_bytes, opt->path_hint, opt->pages_per_split, opt->sinks, opt->window,
+                       plan, a, opt->kv_dtype, opt->k_scale, opt->v_scale);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     rc = kv_write_launch(w, st);

@@ -37,7 +37,8 @@ def test_header_declares_entry_points():
                  "attn_paged_workspace_bytes", "attn_status_string", "attn_quant_fwd",
                  "attn_quant_prep", "attn_quant_attend", "attn_quant_layout_of",
                  "attn_workspace_clear", "attn_paged_kv_write", "attn_paged_fwd_write",
-                 "attn_paged_fwd_opt", "attn_paged_make_plan_opt"):
+                 "attn_paged_fwd_opt", "attn_paged_make_plan_opt", "attn_paged_kv_write_opt",
+                 "attn_paged_fwd_write_opt"):
         assert name in fns
 
 
@@ -272,6 +273,13 @@ def test_fp8_cache_options_validate(pa):
     assert fo(f8(vs=float("nan"))) == E_SHAPE
     # a bf16 cache ignores the scales (a zeroed options struct stays valid)
     assert mp(mod.attn_paged_options(None, 0, 0, 0, 0, 0.0, 0.0)) == OK
+    # the quantising write needs finite, nonzero scales
+    nd = mod.attn_kv_new_dims(8 * 128, 128, 8 * 128, 128)
+    for bad in (f8(ks=0.0), f8(vs=float("inf"))):
+        assert lib.attn_paged_kv_write_opt(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, ctypes.byref(d),
+                                           ctypes.byref(nd), ctypes.byref(bad), None) == E_SHAPE
+    assert lib.attn_paged_kv_write_opt(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1, ctypes.byref(d),
+                                       ctypes.byref(nd), None, None) == E_NULL
 
 
 def test_workspace_clear_validates(pa):

@@ -117,3 +117,41 @@ def test_fp8_prefill_is_unsupported():
     with pytest.raises(pa.AttnError):
         pa.paged_attention(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, case8.max_q,
                            case8.scale, True, k_scale=1.0, v_scale=1.0)
+
+
+@pytest.mark.parametrize("big", [False, True])
+def test_fp8_write_bit_exact(oracle_mod, big):
+    """The quantising write gives the oracle's codes bit for bit (the product
+    x * (1/scale) in f32 on both sides; with large rows the codes saturate)."""
+    import paged_kv_gqa_fwd_amd as pa
+    base = workloads.chunked_prefill(n_seqs=2, q_lo=40, q_hi=90, ctx_hi=300, seed=828)
+    case8 = workloads.fp8_pool_case(base)
+    k_new, v_new = workloads.new_kv_tokens(base, 48, layout="fused_qkv")
+    if big:
+        k_new = k_new * 300.0
+    ks, vs = 0.37, 0.5
+    expect = oracle_mod.kv_write(case8.kv, k_new, v_new, case8.block_table, case8.seq_lens, case8.cu_q,
+                                 k_scale=ks, v_scale=vs)
+    g8 = case8.to("cuda")
+    pa.kv_write(g8.kv, k_new.cuda(), v_new.cuda(), g8.block_table, g8.seq_lens, g8.cu_q, case8.max_q, q_like=g8.q,
+                k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert torch.equal(g8.kv.cpu(), expect)
+
+
+def test_fp8_write_then_attend(oracle_mod):
+    import paged_kv_gqa_fwd_amd as pa
+    base = workloads.decode_batch(n_seqs=10, seed=829)
+    case8 = workloads.fp8_pool_case(base)
+    k_new, v_new = workloads.new_kv_tokens(base, 49)
+    ks, vs = 0.5, 0.5
+    written = oracle_mod.kv_write(case8.kv, k_new, v_new, case8.block_table, case8.seq_lens, case8.cu_q,
+                                  k_scale=ks, v_scale=vs)
+    ref = oracle_mod.paged_attn(case8.q, written, case8.block_table, case8.seq_lens, case8.cu_q, case8.scale, True,
+                                k_scale=ks, v_scale=vs)
+    g8 = case8.to("cuda")
+    out = pa.paged_attention_write(g8.q, k_new.cuda(), v_new.cuda(), g8.kv, g8.block_table, g8.seq_lens, g8.cu_q, 1,
+                                   case8.scale, True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert torch.equal(g8.kv.cpu(), written)
+    compare(out, ref, what="fp8 write + attend")
