@@ -37,7 +37,7 @@ constexpr size_t kWsAlign = 256;
 // resident workgroups (256 CUs x resident workgroups per CU), which balances
 // the per-workgroup start-up cost against the tail of ragged sequences.
 constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kSplitRounds = 8;
+constexpr int64_t kSplitRounds = 4;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

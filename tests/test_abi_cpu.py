@@ -167,13 +167,14 @@ def test_plan_paths_and_sizes(pa):
     assert p3f.max_splits == 1 and p3f.workspace_bytes == 0 and p3f.counter_bytes == 0
     p4 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 3)
     assert p4.pages_per_split == 3 and p4.max_splits == 43
-    # long decode: 128 seqs x 512 pages, 2 KV heads -> at least 16 splits' worth of workgroups
+    # long decode: 128 seqs x 512 pages, 2 KV heads -> about four rounds of workgroups
+    # (1024 resident on 256 CUs at one per CU) from the splits
     d5 = dims(num_q_heads=16, num_kv_heads=2, head_dim=256, q_stride_token=16 * 256, q_stride_head=256,
               o_stride_token=16 * 256, o_stride_head=256, kv_stride_page=64 * 2 * 2 * 256,
               kv_stride_slot=2 * 2 * 256, kv_stride_head=512, kv_stride_kv=256,
               max_pages_per_seq=512, bt_stride=512, num_tokens=128)
     p5 = mod.make_plan(d5, 128, 1)
-    assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_z * 2 * 128 >= 2048
+    assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_z * 2 * 128 >= 4 * 256
 
 
 def test_workspace_bytes_query(pa):
