@@ -139,7 +139,7 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
         "ms_per_step": step_ms,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
-                 pa.PATH_PREFILL: "prefill"}[plan.path],
+                 pa.PATH_SPLIT_BALANCED: "balanced_split_decode+combine", pa.PATH_PREFILL: "prefill"}[plan.path],
         "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
         "bytes": algorithmic_bytes(case, window), "flops": algorithmic_flops(case),
     }

@@ -84,8 +84,10 @@ typedef struct attn_paged_dims {
 /* Execution plan chosen for a call (host-side; no device access). */
 typedef struct attn_paged_plan {
     int32_t path;              /* ATTN_PATH_SPLIT_DECODE or ATTN_PATH_PREFILL */
-    int32_t pages_per_split;   /* KV pages one workgroup streams (split path) */
-    int32_t max_splits;        /* ceil(MP / pages_per_split) */
+    int32_t pages_per_split;   /* KV pages one workgroup streams (split path); balanced
+                                  path: the least pages of one range */
+    int32_t max_splits;        /* ceil(MP / pages_per_split); balanced path: the most
+                                  pieces one sequence can be cut into */
     int32_t grid_x, grid_y, grid_z;
     int32_t block_threads;
     size_t workspace_bytes;    /* bytes of workspace the call needs (0 if none) */
@@ -96,17 +98,31 @@ enum {
     ATTN_PATH_AUTO = 0,
     ATTN_PATH_SPLIT_DECODE = 1, /* split-KV partial kernel + log-sum-exp combine kernel */
     ATTN_PATH_PREFILL = 2,      /* q-tile kernel with causal tile skipping, one pass */
-    ATTN_PATH_SPLIT_FUSED = 3   /* split-KV kernel whose last split per (sequence, KV head)
+    ATTN_PATH_SPLIT_FUSED = 3,  /* split-KV kernel whose last split per (sequence, KV head)
                                    merges the partials: one launch (decode.json's single
                                    launch with an i32 counter scratch, ops.decode.impl).
                                    Same bits as ATTN_PATH_SPLIT_DECODE; AUTO picks the
                                    two-kernel form, which measured faster on MI355X. */
+    ATTN_PATH_SPLIT_BALANCED = 4 /* split-KV over an even division of the batch's pages:
+                                   the pages every sequence needs, in sequence order,
+                                   cut into grid_y equal ranges (at least pages_per_split
+                                   pages each; a range may span sequences), one
+                                   workgroup per (KV head, range), then the combine
+                                   kernel for sequences cut into several pieces.  The
+                                   same PartitionType split as ATTN_PATH_SPLIT_DECODE
+                                   with the cuts placed by length, so ragged batches
+                                   keep every workgroup equally busy.  At most
+                                   1024 sequences.  AUTO's choice for decode-shaped
+                                   calls (G * max_q <= 16, pages_per_split = 0,
+                                   n_seqs <= 1024). */
 };
 
 /*
  * attn_paged_make_plan -- choose path, split size and grid for a call with
  * these sizes.  path_hint: ATTN_PATH_AUTO or a forced path; pages_per_split:
- * 0 = automatic, otherwise forced (split path only).  Pure host logic: it
+ * 0 = automatic, otherwise forced (split paths only; with ATTN_PATH_AUTO a
+ * forced value selects ATTN_PATH_SPLIT_DECODE, and on the balanced path it
+ * is the least range size).  Pure host logic: it
  * reads no device memory and may be called without a GPU.
  * Split-KV partial outputs and (max, sum) statistics per split follow the
  * decode.json manifest's scratch buffers partial / stats (ops.decode.impl

@@ -22,6 +22,7 @@ PATH_AUTO = 0
 PATH_SPLIT_DECODE = 1   # split-KV kernel + combine kernel
 PATH_PREFILL = 2
 PATH_SPLIT_FUSED = 3    # split-KV kernel whose last split per (sequence, KV head) merges
+PATH_SPLIT_BALANCED = 4  # split-KV over equal page ranges of the whole batch + combine kernel
 KV_BF16 = 0
 KV_FP8_E4M3 = 1         # OCP e4m3 codes with per-tensor K and V scales
 

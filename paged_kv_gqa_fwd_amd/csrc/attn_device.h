@@ -17,6 +17,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPage = 64;      // keys per page (one KV tile)
 constexpr int kThreads = 256;  // 4 wave64 per workgroup
+constexpr int kBalMaxSeqs = 1024;  // sequences the balanced split path plans in one workgroup's LDS
 
 // Split-decode tuning (compile-time knobs; the defaults are the measured best
 // on MI355X): register stages = pages in flight per workgroup, and the
@@ -83,6 +84,7 @@ struct AttnArgs {
     int32_t window;             // > 0: a query at pos sees only keys >= pos - window + 1; 0: no window
     int32_t kv_fp8;             // pool holds OCP e4m3 codes (split path only); strides count bytes
     float v_scale;              // V = v_scale * e4m3(code) (1 for a bf16 pool); k_scale is in scale_log2
+    int32_t *seg_splits;        // balanced split path: [B] pieces per sequence (1 = written directly, 0 = no page)
 };
 
 struct CombineArgs {
@@ -94,6 +96,7 @@ struct CombineArgs {
     const float *sinks;
     int64_t o_st, o_sh;
     int32_t n_seqs, max_q, hq, pages_per_split, max_splits, window;
+    const int32_t *seg_splits;  // balanced split path: pieces per sequence (else null)
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

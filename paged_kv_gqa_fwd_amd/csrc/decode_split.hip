@@ -98,6 +98,152 @@ __device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8
     }
 }
 
+// Per-page work of one wave: keys 16w .. 16w+15 of page p (already in LDS)
+// against the rows whose Q^T fragments are in qreg (lane row = lane % 16,
+// visible keys [lo, vis)); updates the wave's online-softmax state.
+template <int D, bool F8>
+__device__ __forceinline__ void decode_compute_page(const uint16_t *ks, const uint16_t *vs,
+                                                    const bf16x8 (&qreg)[D / 32], f32x4 (&oacc)[D / 16],
+                                                    float &m_run, float &l_part, int p, int vis, int lo,
+                                                    float scale_log2, int w, int lane) {
+    using C = DecodeCfg<D, F8>;
+    // S^T[16 keys x 16 rows] = K Q^T.
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+        const uint16_t *kp = ks + (16 * w + (lane & 15)) * C::KROW + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 32 * kk);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], sacc, 0, 0, 0);
+        }
+    }
+    // sacc[i] = score of key p*64 + 16w + 4*(lane/16) + i for this lane's row.
+    const int key0 = p * kPage + 16 * w + 4 * (lane >> 4);
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sv[i] = (key0 + i < vis && key0 + i >= lo) ? sacc[i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    m_run = m_new;
+    bf16x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const __bf16 pr = (__bf16)exp2_fast(sv[i] - m_use);
+        pb[i] = pr;
+        psum += (float)pr;   // the sum uses the same rounded P as the P.V product
+    }
+    l_part = l_part * alpha + psum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+    }
+    // O^T[d, row] += V^T[d, key] P^T[key, row] over this wave's 16 keys.
+    const i16x4 pop = __builtin_bit_cast(i16x4, pb);
+    const uint16_t *vp = vs + (16 * w + 4 * (lane >> 4) + ((lane & 15) >> 2)) * C::VROW + 4 * (lane & 3);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * db));
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
+    }
+}
+
+// Merge the four waves' (m, l, O) of one (sequence, KV head) piece in LDS,
+// then write each of its rows: the unnormalised partial and (max, sum) in
+// split slot split_idx (device-coherent stores when another workgroup of the
+// launch reads them), or, when the piece is the whole sequence, the
+// normalised bf16 output with the row's sink in the normaliser.  Starts with
+// a barrier (all waves done with the K/V tiles); reuses the K/V LDS area.
+template <int D, bool F8>
+__device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *smem, float (&red_m)[4][16],
+                                                   float (&red_l)[4][16], const f32x4 (&oacc)[D / 16],
+                                                   float m_run, float l_part, int b, int g, int q0, int rows,
+                                                   bool split, int split_idx, bool coherent, int tid) {
+    using C = DecodeCfg<D, F8>;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int row = lane & 15;
+    const int G = a.group;
+    float l_row = l_part + shfl_xor_f32(l_part, 16);
+    l_row += shfl_xor_f32(l_row, 32);
+    if (lane < 16) {
+        red_m[w][lane] = m_run;
+        red_l[w][lane] = l_row;
+    }
+    __syncthreads();   // also: all waves are done with the K/V tiles
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][row]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float wgt = exp2_fast(m_run - M_use);
+    float *ored = reinterpret_cast<float *>(smem);   // [4 waves][16 rows][D] f32
+    static_assert(4 * 16 * D * 4 <= C::LDS_ELEMS * 2, "LDS too small for the merge");
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d = 16 * db + 4 * (lane >> 4) + i;
+            ored[(w * 16 + row) * D + d] = oacc[db][i] * wgt;
+        }
+    }
+    __syncthreads();
+
+    // Thread -> (rows r = tid / D + k * (256 / D), column d = tid % D).
+    constexpr int RSTEP = kThreads / D;   // 1 (D=256) or 2 (D=128)
+    const int d = tid % D;
+    for (int r = tid / D; r < rows; r += RSTEP) {
+        float Mr = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) Mr = fmaxf(Mr, red_m[ww][r]);
+        const float Mr_use = (Mr == -INFINITY) ? 0.f : Mr;
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            lsum += red_l[ww][r] * exp2_fast(red_m[ww][r] - Mr_use);
+            osum += ored[(ww * 16 + r) * D + d];
+        }
+        if constexpr (F8) osum *= a.v_scale;   // V = v_scale * e4m3(code)
+        const int ri = r / G;
+        const int rh = g * G + (r - ri * G);
+        const int64_t t = q0 + ri;
+        if (split) {
+            // partial rows are indexed by (sequence, query index), not token,
+            // so the workspace scales with n_seqs * max_q
+            const int64_t prow = (int64_t)b * a.max_q + ri;
+            const int64_t slot = (prow * a.hq + rh) * a.max_splits + split_idx;
+            if (coherent) {
+                // read by another workgroup of this launch: device-coherent
+                store_coherent(a.part_o + slot * D + d, osum);
+                if (d == 0) {
+                    store_coherent(a.part_ml + slot * 2 + 0, Mr);
+                    store_coherent(a.part_ml + slot * 2 + 1, lsum);
+                }
+            } else {
+                a.part_o[slot * D + d] = osum;
+                if (d == 0) {
+                    a.part_ml[slot * 2 + 0] = Mr;
+                    a.part_ml[slot * 2 + 1] = lsum;
+                }
+            }
+        } else {
+            if (a.sinks) {
+                // the row's sink logit joins the normaliser (no value row)
+                const float sink2 = a.sinks[rh] * kLog2e;
+                if (sink2 != -INFINITY) lsum += exp2_fast(sink2 - Mr_use);
+            }
+            const float o = lsum > 0.f ? osum / lsum : 0.f;
+            a.out[t * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(o);
+        }
+    }
+}
+
 template <int D, bool F8>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
@@ -167,54 +313,8 @@ void paged_decode_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
     float l_part = 0.f;        // this lane's share of the running sum
 
-    // Per-page work of one wave: keys 16w .. 16w+15 of page p (already in LDS).
     auto compute_page = [&](int p) {
-        // S^T[16 keys x 16 rows] = K Q^T.
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-        {
-            const uint16_t *kp = ks + (16 * w + (lane & 15)) * C::KROW + 8 * (lane >> 4);
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 32 * kk);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], sacc, 0, 0, 0);
-            }
-        }
-        // sacc[i] = score of key p*64 + 16w + 4*(lane/16) + i for this lane's row.
-        const int key0 = p * kPage + 16 * w + 4 * (lane >> 4);
-        float sv[4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sv[i] = (key0 + i < vis && key0 + i >= lo) ? sacc[i] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[i]);
-        }
-        mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
-        bf16x4 pb;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const __bf16 pr = (__bf16)exp2_fast(sv[i] - m_use);
-            pb[i] = pr;
-            psum += (float)pr;   // the sum uses the same rounded P as the P.V product
-        }
-        l_part = l_part * alpha + psum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
-        }
-        // O^T[d, row] += V^T[d, key] P^T[key, row] over this wave's 16 keys.
-        const i16x4 pop = __builtin_bit_cast(i16x4, pb);
-        const uint16_t *vp = vs + (16 * w + 4 * (lane >> 4) + ((lane & 15) >> 2)) * C::VROW + 4 * (lane & 3);
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-            const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * db));
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
-        }
+        decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, w, lane);
     };
 
     const int64_t sp = a.kv_sp;
@@ -294,79 +394,12 @@ void paged_decode_split_kernel(const AttnArgs a) {
         }
     }
 
-    // ---- merge the four waves' (m, l, O) in LDS --------------------------
-    float l_row = l_part + shfl_xor_f32(l_part, 16);
-    l_row += shfl_xor_f32(l_row, 32);
-    if (lane < 16) {
-        red_m[w][lane] = m_run;
-        red_l[w][lane] = l_row;
-    }
-    __syncthreads();   // also: all waves are done with the K/V tiles
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][row]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    const float wgt = exp2_fast(m_run - M_use);
-    float *ored = reinterpret_cast<float *>(smem);   // [4 waves][16 rows][D] f32
-    static_assert(4 * 16 * D * 4 <= C::LDS_ELEMS * 2, "LDS too small for the merge");
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 16 * db + 4 * (lane >> 4) + i;
-            ored[(w * 16 + row) * D + d] = oacc[db][i] * wgt;
-        }
-    }
-    __syncthreads();
-
+    // ---- merge the four waves' (m, l, O) in LDS, write ------------------
     const bool split = a.max_splits > 1;
-    // Thread -> (rows r = tid / D + k * (256 / D), column d = tid % D).
-    constexpr int RSTEP = kThreads / D;   // 1 (D=256) or 2 (D=128)
+    decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, split, s, a.fuse_merge != 0,
+                              tid);
+    constexpr int RSTEP = kThreads / D;
     const int d = tid % D;
-    for (int r = tid / D; r < rows; r += RSTEP) {
-        float Mr = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) Mr = fmaxf(Mr, red_m[ww][r]);
-        const float Mr_use = (Mr == -INFINITY) ? 0.f : Mr;
-        float lsum = 0.f, osum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            lsum += red_l[ww][r] * exp2_fast(red_m[ww][r] - Mr_use);
-            osum += ored[(ww * 16 + r) * D + d];
-        }
-        if constexpr (F8) osum *= a.v_scale;   // V = v_scale * e4m3(code)
-        const int ri = r / G;
-        const int rh = g * G + (r - ri * G);
-        const int64_t t = q0 + ri;
-        if (split) {
-            // partial rows are indexed by (sequence, query index), not token,
-            // so the workspace scales with n_seqs * max_q
-            const int64_t prow = (int64_t)b * a.max_q + ri;
-            const int64_t slot = (prow * a.hq + rh) * a.max_splits + s;
-            if (a.fuse_merge) {
-                // read by another workgroup of this launch: device-coherent
-                store_coherent(a.part_o + slot * D + d, osum);
-                if (d == 0) {
-                    store_coherent(a.part_ml + slot * 2 + 0, Mr);
-                    store_coherent(a.part_ml + slot * 2 + 1, lsum);
-                }
-            } else {
-                a.part_o[slot * D + d] = osum;
-                if (d == 0) {
-                    a.part_ml[slot * 2 + 0] = Mr;
-                    a.part_ml[slot * 2 + 1] = lsum;
-                }
-            }
-        } else {
-            if (a.sinks) {
-                // the row's sink logit joins the normaliser (no value row)
-                const float sink2 = a.sinks[rh] * kLog2e;
-                if (sink2 != -INFINITY) lsum += exp2_fast(sink2 - Mr_use);
-            }
-            const float o = lsum > 0.f ? osum / lsum : 0.f;
-            a.out[t * a.o_st + (int64_t)rh * a.o_sh + d] = f32_to_bf16_bits(o);
-        }
-    }
     if (!split || !a.fuse_merge) return;
 
     // ---- in-kernel merge ---------------------------------------------------
@@ -418,6 +451,241 @@ void paged_decode_split_kernel(const AttnArgs a) {
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- balanced split decode --------------------------------------------------
+// The pages the batch needs (each sequence's pages from the first one inside
+// row 0's window, sequences in order) are dealt out as gridDim.y equal
+// contiguous ranges of C = max(ceil(total / gridDim.y), pages_per_split)
+// pages; workgroup (g, r) streams range r for KV head g, so every workgroup
+// of the launch reads the same number of pages whatever the mix of lengths.
+// A range may end inside one sequence and go on into the next: each
+// (sequence, range) piece keeps its own online-softmax state.  A sequence
+// held by one range is written out directly; otherwise its pieces go to
+// split slots r - floor(F_b / C) (F_b = pages of the sequences before it)
+// and the combine kernel merges them.  pages_per_split (the plan's minimum
+// C) bounds a sequence's pieces by max_splits.
+//
+// Every workgroup derives the partition itself from seq_lens and cu_q (an
+// LDS prefix sum over at most kBalMaxSeqs sequences), so nothing but the
+// launch orders the two kernels.  Workgroup (0, 0) publishes each
+// sequence's piece count for the combine kernel.
+//
+// The page ring runs across sequence boundaries: the next pages are loaded
+// while the current piece is merged and written, and the Q rows of a new
+// piece travel in the ring with its first page (staged through LDS), so no
+// wait for them drains the loads in flight.
+template <int D, bool F8>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
+void paged_decode_balanced_kernel(const AttnArgs a) {
+    using C = DecodeCfg<D, F8>;
+    constexpr int QROW = D + 8;                       // bf16 per LDS Q row (16 B pad)
+    constexpr int QCPR = D / 8;                       // 16-byte Q chunks per row
+    constexpr int QCH = 16 * QCPR / kThreads;         // Q chunks per thread (16 rows): D / 128
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[16 * QROW];
+    __shared__ float red_m[4][16];
+    __shared__ float red_l[4][16];
+    __shared__ int s_F[kBalMaxSeqs + 1];   // s_F[b] = pages of the sequences before b
+    __shared__ int s_L[kBalMaxSeqs];
+    __shared__ int s_q0[kBalMaxSeqs];
+    __shared__ int s_n[kBalMaxSeqs];
+    __shared__ int s_wsum[4];
+    __shared__ int s_first;
+    uint16_t *ks = smem;
+    uint16_t *vs = smem + kPage * C::KROW;
+
+    const int g = blockIdx.x;
+    const int r = blockIdx.y;
+    const int R = gridDim.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int B = a.n_seqs;       // <= kBalMaxSeqs (the plan checks)
+    const int G = a.group;
+
+    // ---- the partition: pages per sequence and their prefix sum ----------
+    int np4[4];
+    int tsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int bb = 4 * tid + j;
+        int np = 0;
+        if (bb < B) {
+            const int L = a.seq_lens[bb];
+            const int q0 = a.cu_q[bb];
+            int n = a.cu_q[bb + 1] - q0;
+            if (n > a.max_q) n = a.max_q;   // caller contract: n_b <= max_q
+            s_L[bb] = L;
+            s_q0[bb] = q0;
+            s_n[bb] = n;
+            if (n > 0 && L > 0) np = (L + kPage - 1) / kPage - split_first_page(L, n, a.window);
+        }
+        np4[j] = np;
+        tsum += np;
+    }
+    int incl = tsum;   // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_wsum[w] = incl;
+    __syncthreads();
+    int run = incl - tsum;
+    for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
+    if (tid == 0) s_F[0] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        run += np4[j];
+        s_F[4 * tid + j + 1] = run;   // entries past B repeat the total
+    }
+    __syncthreads();
+    const int total = s_F[B];
+    int Cr = (total + R - 1) / R;
+    if (Cr < a.pages_per_split) Cr = a.pages_per_split;
+    if (g == 0 && r == 0) {
+        for (int bb = tid; bb < B; bb += kThreads) {
+            const int F0 = s_F[bb], np = s_F[bb + 1] - F0;
+            a.seg_splits[bb] = np > 0 ? (F0 + np - 1) / Cr - F0 / Cr + 1 : 0;
+        }
+    }
+    if ((int64_t)r * Cr >= total) return;   // uniform: nothing left for this range
+    const int u0 = r * Cr;
+    const int nunits = min(total - u0, Cr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int bb = 4 * tid + j;
+        if (bb < B && s_F[bb] <= u0 && u0 < s_F[bb + 1]) s_first = bb;   // exactly one such sequence
+    }
+    __syncthreads();
+
+    const char *head_base = reinterpret_cast<const char *>(a.kv) + (int64_t)g * a.kv_sh * C::EB;
+    const int64_t sp = a.kv_sp;
+
+    // Loader cursor (uniform): sequence lb, page lp, its first and end pages.
+    int lb = __builtin_amdgcn_readfirstlane(s_first);
+    int lend = __builtin_amdgcn_readfirstlane((s_L[lb] + kPage - 1) / kPage);
+    int lplo = __builtin_amdgcn_readfirstlane(lend - (s_F[lb + 1] - s_F[lb]));
+    int lp = __builtin_amdgcn_readfirstlane(lplo + (u0 - s_F[lb]));
+    auto advance = [&]() {
+        ++lp;
+        if (lp == lend) {
+            do {
+                ++lb;
+            } while (lb < B && s_F[lb + 1] == s_F[lb]);
+            lb = __builtin_amdgcn_readfirstlane(lb);
+            if (lb < B) {
+                lend = __builtin_amdgcn_readfirstlane((s_L[lb] + kPage - 1) / kPage);
+                lplo = __builtin_amdgcn_readfirstlane(lend - (s_F[lb + 1] - s_F[lb]));
+                lp = lplo;
+            }
+        }
+    };
+    auto page_id = [&]() { return a.block_table[(int64_t)lb * a.bt_stride + lp]; };
+
+    // The ring: slot k holds a page's K/V chunks, and for the first page of a
+    // piece also the piece's Q rows.
+    u32x4 st[C::STAGES][C::CH_PER_THREAD];
+    u32x4 qst[C::STAGES][QCH];
+    int sb[C::STAGES], spg[C::STAGES];
+    bool snew[C::STAGES];
+    auto load_slot = [&](int k, int pid, bool first) {
+        load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid, s_L[lb] - lp * kPage);
+        const bool nw = first || lp == lplo;
+        if (nw) {
+            const int n = s_n[lb];
+            const int q0 = s_q0[lb];
+            const int rows = min(n * G, 16);
+#pragma unroll
+            for (int j = 0; j < QCH; ++j) {
+                const int c = j * kThreads + tid;
+                const int qrow = c / QCPR;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (qrow < rows) {
+                    const int qi = qrow / G;
+                    const int h = g * G + (qrow - qi * G);
+                    v = *reinterpret_cast<const u32x4 *>(a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh +
+                                                         8 * (c % QCPR));
+                }
+                qst[k][j] = v;
+            }
+        }
+        sb[k] = lb;
+        spg[k] = lp;
+        snew[k] = nw;
+    };
+
+    // Per-piece state.
+    int cb = -1, cq0 = 0, crows = 0, vis = 0, lo = 0;
+    bf16x8 qreg[D / 32];
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_part = 0.f;
+    const int row = lane & 15;
+    auto finish_piece = [&]() {
+        const int F0 = s_F[cb];
+        const int np = s_F[cb + 1] - F0;
+        const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
+        decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, cb, g, cq0, crows, ns > 1,
+                                  r - F0 / Cr, false, tid);
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_part = 0.f;
+    };
+
+#pragma unroll
+    for (int k = 0; k < C::STAGES; ++k) {
+        if (k < nunits) {
+            load_slot(k, page_id(), k == 0);
+            advance();
+        }
+    }
+    for (int i0 = 0; i0 < nunits; i0 += C::STAGES) {
+#pragma unroll
+        for (int k = 0; k < C::STAGES; ++k) {
+            const int i = i0 + k;
+            if (i >= nunits) break;                      // uniform across the workgroup
+            const bool more = i + C::STAGES < nunits;
+            const int pid = more ? page_id() : 0;
+            if (snew[k] && cb >= 0) finish_piece();      // merge + write the previous piece
+            __syncthreads();                             // the previous page (or the merge) is done with LDS
+            store_page<D, F8>(st[k], ks, vs, tid);
+            if (snew[k]) {
+#pragma unroll
+                for (int j = 0; j < QCH; ++j) {
+                    const int c = j * kThreads + tid;
+                    *reinterpret_cast<u32x4 *>(qs + (c / QCPR) * QROW + 8 * (c % QCPR)) = qst[k][j];
+                }
+            }
+            __syncthreads();
+            const int cp = spg[k];
+            if (snew[k]) {
+                cb = sb[k];
+                const int L = s_L[cb];
+                const int n = s_n[cb];
+                cq0 = s_q0[cb];
+                crows = min(n * G, 16);
+                const bool row_ok = row < crows;
+                const int qi = row / G;
+                vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
+                lo = row_ok ? window_start(L - n + qi, a.window) : 0;
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk)
+                    qreg[kk] = *reinterpret_cast<const bf16x8 *>(qs + row * QROW + 32 * kk + 8 * (lane >> 4));
+            }
+            if (more) {
+                load_slot(k, pid, false);
+                advance();
+            }
+            decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, cp, vis, lo, a.scale_log2, w, lane);
+        }
+    }
+    finish_piece();
+}
+
 // Log-sum-exp merge of the split partials: per (token, q head) row,
 // M = max(max_s m_s, sink), w_s = 2^(m_s - M),
 // out = sum_s w_s O_s / (sum_s w_s l_s + 2^(sink - M)); no sink = -inf.
@@ -433,9 +701,17 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     int n = a.cu_q[b + 1] - q0;
     if (n > a.max_q) n = a.max_q;
     if (i >= n) return;
-    const int L = a.seq_lens[b];
-    const int npages = (L + kPage - 1) / kPage;
-    const int ns = split_count(npages, split_first_page(L, n, a.window), a.pages_per_split, a.max_splits);
+    int ns;
+    if (a.seg_splits) {
+        // balanced split path: a sequence in one piece was written directly;
+        // one with no page (L = 0) is written as zeros below
+        ns = a.seg_splits[b];
+        if (ns == 1) return;
+    } else {
+        const int L = a.seq_lens[b];
+        ns = split_count((L + kPage - 1) / kPage, split_first_page(L, n, a.window), a.pages_per_split,
+                         a.max_splits);
+    }
     const int64_t t = q0 + i;
     const int64_t base = (((int64_t)b * a.max_q + i) * a.hq + h) * a.max_splits;
 
@@ -479,6 +755,15 @@ hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream)
 }
 
 template <int D>
+hipError_t launch_decode_balanced(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    if (a.kv_fp8)
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
     dim3 grid((a.hq + 3) / 4, a.max_q, a.n_seqs);
     hipLaunchKernelGGL(paged_combine_kernel<D>, grid, dim3(kThreads), 0, stream, a);
@@ -500,6 +785,10 @@ hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream)
 
 hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream) {
     return D == 128 ? launch_decode_split<128>(a, grid, stream) : launch_decode_split<256>(a, grid, stream);
+}
+
+hipError_t launch_decode_balanced_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    return D == 128 ? launch_decode_balanced<128>(a, grid, stream) : launch_decode_balanced<256>(a, grid, stream);
 }
 
 hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream) {

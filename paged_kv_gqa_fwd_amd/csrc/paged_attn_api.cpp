@@ -19,6 +19,7 @@
 
 namespace pa {
 hipError_t launch_decode_split_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
+hipError_t launch_decode_balanced_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
 hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream);
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
@@ -38,6 +39,11 @@ constexpr size_t kWsAlign = 256;
 // the per-workgroup start-up cost against the tail of ragged sequences.
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kSplitRounds = 4;
+// Balanced split path: one round of resident workgroups (every workgroup
+// streams the same number of pages, so there is no tail to fill), and a
+// bound on the partial workspace that sets the least range size.
+constexpr int64_t kBalRounds = 1;
+constexpr size_t kBalPartialBudget = size_t(64) << 20;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -73,6 +79,16 @@ int32_t effective_window(const attn_paged_dims *d, int32_t window) {
     return (int64_t)window >= (int64_t)d->max_pages_per_seq * pa::kPage ? 0 : window;
 }
 
+// The balanced split path plans a batch in one workgroup's LDS (at most
+// kBalMaxSeqs sequences) and counts its pages in int32.
+bool balanced_fits(const attn_paged_dims *d, int32_t n_seqs, int64_t mq, int32_t window) {
+    int64_t MP = d->max_pages_per_seq;
+    if (window > 0) MP = std::min<int64_t>(MP, (window + mq + 62) / pa::kPage + 1);
+    return n_seqs >= 0 && n_seqs <= pa::kBalMaxSeqs && (int64_t)n_seqs * MP <= INT32_MAX;
+}
+
+size_t bal_lead_bytes(int32_t n_seqs) { return align_up((size_t)std::max<int32_t>(n_seqs, 1) * 4, kWsAlign); }
+
 int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
               int32_t pps, int32_t window, attn_paged_plan *plan, int32_t kv_dtype = ATTN_KV_BF16) {
     int rc = validate_dims(d, n_seqs, max_q);
@@ -85,7 +101,7 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
             if ((st & 15) != 0) return ATTN_ERR_STRIDE;
     }
     if (!plan) return ATTN_ERR_NULL;
-    if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_SPLIT_FUSED) return ATTN_ERR_SHAPE;
+    if (path_hint < ATTN_PATH_AUTO || path_hint > ATTN_PATH_SPLIT_BALANCED) return ATTN_ERR_SHAPE;
     if (pps < 0 || window < 0) return ATTN_ERR_SHAPE;
     window = effective_window(d, window);
     const int G = d->num_q_heads / d->num_kv_heads;
@@ -95,9 +111,16 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         // The two-kernel split form measured faster than the single-launch
         // merge on MI355X (the merge form makes every workgroup wait for its
         // write-through partial stores and the ticket atomic before it ends).
-        path = (mq * G <= kMaxDecodeRows) ? ATTN_PATH_SPLIT_DECODE : ATTN_PATH_PREFILL;
-    const bool split_path = path == ATTN_PATH_SPLIT_DECODE || path == ATTN_PATH_SPLIT_FUSED;
+        // Among split forms, the balanced one (cuts placed by length) keeps a
+        // ragged batch's workgroups equally busy; a forced split size asks
+        // for the fixed-size form.
+        path = (mq * G > kMaxDecodeRows) ? ATTN_PATH_PREFILL
+               : (pps == 0 && balanced_fits(d, n_seqs, mq, window)) ? ATTN_PATH_SPLIT_BALANCED
+                                                                    : ATTN_PATH_SPLIT_DECODE;
+    const bool balanced = path == ATTN_PATH_SPLIT_BALANCED;
+    const bool split_path = path == ATTN_PATH_SPLIT_DECODE || path == ATTN_PATH_SPLIT_FUSED || balanced;
     if (split_path && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
+    if (balanced && !balanced_fits(d, n_seqs, mq, window)) return ATTN_ERR_UNSUPPORTED;
     if (!split_path && kv_dtype != ATTN_KV_BF16) return ATTN_ERR_UNSUPPORTED;   // prefill reads bf16 only
     *plan = attn_paged_plan{};
     plan->path = path;
@@ -106,7 +129,30 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     // with a window those from row 0's window start to the last key.
     int64_t MP = d->max_pages_per_seq;
     if (split_path && window > 0) MP = std::min<int64_t>(MP, (window + mq + 62) / pa::kPage + 1);
-    if (split_path) {
+    if (balanced) {
+        // Ranges: one per (resident workgroup slot / KV head).  The least
+        // range size C_min bounds the pieces of one sequence by
+        // floor((MP - 1) / C_min) + 2, which sizes the partial workspace.
+        const int64_t waves = kv_dtype == ATTN_KV_FP8_E4M3 ? pa::decode_waves_per_simd_f8(d->head_dim)
+                                                           : pa::decode_waves_per_simd(d->head_dim);
+        const int64_t slots = kBalRounds * kComputeUnits * waves;
+        const int64_t R = std::min<int64_t>(std::max<int64_t>((slots + d->num_kv_heads - 1) / d->num_kv_heads, 1),
+                                            kGridYZMax);
+        const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads;
+        const size_t per_split = rows * ((size_t)d->head_dim + 2) * 4;
+        const int64_t s_cap = std::max<int64_t>(1, std::min<int64_t>((int64_t)(kBalPartialBudget / per_split), R));
+        int64_t c_min = (MP + s_cap - 1) / s_cap;
+        c_min = std::max<int64_t>(c_min, pps);
+        const int64_t S = (MP - 1) / c_min + 2;
+        plan->pages_per_split = (int32_t)c_min;
+        plan->max_splits = (int32_t)S;
+        plan->grid_x = d->num_kv_heads;
+        plan->grid_y = (int32_t)R;
+        plan->grid_z = 1;
+        // [pieces per sequence (i32) | partial O | partial (m, l)]
+        plan->workspace_bytes = bal_lead_bytes(n_seqs) + align_up(rows * (size_t)S * (size_t)d->head_dim * 4, kWsAlign) +
+                                align_up(rows * (size_t)S * 8, kWsAlign);
+    } else if (split_path) {
         int64_t p = pps;
         if (p == 0) {
             // one workgroup per SIMD-wave slot: 4 waves = one per SIMD
@@ -231,12 +277,19 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     a.sinks = sinks;
     a.window = effective_window(dims, window);
     if (plan.workspace_bytes > 0) {
-        // [merge counters | partial O | partial (m, l)], each 256-byte aligned
+        // [merge counters or pieces per sequence | partial O | partial (m, l)],
+        // each 256-byte aligned
         const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
         char *ws = static_cast<char *>(workspace);
-        a.counters = reinterpret_cast<int32_t *>(ws);
-        a.part_o = reinterpret_cast<float *>(ws + plan.counter_bytes);
-        a.part_ml = reinterpret_cast<float *>(ws + plan.counter_bytes + align_up(rows * (size_t)D * 4, kWsAlign));
+        size_t lead = plan.counter_bytes;
+        if (plan.path == ATTN_PATH_SPLIT_BALANCED) {
+            a.seg_splits = reinterpret_cast<int32_t *>(ws);
+            lead = bal_lead_bytes(n_seqs);
+        } else {
+            a.counters = reinterpret_cast<int32_t *>(ws);
+        }
+        a.part_o = reinterpret_cast<float *>(ws + lead);
+        a.part_ml = reinterpret_cast<float *>(ws + lead + align_up(rows * (size_t)D * 4, kWsAlign));
         a.fuse_merge = plan.path == ATTN_PATH_SPLIT_FUSED ? 1 : 0;
     }
     return ATTN_OK;
@@ -248,11 +301,13 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
     const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
     if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
-    hipError_t e = plan.path == ATTN_PATH_PREFILL ? pa::launch_prefill_any(D, a, grid, st)
-                                                 : pa::launch_decode_split_any(D, a, grid, st);
+    hipError_t e = plan.path == ATTN_PATH_PREFILL            ? pa::launch_prefill_any(D, a, grid, st)
+                   : plan.path == ATTN_PATH_SPLIT_BALANCED ? pa::launch_decode_balanced_any(D, a, grid, st)
+                                                           : pa::launch_decode_split_any(D, a, grid, st);
     if (e != hipSuccess) return ATTN_ERR_HIP;
     if (timing && record_event(&t_main.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
-    const bool need_combine = plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1;
+    const bool need_combine = (plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1) ||
+                              plan.path == ATTN_PATH_SPLIT_BALANCED;
     if (need_combine) {
         pa::CombineArgs c{};
         c.out = a.out;
@@ -269,6 +324,7 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
         c.max_splits = plan.max_splits;
         c.sinks = a.sinks;
         c.window = a.window;
+        c.seg_splits = a.seg_splits;
         if (timing && record_event(&t_comb.start, st) != ATTN_OK) return ATTN_ERR_HIP;
         e = pa::launch_combine_any(D, c, st);
         if (e != hipSuccess) return ATTN_ERR_HIP;

@@ -136,7 +136,7 @@ def test_plan_paths_and_sizes(pa):
     import paged_kv_gqa_fwd_amd as mod
     # decode batch: 64 seqs, G=4, MP=128 -> split decode
     d = dims(max_pages_per_seq=128, bt_stride=128)
-    assert mod.make_plan(d, 64, 1).path == mod.PATH_SPLIT_DECODE
+    assert mod.make_plan(d, 64, 1).path == mod.PATH_SPLIT_BALANCED
     p = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_FUSED)
     assert p.path == mod.PATH_SPLIT_FUSED
     assert p.grid_z == p.max_splits and p.grid_x == 8 and p.grid_y == 64
@@ -173,8 +173,50 @@ def test_plan_paths_and_sizes(pa):
               o_stride_token=16 * 256, o_stride_head=256, kv_stride_page=64 * 2 * 2 * 256,
               kv_stride_slot=2 * 2 * 256, kv_stride_head=512, kv_stride_kv=256,
               max_pages_per_seq=512, bt_stride=512, num_tokens=128)
-    p5 = mod.make_plan(d5, 128, 1)
+    p5 = mod.make_plan(d5, 128, 1, mod.PATH_SPLIT_DECODE)
     assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_z * 2 * 128 >= 4 * 256
+
+
+def test_plan_balanced(pa):
+    import paged_kv_gqa_fwd_amd as mod
+    d = dims(max_pages_per_seq=128, bt_stride=128)        # 32/8 heads, D 128
+    p = mod.make_plan(d, 64, 1)
+    # one round of resident workgroups: 256 CUs x 2 per CU over 8 KV heads
+    assert p.path == mod.PATH_SPLIT_BALANCED and (p.grid_x, p.grid_y, p.grid_z) == (8, 64, 1)
+    assert p.counter_bytes == 0
+    # pieces per sequence bounded by floor((MP - 1) / C_min) + 2
+    assert p.max_splits == 127 // p.pages_per_split + 2
+    rows = 64 * 32 * p.max_splits
+    assert p.workspace_bytes == 256 + rows * 128 * 4 + rows * 8
+    # the least range size caps the partials at 64 MiB plus one split's worth
+    assert p.max_splits * 64 * 32 * 130 * 4 <= (64 << 20) + 64 * 32 * 130 * 4
+    # a forced least range size
+    p7 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_BALANCED, 7)
+    assert p7.pages_per_split == 7 and p7.max_splits == 127 // 7 + 2
+    # AUTO with a forced split size keeps the fixed-size split path
+    assert mod.make_plan(d, 64, 1, mod.PATH_AUTO, 16).path == mod.PATH_SPLIT_DECODE
+    # more than 1024 sequences: the fixed-size split path; forcing balanced is unsupported
+    d_big = dims(max_pages_per_seq=128, bt_stride=128, num_tokens=2048)
+    assert mod.make_plan(d_big, 1025, 1).path == mod.PATH_SPLIT_DECODE
+    assert mod.make_plan(d_big, 1024, 1).path == mod.PATH_SPLIT_BALANCED
+    lib = pa.load_library()
+    plan = mod.attn_paged_plan()
+    assert lib.attn_paged_make_plan(ctypes.byref(d_big), 1025, 1, mod.PATH_SPLIT_BALANCED, 0,
+                                    ctypes.byref(plan)) == E_UNSUP
+    # long decode, 2 KV heads at D 256 (one workgroup per CU): 128 ranges
+    d5 = dims(num_q_heads=16, num_kv_heads=2, head_dim=256, q_stride_token=16 * 256, q_stride_head=256,
+              o_stride_token=16 * 256, o_stride_head=256, kv_stride_page=64 * 2 * 2 * 256,
+              kv_stride_slot=2 * 2 * 256, kv_stride_head=512, kv_stride_kv=256,
+              max_pages_per_seq=512, bt_stride=512, num_tokens=128)
+    p5 = mod.make_plan(d5, 128, 1)
+    assert p5.path == mod.PATH_SPLIT_BALANCED and (p5.grid_x, p5.grid_y) == (2, 128)
+    assert p5.max_splits == 511 // p5.pages_per_split + 2
+    # with a window only the pages from row 0's window start count
+    pw = mod.make_plan(d5, 128, 1, window=4096)
+    mp_w = (4096 + 1 + 62) // 64 + 1      # 65 pages from row 0's window start
+    assert pw.max_splits == (mp_w - 1) // pw.pages_per_split + 2
+    # more query rows than one MFMA tile -> prefill
+    assert mod.make_plan(d, 64, 5).path == mod.PATH_PREFILL
 
 
 def test_workspace_bytes_query(pa):
@@ -265,7 +307,7 @@ def test_fp8_cache_options_validate(pa):
     f8 = lambda **kw: mod.attn_paged_options(kw.get("sinks"), kw.get("window", 0), kw.get("path", 0),
                                              kw.get("pps", 0), kw.get("dtype", 1), kw.get("ks", 1.0),
                                              kw.get("vs", 1.0))
-    assert mp(f8()) == OK and plan.path == mod.PATH_SPLIT_DECODE
+    assert mp(f8()) == OK and plan.path == mod.PATH_SPLIT_BALANCED
     assert mp(f8(dtype=2)) == E_UNSUP
     assert mp(f8(path=2)) == E_UNSUP                        # the prefill kernel reads bf16 only
     assert mp(f8(), max_q=5) == E_UNSUP                     # 20 packed rows: prefill would be needed
