@@ -111,6 +111,17 @@ def _kernel_times(fn, steps):
     return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
 
 
+# Nominal ms per step of each workload on MI355X: bounds the secondary lines'
+# step counts so that each times about a third of a second.
+NOMINAL_MS = {"decode_batch": 0.25, "long_decode": 1.5, "chunked_prefill": 4.0, "dit_self_attn": 40.0,
+              "dit_quant": 25.0, "tiny_mixed": 0.05}
+
+
+def sec_counts(name, steps, warmup):
+    per = NOMINAL_MS.get(name.split("+")[0], 1.0)
+    return max(3, min(steps // 2, int(300.0 / per))), max(1, min(warmup // 2, int(100.0 / per)))
+
+
 def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
     import paged_kv_gqa_fwd_amd as pa
     log("[bench] generating %s%s%s" % (name, " (window %d)" % window if window else "", " (fp8 cache)" if fp8 else ""))
@@ -337,8 +348,8 @@ def calibrate_gemm(n=16384, iters=20):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant,"
                                            "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096,"
@@ -382,7 +393,7 @@ def main():
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
         if name.endswith("+fp8"):
-            r = run_workload(name[:-len("+fp8")], max(3, args.steps // 2), max(1, args.warmup // 2), fp8=True)
+            r = run_workload(name[:-len("+fp8")], *sec_counts(name, args.steps, args.warmup), fp8=True)
             ss = summarize(r)
             log("[bench] %s" % json.dumps(ss))
             secondary.append(ss)
@@ -391,7 +402,7 @@ def main():
             continue
         if "+window" in name:
             base, w = name.split("+window")
-            r = run_workload(base, max(3, args.steps // 2), max(1, args.warmup // 2), window=int(w))
+            r = run_workload(base, *sec_counts(name, args.steps, args.warmup), window=int(w))
             ss = summarize(r)
             log("[bench] %s" % json.dumps(ss))
             secondary.append(ss)
@@ -399,19 +410,19 @@ def main():
             torch.cuda.empty_cache()
             continue
         if name.endswith("+kv_write"):
-            ss = run_write(name[:-len("+kv_write")], max(3, args.steps // 2), max(1, args.warmup // 2))
+            ss = run_write(name[:-len("+kv_write")], *sec_counts(name, args.steps, args.warmup))
             log("[bench] %s" % json.dumps(ss))
             secondary.append(ss)
             torch.cuda.empty_cache()
             continue
         if name == "dit_quant":
-            ss = run_quant(max(3, args.steps // 2), max(1, args.warmup // 2))
+            ss = run_quant(*sec_counts(name, args.steps, args.warmup))
             log("[bench] %s" % json.dumps(ss))
             secondary.append(ss)
             torch.cuda.empty_cache()
             continue
         sec_path = args.path if args.path != 2 and BOUND[name] == "hbm" else 0   # 2 = prefill
-        r = run_workload(name, max(3, args.steps // 2), max(1, args.warmup // 2), path=sec_path)
+        r = run_workload(name, *sec_counts(name, args.steps, args.warmup), path=sec_path)
         ss = summarize(r)
         log("[bench] %s" % json.dumps(ss))
         secondary.append(ss)
@@ -420,13 +431,14 @@ def main():
     bound = BOUND[args.workload]
     if bound == "hbm":
         traffic = None
+        kname = ("paged_decode_balanced_kernel" if prim["path"].startswith("balanced") else
+                 "paged_decode_split_kernel" if "split" in prim["path"] else "paged_prefill_kernel")
         if args.workload == "decode_batch" and "split" in prim["path"]:
             traffic = measured_traffic(["decode_split.hip", "attn_device.h"],
-                                       "paged_decode_split_kernel__decode_batch.traffic.json")
+                                       "%s__decode_batch.traffic.json" % kname)
         roof = {"bound": "hbm", "achieved": s["main_kernel_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(s["main_kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "paged_decode_split_kernel" if "split" in prim["path"] else "paged_prefill_kernel",
-                "kernel_ms": s["main_kernel_ms"]}
+                "kernel": kname, "kernel_ms": s["main_kernel_ms"]}
     else:
         ach = prim["flops"] / (prim["main_kernel_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

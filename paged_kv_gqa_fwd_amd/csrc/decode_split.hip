@@ -28,6 +28,15 @@ __device__ __forceinline__ float load_coherent(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Load of an int32 that stays constant for the whole launch, from an address
+// uniform across the wave, through the scalar cache: the wait for it counts
+// scalar loads only, so it never waits for the page loads in flight (vector
+// loads complete in order, and waiting for a vector load issued after them
+// would wait for all of them).
+__device__ __forceinline__ int32_t load_invariant_i32(const int32_t *p) {
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
 template <int D, bool F8>
 struct DecodeCfg {
     static constexpr int STAGES = F8 ? decode_stages_f8(D) : decode_stages(D);
@@ -45,14 +54,33 @@ struct DecodeCfg {
 // Issue the 16-byte loads of one page (K and V rows of one KV head) into
 // registers.  Chunk c -> key = c / (2 DC), kv = (c / DC) % 2, dc = c % DC:
 // consecutive threads read consecutive 16 bytes of one key's K row then V row.
-// Slots at or past `valid` (the tail of a sequence's last page) are not read
-// and stage as zeros: their memory may hold anything, and a non-finite V
-// would turn the zero softmax weight of a masked key into NaN in P.V.
+// Every slot of the page is read, also those past the sequence's last key
+// (they lie inside the page, and store_page replaces them by zeros): loads
+// that always issue let the compiler count them, so waiting for one stage
+// of the ring does not wait for the stages issued after it.
 // `head_base` and the strides address pool elements (bf16 or fp8 bytes).
 template <int D, bool F8>
 __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
                                           const char *head_base, int64_t page_off,
-                                          int64_t kv_ss, int64_t kv_skv, int tid, int valid) {
+                                          int64_t kv_ss, int64_t kv_skv, int tid) {
+    using C = DecodeCfg<D, F8>;
+#pragma unroll
+    for (int it = 0; it < C::CH_PER_THREAD; ++it) {
+        const int c = it * kThreads + tid;
+        const int dc = c % C::DC;
+        const int kv = (c / C::DC) & 1;
+        const int key = c / (2 * C::DC);
+        const char *src = head_base + (page_off + (int64_t)key * kv_ss + kv * kv_skv) * C::EB + dc * 16;
+        stage[it] = *reinterpret_cast<const u32x4 *>(src);
+    }
+}
+
+// The same loads, issued only for slots before `valid` (the rest stage as
+// zeros); the count of loads issued then depends on the data.
+template <int D, bool F8>
+__device__ __forceinline__ void load_page_valid(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
+                                                const char *head_base, int64_t page_off,
+                                                int64_t kv_ss, int64_t kv_skv, int tid, int valid) {
     using C = DecodeCfg<D, F8>;
 #pragma unroll
     for (int it = 0; it < C::CH_PER_THREAD; ++it) {
@@ -73,9 +101,13 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint3
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));   // bytes 2, 3
 }
 
-template <int D, bool F8>
-__device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
-                                           uint16_t *ks, uint16_t *vs, int tid) {
+// Write a staged page into the LDS K and V tiles.  Slots at or past `valid`
+// (the tail of a sequence's last page) stage as zeros: their memory may hold
+// anything, and a non-finite V would turn the zero softmax weight of a
+// masked key into NaN in P.V.
+template <int D, bool F8, bool MASK>
+__device__ __forceinline__ void store_page_impl(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
+                                                uint16_t *ks, uint16_t *vs, int tid, int valid) {
     using C = DecodeCfg<D, F8>;
 #pragma unroll
     for (int it = 0; it < C::CH_PER_THREAD; ++it) {
@@ -84,18 +116,30 @@ __device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8
         const int kv = (c / C::DC) & 1;
         const int key = c / (2 * C::DC);
         uint16_t *dst = kv ? (vs + key * C::VROW + dc * C::EPC) : (ks + key * C::KROW + dc * C::EPC);
+        const u32x4 v = (!MASK || key < valid) ? stage[it] : u32x4{0u, 0u, 0u, 0u};
         if constexpr (!F8) {
-            *reinterpret_cast<u32x4 *>(dst) = stage[it];
+            *reinterpret_cast<u32x4 *>(dst) = v;
         } else {
             // 16 codes -> 16 bf16 (dequantised; the scales are applied to
             // the scores and the output)
             uint32_t o[8];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) e4m3x4_to_bf16x4(stage[it][q4], o[2 * q4], o[2 * q4 + 1]);
+            for (int q4 = 0; q4 < 4; ++q4) e4m3x4_to_bf16x4(v[q4], o[2 * q4], o[2 * q4 + 1]);
             *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
             *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{o[4], o[5], o[6], o[7]};
         }
     }
+}
+
+// `valid` is uniform across the workgroup: a full page takes the branch
+// without the per-chunk selects.
+template <int D, bool F8>
+__device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
+                                           uint16_t *ks, uint16_t *vs, int tid, int valid) {
+    if (valid >= kPage)
+        store_page_impl<D, F8, false>(stage, ks, vs, tid, valid);
+    else
+        store_page_impl<D, F8, true>(stage, ks, vs, tid, valid);
 }
 
 // Per-page work of one wave: keys 16w .. 16w+15 of page p (already in LDS)
@@ -318,7 +362,18 @@ void paged_decode_split_kernel(const AttnArgs a) {
     };
 
     const int64_t sp = a.kv_sp;
-    if constexpr (C::STAGES >= 3) {
+    // Every stage refill issues its loads, also past the split's last page
+    // (then of the last page again, which is still in L2): loads that always
+    // issue keep the compiler's count of loads in flight exact, so the wait
+    // for one stage never waits for the stages loaded after it.
+    const int p_last = p_end - 1;
+    auto load_id = [&](u32x4 (&stg)[C::CH_PER_THREAD], int pid) {
+        load_page<D, F8>(stg, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid);
+    };
+    auto refill = [&](u32x4 (&stg)[C::CH_PER_THREAD], int p) { load_id(stg, bt_row[min(p, p_last)]); };
+    if (p_begin > p_last) {
+        // no page: only the epilogue runs (rows of an empty sequence are zeros)
+    } else if constexpr (C::STAGES >= 3) {
         // A ring of STAGES pages in flight: page p stages in slot (p - p_begin)
         // % STAGES, and its slot is refilled with page p + STAGES once the
         // page is in LDS.  Each page id is read before the LDS store so its
@@ -326,22 +381,22 @@ void paged_decode_split_kernel(const AttnArgs a) {
         u32x4 st[C::STAGES][C::CH_PER_THREAD];
 #pragma unroll
         for (int k = 0; k < C::STAGES; ++k)
-            if (p_begin + k < p_end)
-                load_page<D, F8>(st[k], head_base, (int64_t)bt_row[p_begin + k] * sp, a.kv_ss, a.kv_skv, tid,
-                                 L - (p_begin + k) * kPage);
+            refill(st[k], p_begin + k);
         for (int p0 = p_begin; p0 < p_end; p0 += C::STAGES) {
 #pragma unroll
             for (int k = 0; k < C::STAGES; ++k) {
+                // Past the last page the group's remaining slots are skipped
+                // (uniform) but the loop body keeps one exit, at its end, so
+                // every path into the loop head has the same loads in flight.
                 const int p = p0 + k;
-                if (p >= p_end) break;           // uniform across the workgroup
-                const int pn = p + C::STAGES;
-                const int pid = pn < p_end ? bt_row[pn] : 0;
-                __syncthreads();                 // the previous page is fully consumed
-                store_page<D, F8>(st[k], ks, vs, tid);
-                __syncthreads();
-                if (pn < p_end)
-                    load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid, L - pn * kPage);
-                compute_page(p);
+                const bool live = p < p_end;
+                if (live) {
+                    __syncthreads();             // the previous page is fully consumed
+                    store_page<D, F8>(st[k], ks, vs, tid, L - p * kPage);
+                    __syncthreads();
+                }
+                refill(st[k], p + C::STAGES);
+                if (live) compute_page(p);
             }
         }
     } else if constexpr (C::STAGES == 2) {
@@ -349,47 +404,35 @@ void paged_decode_split_kernel(const AttnArgs a) {
         // odd ones.  Each page id is read one compute phase before its loads
         // issue, so the block-table latency stays off the critical path.
         u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
-        if (p_begin < p_end)
-            load_page<D, F8>(stA, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
-                         L - p_begin * kPage);
-        if (p_begin + 1 < p_end)
-            load_page<D, F8>(stB, head_base, (int64_t)bt_row[p_begin + 1] * sp, a.kv_ss, a.kv_skv, tid,
-                         L - (p_begin + 1) * kPage);
-        int pid_a = (p_begin + 2 < p_end) ? bt_row[p_begin + 2] : 0;
+        refill(stA, p_begin);
+        refill(stB, p_begin + 1);
+        int pid_a = bt_row[min(p_begin + 2, p_last)];
         for (int p = p_begin; p < p_end; p += 2) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(stA, ks, vs, tid);
+            store_page<D, F8>(stA, ks, vs, tid, L - p * kPage);
             __syncthreads();
-            if (p + 2 < p_end)
-                load_page<D, F8>(stA, head_base, (int64_t)pid_a * sp, a.kv_ss, a.kv_skv, tid,
-                             L - (p + 2) * kPage);
-            const int pid_b = (p + 3 < p_end) ? bt_row[p + 3] : 0;
+            load_id(stA, pid_a);
+            const int pid_b = bt_row[min(p + 3, p_last)];
             compute_page(p);
             if (p + 1 >= p_end) break;       // uniform across the workgroup
             __syncthreads();
-            store_page<D, F8>(stB, ks, vs, tid);
+            store_page<D, F8>(stB, ks, vs, tid, L - (p + 1) * kPage);
             __syncthreads();
-            if (p + 3 < p_end)
-                load_page<D, F8>(stB, head_base, (int64_t)pid_b * sp, a.kv_ss, a.kv_skv, tid,
-                             L - (p + 3) * kPage);
-            pid_a = (p + 4 < p_end) ? bt_row[p + 4] : 0;
+            load_id(stB, pid_b);
+            pid_a = bt_row[min(p + 4, p_last)];
             compute_page(p + 1);
         }
     } else {
         // One page in flight per workgroup; several workgroups per CU overlap.
         u32x4 st[C::CH_PER_THREAD];
-        if (p_begin < p_end)
-            load_page<D, F8>(st, head_base, (int64_t)bt_row[p_begin] * sp, a.kv_ss, a.kv_skv, tid,
-                         L - p_begin * kPage);
-        int pid = (p_begin + 1 < p_end) ? bt_row[p_begin + 1] : 0;
+        refill(st, p_begin);
+        int pid = bt_row[min(p_begin + 1, p_last)];
         for (int p = p_begin; p < p_end; ++p) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(st, ks, vs, tid);
+            store_page<D, F8>(st, ks, vs, tid, L - p * kPage);
             __syncthreads();
-            if (p + 1 < p_end)
-                load_page<D, F8>(st, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid,
-                             L - (p + 1) * kPage);
-            pid = (p + 2 < p_end) ? bt_row[p + 2] : 0;
+            load_id(st, pid);
+            pid = bt_row[min(p + 2, p_last)];
             compute_page(p);
         }
     }
@@ -478,6 +521,11 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
 void paged_decode_balanced_kernel(const AttnArgs a) {
     using C = DecodeCfg<D, F8>;
+    // bf16 pages at D = 128 (32 KB per page, two workgroups per CU) measured
+    // faster with each ring step first waiting for every load in flight (so
+    // about one page per workgroup is in flight); fp8 pages and D = 256 pages
+    // run the exact-count ring.
+    constexpr bool kDrainSteps = D == 128 && !F8;
     constexpr int QROW = D + 8;                       // bf16 per LDS Q row (16 B pad)
     constexpr int QCPR = D / 8;                       // 16-byte Q chunks per row
     constexpr int QCH = 16 * QCPR / kThreads;         // Q chunks per thread (16 rows): D / 128
@@ -581,16 +629,21 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
             }
         }
     };
-    auto page_id = [&]() { return a.block_table[(int64_t)lb * a.bt_stride + lp]; };
+    auto page_id = [&]() { return load_invariant_i32(a.block_table + (int64_t)lb * a.bt_stride + lp); };
 
     // The ring: slot k holds a page's K/V chunks, and for the first page of a
-    // piece also the piece's Q rows.
+    // piece also the piece's Q rows.  Page loads always issue, so the
+    // compiler's count of loads in flight stays exact and the wait for one
+    // slot never waits for the slots loaded after it.
     u32x4 st[C::STAGES][C::CH_PER_THREAD];
     u32x4 qst[C::STAGES][QCH];
-    int sb[C::STAGES], spg[C::STAGES];
+    int sb[C::STAGES], spg[C::STAGES], svalid[C::STAGES];
     bool snew[C::STAGES];
-    auto load_slot = [&](int k, int pid, bool first) {
-        load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid, s_L[lb] - lp * kPage);
+    // Q rows (first page of a piece) and the slot's bookkeeping for the
+    // loader's current page; then the cursor moves on.  The page id of the
+    // cursor's page is read one ring step before its loads issue, so the
+    // block-table latency stays off the critical path.
+    auto load_slot_meta = [&](int k, bool first) {
         const bool nw = first || lp == lplo;
         if (nw) {
             const int n = s_n[lb];
@@ -612,7 +665,9 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
         }
         sb[k] = lb;
         spg[k] = lp;
+        svalid[k] = __builtin_amdgcn_readfirstlane(s_L[lb] - lp * kPage);
         snew[k] = nw;
+        advance();
     };
 
     // Per-piece state.
@@ -636,23 +691,51 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
         l_part = 0.f;
     };
 
+    // Past the range's last page a slot's loads still issue, of that page
+    // again (still in L2; never used).
+    auto load_id = [&](int k, int pid) {
+        load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid);
+    };
+    int pid_next = page_id();   // unit 0; later the unit after the last one loaded
 #pragma unroll
     for (int k = 0; k < C::STAGES; ++k) {
-        if (k < nunits) {
-            load_slot(k, page_id(), k == 0);
-            advance();
+        if constexpr (kDrainSteps) {
+            if (k < nunits) {
+                load_page_valid<D, F8>(st[k], head_base, (int64_t)page_id() * sp, a.kv_ss, a.kv_skv, tid,
+                                       s_L[lb] - lp * kPage);
+                load_slot_meta(k, k == 0);
+            }
+        } else {
+            load_id(k, pid_next);
+            if (k < nunits) {
+                load_slot_meta(k, k == 0);
+                if (k + 1 < nunits) pid_next = page_id();
+            }
         }
     }
     for (int i0 = 0; i0 < nunits; i0 += C::STAGES) {
 #pragma unroll
         for (int k = 0; k < C::STAGES; ++k) {
             const int i = i0 + k;
-            if (i >= nunits) break;                      // uniform across the workgroup
+            // uniform; leaving both loops (not re-entering the loop head) keeps
+            // the compiler's count of loads in flight exact there
+            if (i >= nunits) goto ring_done;
             const bool more = i + C::STAGES < nunits;
-            const int pid = more ? page_id() : 0;
-            if (snew[k] && cb >= 0) finish_piece();      // merge + write the previous piece
+            int pid_now = 0;
+            if constexpr (kDrainSteps) {
+                // a vector load: using it waits for every load in flight
+                if (more) pid_now = a.block_table[(int64_t)lb * a.bt_stride + lp];
+            }
+            if (snew[k] && cb >= 0) {
+                finish_piece();                          // merge + write the previous piece
+                // Wait for the piece's stores here, once: while stores are
+                // in flight the compiler cannot count the page loads (stores
+                // and loads share the counter and may complete out of order)
+                // and would wait for every load in flight at each page.
+                if constexpr (!kDrainSteps) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
+            }
             __syncthreads();                             // the previous page (or the merge) is done with LDS
-            store_page<D, F8>(st[k], ks, vs, tid);
+            store_page<D, F8>(st[k], ks, vs, tid, kDrainSteps ? kPage : svalid[k]);
             if (snew[k]) {
 #pragma unroll
                 for (int j = 0; j < QCH; ++j) {
@@ -676,13 +759,23 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
                 for (int kk = 0; kk < D / 32; ++kk)
                     qreg[kk] = *reinterpret_cast<const bf16x8 *>(qs + row * QROW + 32 * kk + 8 * (lane >> 4));
             }
-            if (more) {
-                load_slot(k, pid, false);
-                advance();
+            if constexpr (kDrainSteps) {
+                if (more) {
+                    load_page_valid<D, F8>(st[k], head_base, (int64_t)pid_now * sp, a.kv_ss, a.kv_skv, tid,
+                                           s_L[lb] - lp * kPage);
+                    load_slot_meta(k, false);
+                }
+            } else {
+                load_id(k, pid_next);
+                if (more) {
+                    load_slot_meta(k, false);
+                    if (i + C::STAGES + 1 < nunits) pid_next = page_id();
+                }
             }
             decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, cp, vis, lo, a.scale_log2, w, lane);
         }
     }
+ring_done:
     finish_piece();
 }
 
