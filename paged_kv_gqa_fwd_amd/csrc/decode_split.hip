@@ -288,6 +288,100 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
     }
 }
 
+// Stream pages [p_begin, p_end) of one (sequence, KV head) through LDS into
+// the wave's online-softmax state: the ring of register stages (loads of
+// the next pages in flight while a page is computed), STAGES deep.
+//
+// The compiler's wait for one stage is exact only if every path into it
+// issued the same loads, so: page loads always issue (past the last page a
+// stage reloads the last page, still in L2; the tail of a sequence's last
+// page is read and zeroed in LDS), page ids come through the scalar cache,
+// read a compute phase ahead, and the ring has one exit.  Otherwise the
+// wait covers every load in flight and the ring drains at each page.
+template <int D, bool F8>
+__device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t *ks, uint16_t *vs,
+                                                    const char *head_base, const int32_t *bt_row, int p_begin,
+                                                    int p_end, int L, const bf16x8 (&qreg)[D / 32],
+                                                    f32x4 (&oacc)[D / 16], float &m_run, float &l_part, int vis,
+                                                    int lo, int tid) {
+    using C = DecodeCfg<D, F8>;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    auto compute_page = [&](int p) {
+        decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, w, lane);
+    };
+    const int64_t sp = a.kv_sp;
+    const int p_last = p_end - 1;
+    auto load_id = [&](u32x4 (&stg)[C::CH_PER_THREAD], int pid) {
+        load_page<D, F8>(stg, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid);
+    };
+    auto refill = [&](u32x4 (&stg)[C::CH_PER_THREAD], int p) { load_id(stg, load_invariant_i32(bt_row + min(p, p_last))); };
+    if (p_begin > p_last) {
+        // no page
+    } else if constexpr (C::STAGES >= 3) {
+        // A ring of STAGES pages in flight: page p stages in slot (p - p_begin)
+        // % STAGES, and its slot is refilled with page p + STAGES once the
+        // page is in LDS.
+        u32x4 st[C::STAGES][C::CH_PER_THREAD];
+#pragma unroll
+        for (int k = 0; k < C::STAGES; ++k)
+            refill(st[k], p_begin + k);
+        for (int p0 = p_begin; p0 < p_end; p0 += C::STAGES) {
+#pragma unroll
+            for (int k = 0; k < C::STAGES; ++k) {
+                // Past the last page the group's remaining slots are skipped
+                // (uniform) but the loop body keeps one exit, at its end, so
+                // every path into the loop head has the same loads in flight.
+                const int p = p0 + k;
+                const bool live = p < p_end;
+                if (live) {
+                    __syncthreads();             // the previous page is fully consumed
+                    store_page<D, F8>(st[k], ks, vs, tid, L - p * kPage);
+                    __syncthreads();
+                }
+                refill(st[k], p + C::STAGES);
+                if (live) compute_page(p);
+            }
+        }
+    } else if constexpr (C::STAGES == 2) {
+        // Two pages in flight: stage A holds even pages of the split, stage B
+        // odd ones.  Each page id is read one compute phase before its loads
+        // issue, so the block-table latency stays off the critical path.
+        u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
+        refill(stA, p_begin);
+        refill(stB, p_begin + 1);
+        int pid_a = load_invariant_i32(bt_row + min(p_begin + 2, p_last));
+        for (int p = p_begin; p < p_end; p += 2) {
+            __syncthreads();                 // the previous page is fully consumed
+            store_page<D, F8>(stA, ks, vs, tid, L - p * kPage);
+            __syncthreads();
+            load_id(stA, pid_a);
+            const int pid_b = load_invariant_i32(bt_row + min(p + 3, p_last));
+            compute_page(p);
+            if (p + 1 >= p_end) break;       // uniform across the workgroup
+            __syncthreads();
+            store_page<D, F8>(stB, ks, vs, tid, L - (p + 1) * kPage);
+            __syncthreads();
+            load_id(stB, pid_b);
+            pid_a = load_invariant_i32(bt_row + min(p + 4, p_last));
+            compute_page(p + 1);
+        }
+    } else {
+        // One page in flight per workgroup; several workgroups per CU overlap.
+        u32x4 st[C::CH_PER_THREAD];
+        refill(st, p_begin);
+        int pid = load_invariant_i32(bt_row + min(p_begin + 1, p_last));
+        for (int p = p_begin; p < p_end; ++p) {
+            __syncthreads();                 // the previous page is fully consumed
+            store_page<D, F8>(st, ks, vs, tid, L - p * kPage);
+            __syncthreads();
+            load_id(st, pid);
+            pid = load_invariant_i32(bt_row + min(p + 2, p_last));
+            compute_page(p);
+        }
+    }
+}
+
 template <int D, bool F8>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
@@ -307,7 +401,6 @@ void paged_decode_split_kernel(const AttnArgs a) {
     const int s = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
 
     const int L = a.seq_lens[b];
     const int q0 = a.cu_q[b];
@@ -357,85 +450,9 @@ void paged_decode_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
     float l_part = 0.f;        // this lane's share of the running sum
 
-    auto compute_page = [&](int p) {
-        decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, w, lane);
-    };
 
-    const int64_t sp = a.kv_sp;
-    // Every stage refill issues its loads, also past the split's last page
-    // (then of the last page again, which is still in L2): loads that always
-    // issue keep the compiler's count of loads in flight exact, so the wait
-    // for one stage never waits for the stages loaded after it.
-    const int p_last = p_end - 1;
-    auto load_id = [&](u32x4 (&stg)[C::CH_PER_THREAD], int pid) {
-        load_page<D, F8>(stg, head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid);
-    };
-    auto refill = [&](u32x4 (&stg)[C::CH_PER_THREAD], int p) { load_id(stg, bt_row[min(p, p_last)]); };
-    if (p_begin > p_last) {
-        // no page: only the epilogue runs (rows of an empty sequence are zeros)
-    } else if constexpr (C::STAGES >= 3) {
-        // A ring of STAGES pages in flight: page p stages in slot (p - p_begin)
-        // % STAGES, and its slot is refilled with page p + STAGES once the
-        // page is in LDS.  Each page id is read before the LDS store so its
-        // latency overlaps it.
-        u32x4 st[C::STAGES][C::CH_PER_THREAD];
-#pragma unroll
-        for (int k = 0; k < C::STAGES; ++k)
-            refill(st[k], p_begin + k);
-        for (int p0 = p_begin; p0 < p_end; p0 += C::STAGES) {
-#pragma unroll
-            for (int k = 0; k < C::STAGES; ++k) {
-                // Past the last page the group's remaining slots are skipped
-                // (uniform) but the loop body keeps one exit, at its end, so
-                // every path into the loop head has the same loads in flight.
-                const int p = p0 + k;
-                const bool live = p < p_end;
-                if (live) {
-                    __syncthreads();             // the previous page is fully consumed
-                    store_page<D, F8>(st[k], ks, vs, tid, L - p * kPage);
-                    __syncthreads();
-                }
-                refill(st[k], p + C::STAGES);
-                if (live) compute_page(p);
-            }
-        }
-    } else if constexpr (C::STAGES == 2) {
-        // Two pages in flight: stage A holds even pages of the split, stage B
-        // odd ones.  Each page id is read one compute phase before its loads
-        // issue, so the block-table latency stays off the critical path.
-        u32x4 stA[C::CH_PER_THREAD], stB[C::CH_PER_THREAD];
-        refill(stA, p_begin);
-        refill(stB, p_begin + 1);
-        int pid_a = bt_row[min(p_begin + 2, p_last)];
-        for (int p = p_begin; p < p_end; p += 2) {
-            __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(stA, ks, vs, tid, L - p * kPage);
-            __syncthreads();
-            load_id(stA, pid_a);
-            const int pid_b = bt_row[min(p + 3, p_last)];
-            compute_page(p);
-            if (p + 1 >= p_end) break;       // uniform across the workgroup
-            __syncthreads();
-            store_page<D, F8>(stB, ks, vs, tid, L - (p + 1) * kPage);
-            __syncthreads();
-            load_id(stB, pid_b);
-            pid_a = bt_row[min(p + 4, p_last)];
-            compute_page(p + 1);
-        }
-    } else {
-        // One page in flight per workgroup; several workgroups per CU overlap.
-        u32x4 st[C::CH_PER_THREAD];
-        refill(st, p_begin);
-        int pid = bt_row[min(p_begin + 1, p_last)];
-        for (int p = p_begin; p < p_end; ++p) {
-            __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(st, ks, vs, tid, L - p * kPage);
-            __syncthreads();
-            load_id(st, pid);
-            pid = bt_row[min(p + 2, p_last)];
-            compute_page(p);
-        }
-    }
+    decode_stream_pages<D, F8>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part, vis, lo,
+                               tid);
 
     // ---- merge the four waves' (m, l, O) in LDS, write ------------------
     const bool split = a.max_splits > 1;
@@ -501,36 +518,22 @@ void paged_decode_split_kernel(const AttnArgs a) {
 // pages; workgroup (g, r) streams range r for KV head g, so every workgroup
 // of the launch reads the same number of pages whatever the mix of lengths.
 // A range may end inside one sequence and go on into the next: each
-// (sequence, range) piece keeps its own online-softmax state.  A sequence
-// held by one range is written out directly; otherwise its pieces go to
-// split slots r - floor(F_b / C) (F_b = pages of the sequences before it)
-// and the combine kernel merges them.  pages_per_split (the plan's minimum
-// C) bounds a sequence's pieces by max_splits.
+// (sequence, range) piece is streamed with its own online-softmax state.  A
+// sequence held by one range is written out directly; otherwise its pieces
+// go to split slots r - floor(F_b / C) (F_b = pages of the sequences before
+// it) and the combine kernel merges them.  pages_per_split (the plan's
+// minimum C) bounds a sequence's pieces by max_splits.
 //
 // Every workgroup derives the partition itself from seq_lens and cu_q (an
 // LDS prefix sum over at most kBalMaxSeqs sequences), so nothing but the
 // launch orders the two kernels.  Workgroup (0, 0) publishes each
 // sequence's piece count for the combine kernel.
-//
-// The page ring runs across sequence boundaries: the next pages are loaded
-// while the current piece is merged and written, and the Q rows of a new
-// piece travel in the ring with its first page (staged through LDS), so no
-// wait for them drains the loads in flight.
 template <int D, bool F8>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
 void paged_decode_balanced_kernel(const AttnArgs a) {
     using C = DecodeCfg<D, F8>;
-    // bf16 pages at D = 128 (32 KB per page, two workgroups per CU) measured
-    // faster with each ring step first waiting for every load in flight (so
-    // about one page per workgroup is in flight); fp8 pages and D = 256 pages
-    // run the exact-count ring.
-    constexpr bool kDrainSteps = D == 128 && !F8;
-    constexpr int QROW = D + 8;                       // bf16 per LDS Q row (16 B pad)
-    constexpr int QCPR = D / 8;                       // 16-byte Q chunks per row
-    constexpr int QCH = 16 * QCPR / kThreads;         // Q chunks per thread (16 rows): D / 128
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t qs[16 * QROW];
     __shared__ float red_m[4][16];
     __shared__ float red_l[4][16];
     __shared__ int s_F[kBalMaxSeqs + 1];   // s_F[b] = pages of the sequences before b
@@ -608,175 +611,60 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
     __syncthreads();
 
     const char *head_base = reinterpret_cast<const char *>(a.kv) + (int64_t)g * a.kv_sh * C::EB;
-    const int64_t sp = a.kv_sp;
-
-    // Loader cursor (uniform): sequence lb, page lp, its first and end pages.
-    int lb = __builtin_amdgcn_readfirstlane(s_first);
-    int lend = __builtin_amdgcn_readfirstlane((s_L[lb] + kPage - 1) / kPage);
-    int lplo = __builtin_amdgcn_readfirstlane(lend - (s_F[lb + 1] - s_F[lb]));
-    int lp = __builtin_amdgcn_readfirstlane(lplo + (u0 - s_F[lb]));
-    auto advance = [&]() {
-        ++lp;
-        if (lp == lend) {
-            do {
-                ++lb;
-            } while (lb < B && s_F[lb + 1] == s_F[lb]);
-            lb = __builtin_amdgcn_readfirstlane(lb);
-            if (lb < B) {
-                lend = __builtin_amdgcn_readfirstlane((s_L[lb] + kPage - 1) / kPage);
-                lplo = __builtin_amdgcn_readfirstlane(lend - (s_F[lb + 1] - s_F[lb]));
-                lp = lplo;
-            }
-        }
-    };
-    auto page_id = [&]() { return load_invariant_i32(a.block_table + (int64_t)lb * a.bt_stride + lp); };
-
-    // The ring: slot k holds a page's K/V chunks, and for the first page of a
-    // piece also the piece's Q rows.  Page loads always issue, so the
-    // compiler's count of loads in flight stays exact and the wait for one
-    // slot never waits for the slots loaded after it.
-    u32x4 st[C::STAGES][C::CH_PER_THREAD];
-    u32x4 qst[C::STAGES][QCH];
-    int sb[C::STAGES], spg[C::STAGES], svalid[C::STAGES];
-    bool snew[C::STAGES];
-    // Q rows (first page of a piece) and the slot's bookkeeping for the
-    // loader's current page; then the cursor moves on.  The page id of the
-    // cursor's page is read one ring step before its loads issue, so the
-    // block-table latency stays off the critical path.
-    auto load_slot_meta = [&](int k, bool first) {
-        const bool nw = first || lp == lplo;
-        if (nw) {
-            const int n = s_n[lb];
-            const int q0 = s_q0[lb];
-            const int rows = min(n * G, 16);
-#pragma unroll
-            for (int j = 0; j < QCH; ++j) {
-                const int c = j * kThreads + tid;
-                const int qrow = c / QCPR;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (qrow < rows) {
-                    const int qi = qrow / G;
-                    const int h = g * G + (qrow - qi * G);
-                    v = *reinterpret_cast<const u32x4 *>(a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh +
-                                                         8 * (c % QCPR));
-                }
-                qst[k][j] = v;
-            }
-        }
-        sb[k] = lb;
-        spg[k] = lp;
-        svalid[k] = __builtin_amdgcn_readfirstlane(s_L[lb] - lp * kPage);
-        snew[k] = nw;
-        advance();
-    };
-
-    // Per-piece state.
-    int cb = -1, cq0 = 0, crows = 0, vis = 0, lo = 0;
-    bf16x8 qreg[D / 32];
-    f32x4 oacc[D / 16];
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_part = 0.f;
     const int row = lane & 15;
-    auto finish_piece = [&]() {
-        const int F0 = s_F[cb];
-        const int np = s_F[cb + 1] - F0;
-        const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
-        decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, cb, g, cq0, crows, ns > 1,
-                                  r - F0 / Cr, false, tid);
+    f32x4 oacc[D / 16];
+    bf16x8 qreg[D / 32];
+
+    // The range's pieces, in sequence order: sequence b from page p.
+    int b = __builtin_amdgcn_readfirstlane(s_first);
+    int p = __builtin_amdgcn_readfirstlane((s_L[b] + kPage - 1) / kPage - (s_F[b + 1] - s_F[b]) + (u0 - s_F[b]));
+    int left = nunits;
+    while (true) {   // uniform
+        const int L = __builtin_amdgcn_readfirstlane(s_L[b]);
+        const int n = __builtin_amdgcn_readfirstlane(s_n[b]);
+        const int q0 = __builtin_amdgcn_readfirstlane(s_q0[b]);
+        const int F0 = __builtin_amdgcn_readfirstlane(s_F[b]);
+        const int np = __builtin_amdgcn_readfirstlane(s_F[b + 1]) - F0;
+        const int cnt = min(left, (L + kPage - 1) / kPage - p);
+        const int rows = min(n * G, 16);
+        const bool row_ok = row < rows;
+        const int qi = row / G;
+        const int h = g * G + (row - qi * G);
+        const int vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
+        const int lo = row_ok ? window_start(L - n + qi, a.window) : 0;
+        {
+            const uint16_t *qp = a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh + 8 * (lane >> 4);
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk);
+                qreg[kk] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
-        l_part = 0.f;
-    };
-
-    // Past the range's last page a slot's loads still issue, of that page
-    // again (still in L2; never used).
-    auto load_id = [&](int k, int pid) {
-        load_page<D, F8>(st[k], head_base, (int64_t)pid * sp, a.kv_ss, a.kv_skv, tid);
-    };
-    int pid_next = page_id();   // unit 0; later the unit after the last one loaded
-#pragma unroll
-    for (int k = 0; k < C::STAGES; ++k) {
-        if constexpr (kDrainSteps) {
-            if (k < nunits) {
-                load_page_valid<D, F8>(st[k], head_base, (int64_t)page_id() * sp, a.kv_ss, a.kv_skv, tid,
-                                       s_L[lb] - lp * kPage);
-                load_slot_meta(k, k == 0);
-            }
-        } else {
-            load_id(k, pid_next);
-            if (k < nunits) {
-                load_slot_meta(k, k == 0);
-                if (k + 1 < nunits) pid_next = page_id();
-            }
-        }
+        float m_run = -INFINITY;
+        float l_part = 0.f;
+        decode_stream_pages<D, F8>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p, p + cnt, L,
+                                   qreg, oacc, m_run, l_part, vis, lo, tid);
+        // The piece: the whole sequence (written out) or split slot
+        // r - floor(F_b / C) of its ns pieces.
+        const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
+        decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, ns > 1,
+                                  r - F0 / Cr, false, tid);
+        left -= cnt;
+        if (left <= 0) break;
+        // Wait for the piece's stores before the next piece's loads: while
+        // stores are in flight the compiler cannot count loads exactly
+        // (stores and loads share the counter) and would drain the ring at
+        // every page.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+        do {
+            ++b;
+        } while (s_F[b + 1] == s_F[b]);       // a later sequence with pages exists: left > 0
+        b = __builtin_amdgcn_readfirstlane(b);
+        p = __builtin_amdgcn_readfirstlane((s_L[b] + kPage - 1) / kPage - (s_F[b + 1] - s_F[b]));
     }
-    for (int i0 = 0; i0 < nunits; i0 += C::STAGES) {
-#pragma unroll
-        for (int k = 0; k < C::STAGES; ++k) {
-            const int i = i0 + k;
-            // uniform; leaving both loops (not re-entering the loop head) keeps
-            // the compiler's count of loads in flight exact there
-            if (i >= nunits) goto ring_done;
-            const bool more = i + C::STAGES < nunits;
-            int pid_now = 0;
-            if constexpr (kDrainSteps) {
-                // a vector load: using it waits for every load in flight
-                if (more) pid_now = a.block_table[(int64_t)lb * a.bt_stride + lp];
-            }
-            if (snew[k] && cb >= 0) {
-                finish_piece();                          // merge + write the previous piece
-                // Wait for the piece's stores here, once: while stores are
-                // in flight the compiler cannot count the page loads (stores
-                // and loads share the counter and may complete out of order)
-                // and would wait for every load in flight at each page.
-                if constexpr (!kDrainSteps) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
-            }
-            __syncthreads();                             // the previous page (or the merge) is done with LDS
-            store_page<D, F8>(st[k], ks, vs, tid, kDrainSteps ? kPage : svalid[k]);
-            if (snew[k]) {
-#pragma unroll
-                for (int j = 0; j < QCH; ++j) {
-                    const int c = j * kThreads + tid;
-                    *reinterpret_cast<u32x4 *>(qs + (c / QCPR) * QROW + 8 * (c % QCPR)) = qst[k][j];
-                }
-            }
-            __syncthreads();
-            const int cp = spg[k];
-            if (snew[k]) {
-                cb = sb[k];
-                const int L = s_L[cb];
-                const int n = s_n[cb];
-                cq0 = s_q0[cb];
-                crows = min(n * G, 16);
-                const bool row_ok = row < crows;
-                const int qi = row / G;
-                vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
-                lo = row_ok ? window_start(L - n + qi, a.window) : 0;
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk)
-                    qreg[kk] = *reinterpret_cast<const bf16x8 *>(qs + row * QROW + 32 * kk + 8 * (lane >> 4));
-            }
-            if constexpr (kDrainSteps) {
-                if (more) {
-                    load_page_valid<D, F8>(st[k], head_base, (int64_t)pid_now * sp, a.kv_ss, a.kv_skv, tid,
-                                           s_L[lb] - lp * kPage);
-                    load_slot_meta(k, false);
-                }
-            } else {
-                load_id(k, pid_next);
-                if (more) {
-                    load_slot_meta(k, false);
-                    if (i + C::STAGES + 1 < nunits) pid_next = page_id();
-                }
-            }
-            decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, cp, vis, lo, a.scale_log2, w, lane);
-        }
-    }
-ring_done:
-    finish_piece();
 }
 
 // Log-sum-exp merge of the split partials: per (token, q head) row,
