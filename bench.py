@@ -95,6 +95,48 @@ def _time_steps(fn, steps):
     return t0.elapsed_time(t1) / steps
 
 
+def _step_distribution(fn, steps):
+    """Per-step ms from an event pair around each call (a separate pass):
+    mean, p50, p90, min, max."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: ts[min(len(ts) - 1, int(round(q * (len(ts) - 1))))]
+    return {"mean": round(sum(ts) / len(ts), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4),
+            "min": round(ts[0], 4), "max": round(ts[-1], 4)}
+
+
+def stream_read_ceiling(nbytes, launches=50, grids=(512, 1024, 2048)):
+    """The on-box read ceiling: GB/s of the library's plain streaming-read
+    kernel over a buffer of nbytes (best over a few grid sizes)."""
+    import paged_kv_gqa_fwd_amd as pa
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    best = None
+    for g in grids:
+        for _ in range(10):
+            pa.stream_read(buf, g, sink)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(launches):
+            pa.stream_read(buf, g, sink)
+        t1.record()
+        torch.cuda.synchronize()
+        gbs = n / (t0.elapsed_time(t1) / launches * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, g)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"GBps": round(best[0], 2), "grid": best[1], "bytes": n, "launches": launches}
+
+
 def _kernel_times(fn, steps):
     """Per-kind average kernel ms from the library's per-launch HIP events
     (recorded on the launch stream), in a separate pass so the step timing
@@ -145,9 +187,10 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
         step()
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, _ = _kernel_times(step, steps)
+    dist = _step_distribution(step, steps)
     res = {
         "workload": name + ("+window%d" % window if window else "") + ("+fp8" if fp8 else ""), "case": case,
-        "ms_per_step": step_ms,
+        "ms_per_step": step_ms, "step_ms_dist": dist,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
                  pa.PATH_SPLIT_BALANCED: "balanced_split_decode+combine", pa.PATH_PREFILL: "prefill"}[plan.path],
@@ -240,11 +283,13 @@ def summarize(res):
                 "main_kernel_ms": round(res["main_kernel_ms"], 4),
                 "combine_kernel_ms": round(res["combine_kernel_ms"], 4),
                 "main_kernel_GBps": round(kern, 2), "path": res["path"],
-                "pages_per_split": res["pages_per_split"], "max_splits": res["max_splits"]}
+                "pages_per_split": res["pages_per_split"], "max_splits": res["max_splits"],
+                "step_ms_dist": res.get("step_ms_dist")}
     val = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
     return {"workload": name, "value": round(val, 2), "unit": "TFLOP/s",
             "frac_of_peak": round(val / BF16_PEAK_TFLOPS, 4), "ms_per_step": round(res["ms_per_step"], 4),
-            "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"]}
+            "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"],
+            "step_ms_dist": res.get("step_ms_dist")}
 
 
 def cpu_baseline(res, max_seconds=20.0):
@@ -281,7 +326,18 @@ def cpu_baseline(res, max_seconds=20.0):
         unit = "TFLOP/s"
     return {"value": round(val, 4), "unit": unit, "cores": nthreads, "kind": "oracle",
             "sample": "first %d of %d sequences of the %s workload, %d timed passes of %.3f s each "
-                      "(fp64 oracle, OpenMP threads=%d)" % (k, case.n_seqs, name, reps, t_used, nthreads)}
+                      "(fp64 oracle, OpenMP threads=%d)" % (k, case.n_seqs, name, reps, t_used, nthreads),
+            "cpu": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _prefix_case(case, k):
@@ -444,6 +500,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "kernel": "paged_prefill_kernel", "kernel_ms": s["main_kernel_ms"]}
+    ceiling = None
+    if bound == "hbm":
+        # the practical denominator beside the 8 TB/s peak: a plain read
+        # stream over as many bytes as one step moves
+        ceiling = stream_read_ceiling(prim["bytes"])
+        ceiling["kernel_frac"] = round(s["main_kernel_GBps"] / ceiling["GBps"], 4)
+        ceiling["step_frac"] = round(s["value"] / ceiling["GBps"], 4)
+        log("[bench] read ceiling %s" % json.dumps(ceiling))
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
@@ -462,6 +526,8 @@ def main():
                    "pages_per_split": prim["pages_per_split"], "max_splits": prim["max_splits"]},
         "frac_of_peak": s["frac_of_peak"],
         "roofline": roof,
+        "read_ceiling": ceiling,
+        "step_ms_dist": s.get("step_ms_dist"),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

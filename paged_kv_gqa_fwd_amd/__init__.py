@@ -157,6 +157,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     dp, ip = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)
     lib.attn_kernel_timing_read.argtypes = [dp, ip, dp, ip, dp, ip]
     lib.attn_kernel_timing_read.restype = ctypes.c_int
+    lib.attn_stream_read.argtypes = [p, sz, p, i32, p]
+    lib.attn_stream_read.restype = ctypes.c_int
     qd_p = ctypes.POINTER(attn_quant_dims)
     lib.attn_quant_layout_of.argtypes = [qd_p, ctypes.POINTER(attn_quant_layout)]
     lib.attn_quant_layout_of.restype = ctypes.c_int
@@ -399,6 +401,26 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
     if cached is not None:
         cached.clean = plan.counter_bytes
     return out
+
+
+def stream_read(buf: torch.Tensor, grid: int = 512, sink: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Read the bytes of a contiguous GPU tensor once through
+    ``attn_stream_read`` (the plain HBM read stream used as the on-box read
+    ceiling).  Returns the sink (uint32 [grid * 256], overwritten)."""
+    lib = load_library()
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=buf.device)
+    if sink.numel() < grid * 256 or not sink.is_cuda:
+        raise ValueError("sink must be a GPU tensor of at least grid * 256 int32")
+    st = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    rc = lib.attn_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), int(grid), ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return sink
 
 
 def kernel_timing_enable(on: bool) -> None:

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["paged_attn_api.cpp", "decode_split.hip", "prefill.hip", "quant.hip", "kv_write.hip"]
+SOURCES = ["paged_attn_api.cpp", "decode_split.hip", "prefill.hip", "quant.hip", "kv_write.hip", "stream_read.hip"]
 
 
 def _hipcc() -> str:

@@ -57,7 +57,10 @@ struct DecodeCfg {
 // Every slot of the page is read, also those past the sequence's last key
 // (they lie inside the page, and store_page replaces them by zeros): loads
 // that always issue let the compiler count them, so waiting for one stage
-// of the ring does not wait for the stages issued after it.
+// of the ring does not wait for the stages issued after it.  The loads are
+// non-temporal (each K/V byte is read once per launch): on MI355X that
+// raised a plain read stream from 6.45 to 7.3 TB/s and the decode kernels
+// by 2-13%.
 // `head_base` and the strides address pool elements (bf16 or fp8 bytes).
 template <int D, bool F8>
 __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
@@ -71,7 +74,7 @@ __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_P
         const int kv = (c / C::DC) & 1;
         const int key = c / (2 * C::DC);
         const char *src = head_base + (page_off + (int64_t)key * kv_ss + kv * kv_skv) * C::EB + dc * 16;
-        stage[it] = *reinterpret_cast<const u32x4 *>(src);
+        stage[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
     }
 }
 

@@ -409,3 +409,15 @@ def test_quant_calls_validate_before_launch(pa):
     assert lib.attn_quant_fwd(0x1008, 0x1000, 0x1000, 0x1000, ctypes.byref(d), 0.1, 0, 0x1000, 1 << 30, None) == -5
     # non-finite scale
     assert lib.attn_quant_fwd(0x1000, 0x1000, 0x1000, 0x1000, ctypes.byref(d), float("nan"), 0, 0x1000, 1 << 30, None) == -2
+
+
+def test_stream_read_validation(pa):
+    lib = pa.load_library()
+    assert lib.attn_stream_read(None, 16, FAKE, 1, None) == E_NULL
+    assert lib.attn_stream_read(FAKE, 16, None, 1, None) == E_NULL
+    assert lib.attn_stream_read(FAKE + 8, 16, FAKE, 1, None) == E_ALIGN     # buffer not 16-byte aligned
+    assert lib.attn_stream_read(FAKE, 24, FAKE, 1, None) == E_ALIGN         # not a multiple of 16 bytes
+    assert lib.attn_stream_read(FAKE, 16, FAKE + 2, 1, None) == E_ALIGN     # sink not 4-byte aligned
+    assert lib.attn_stream_read(FAKE, 16, FAKE, 0, None) == E_SHAPE
+    assert lib.attn_stream_read(FAKE, 16, FAKE, 65536, None) == E_SHAPE
+    assert lib.attn_stream_read(FAKE, 0, FAKE, 1, None) == OK               # nothing to read: no launch
