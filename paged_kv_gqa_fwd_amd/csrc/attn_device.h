@@ -24,7 +24,7 @@ constexpr int kBalMaxSeqs = 1024;  // sequences the balanced split path plans in
 // resident waves per SIMD requested from the register allocator.  The host
 // planner sizes splits from the same numbers.
 #ifndef PA_DECODE_STAGES_128
-#define PA_DECODE_STAGES_128 2
+#define PA_DECODE_STAGES_128 1
 #endif
 #ifndef PA_DECODE_STAGES_256
 #define PA_DECODE_STAGES_256 1
@@ -44,10 +44,12 @@ constexpr int prefill_rows(int d) { return d == 128 ? 256 : 128; }
 #endif
 constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 256; }
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
-// Pages in flight per workgroup over an fp8 cache: a page carries half the
-// bytes, so more of them keep the same bytes in flight in the same registers.
+// Pages in flight per workgroup over an fp8 cache.  With non-temporal page
+// loads fewer bytes in flight per workgroup read faster on MI355X (as for a
+// plain read stream): one page at D = 128 (two workgroups per CU), two at
+// D = 256 (one workgroup per CU).
 #ifndef PA_DECODE_F8_STAGES_128
-#define PA_DECODE_F8_STAGES_128 4
+#define PA_DECODE_F8_STAGES_128 1
 #endif
 #ifndef PA_DECODE_F8_STAGES_256
 #define PA_DECODE_F8_STAGES_256 2
