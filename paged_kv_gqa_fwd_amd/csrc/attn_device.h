@@ -35,14 +35,17 @@ constexpr int kBalMaxSeqs = 1024;  // sequences the balanced split path plans in
 #ifndef PA_DECODE_WAVES_256
 #define PA_DECODE_WAVES_256 1
 #endif
-// Packed query rows per prefill workgroup: 8 waves x 32 rows (or 4 x 64)
-// at D = 128, 4 waves x 32 rows at D = 256.
-constexpr int prefill_rows(int d) { return d == 128 ? 256 : 128; }
-// Threads per prefill workgroup (two wave64 per SIMD at head_dim 128).
+// Prefill workgroups: wave64 count at each head_dim (two per SIMD at
+// D = 128; one per SIMD at D = 256 by default) and packed query rows: 32
+// rows per wave (4 x 64 at D = 128 with PA_PF_WAVES128 = 4).
 #ifndef PA_PF_WAVES128
 #define PA_PF_WAVES128 8
 #endif
-constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 256; }
+#ifndef PA_PF_WAVES256
+#define PA_PF_WAVES256 4
+#endif
+constexpr int prefill_rows(int d) { return d == 128 ? 256 : 32 * PA_PF_WAVES256; }
+constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 64 * PA_PF_WAVES256; }
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
 // Pages in flight per workgroup over an fp8 cache.  With non-temporal page
 // loads fewer bytes in flight per workgroup read faster on MI355X (as for a

@@ -47,7 +47,7 @@ namespace pa {
 
 template <int D>
 struct PfCfg {
-    static constexpr int WAVES = D == 128 ? PA_PF_WAVES128 : 4;
+    static constexpr int WAVES = D == 128 ? PA_PF_WAVES128 : PA_PF_WAVES256;
     static constexpr int THREADS = 64 * WAVES;
     // 32-row MFMA blocks per wave: two when one wave runs per SIMD (every
     // LDS operand feeds two MFMAs); one when two waves share a SIMD (their
