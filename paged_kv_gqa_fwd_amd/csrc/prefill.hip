@@ -24,8 +24,10 @@
 //    (global_load_lds_dwordx4), no register staging, through rings of K and
 //    V page buffers with one or two pages in flight beyond the next one.
 //    Rows are stored with an XOR swizzle of their 16-byte chunks (K: chunk c
-//    of key k at c ^ (k&7); V: at c ^ 2(k&3)) so both the b128 K reads and
-//    the transposing V reads are bank-conflict free without padding.
+//    of key k at c ^ (k&15); V: at c ^ 4(k&3)) so both the b128 K reads and
+//    the transposing V reads are bank-conflict free without padding on
+//    gfx950's 64-bank LDS (zero SQ_LDS_BANK_CONFLICT; the 32-bank layout
+//    this replaced spent half of its LDS cycles in conflicts).
 //  * The 32-key steps are software pipelined: the P.V MFMAs of step j-1
 //    run while the VALU takes the row max of step j, and the Q.K MFMAs of
 //    step j+1 run while the VALU exponentiates step j.
@@ -76,9 +78,10 @@ constexpr float kRescaleThreshold = 8.f;   // log2 units: P stays <= 256
 // Direct HBM -> LDS loads of one page (K and V rows of one KV head).  LDS
 // position p = i*THREADS + tid of a tile holds key p / CH, physical chunk
 // p % CH.  The 16-byte chunks of a row are permuted so that the operand
-// reads hit 32 distinct 4-byte banks per LDS cycle: K chunk c of key k is
-// stored at c ^ (k & 7) (eight keys per b128 read cycle), V chunk c at
-// c ^ 2(k & 3) (four keys x two chunks per transposing read cycle).
+// reads hit 64 distinct 4-byte banks per LDS cycle (256 bytes): K chunk c
+// of key k is stored at c ^ (k & 15) (sixteen keys per b128 read cycle), V
+// chunk c at c ^ 4(k & 3) (four keys x four chunks per transposing read
+// cycle).
 // kof / vof hold this thread's byte offsets within a page, kof0 / vof0 the
 // same chunks of key 0.  Keys at or past `valid` re-read key 0 (always valid
 // when a page is loaded): their weight is exactly zero, but a poisoned
@@ -187,8 +190,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     for (int i = 0; i < C::LOADS; ++i) {
         const int p = i * C::THREADS + tid;
         const int key = p / C::CH;
-        const int ck = (p % C::CH) ^ (key & 7);
-        const int cv = (p % C::CH) ^ (2 * (key & 3));
+        const int ck = (p % C::CH) ^ (key & 15);
+        const int cv = (p % C::CH) ^ (4 * (key & 3));
         pl.key[i] = key;
         pl.kof[i] = (uint32_t)(key * a.kv_ss + ck * 8) * 2u;
         pl.vof[i] = (uint32_t)(key * a.kv_ss + cv * 8) * 2u;
@@ -234,15 +237,15 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     const float sl2 = a.scale_log2_pos;   // > 0
 
     // Per-lane LDS element offsets.  K operand of a 32-key step: key
-    // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ (lane & 7).
+    // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ (lane & 15).
     // V operand (transposing reads): key vkey (+8), columns of chunk
-    // 4 db + vcol_chunk, physical chunk ^ 2(vkey & 3).
+    // 4 db + vcol_chunk, physical chunk ^ 4(vkey & 3).
     const int klane = (lane & 31) * D;
-    const int kswz = lane & 7;
+    const int kswz = lane & 15;
     const int q16 = lane >> 4;
     const int vkey = 4 * hi + ((lane & 15) >> 2);
     const int vlane = vkey * D + ((4 * (lane & 3)) & 7);
-    const int vswz = 2 * (vkey & 3);
+    const int vswz = 4 * (vkey & 3);
     const int vcol_chunk = 2 * (q16 & 1) + ((4 * (lane & 3)) >> 3);
 
     constexpr int NKS = D / 16;            // Q.K MFMA k-steps per 32-key step

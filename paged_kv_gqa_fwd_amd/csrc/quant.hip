@@ -251,17 +251,19 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
     const float qscale = a.sq[((int64_t)b * a.h + h) * a.blocks + (row_ok ? row : 0) / kQuantBlock];
 
     // per-thread DMA offsets: K tile chunk p = i*256 + tid (16-byte units,
-    // 8 per key row): key p/8, physical chunk p%8, logical chunk ^ (key & 7).
-    // V^T tile: row d = p/4, physical chunk p%4, logical chunk ^ ((d>>1)&3).
+    // 8 per key row): key p/8, physical chunk p%8, logical chunk ^ ((key>>1) & 7).
+    // V^T tile: row d = p/4, physical chunk p%4, logical chunk ^ ((d>>2)&3).
+    // With 64 four-byte banks (256 bytes per LDS cycle) the sixteen lanes of
+    // one b128 read cycle then hit sixteen distinct 16-byte bank groups.
     uint32_t koff[2], voff[2];
     int kkey[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = i * 256 + tid;
-        const int key = p / 8, ck = (p % 8) ^ (key & 7);
+        const int key = p / 8, ck = (p % 8) ^ ((key >> 1) & 7);
         kkey[i] = key;
         koff[i] = (uint32_t)(key * a.h * D + ck * 16);
-        const int d = p / 4, cv = (p % 4) ^ ((d >> 1) & 3);
+        const int d = p / 4, cv = (p % 4) ^ ((d >> 2) & 3);
         voff[i] = (uint32_t)(d * a.vt_stride + cv * 16);
     }
     const int8_t *kbase = a.ki + ((int64_t)b * N * a.h + h) * D;
@@ -306,9 +308,9 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
 
     // operand offsets
     const int klane = (lane & 31) * D;
-    const int kswz = lane & 7;
+    const int kswz = ((lane & 31) >> 1) & 7;
     const int vrow = (lane & 31);
-    const int vswz = (vrow >> 1) & 3;
+    const int vswz = (vrow >> 2) & 3;
 
     for (int t = 0; t < ntiles; ++t) {
         const int st = t % kQStages;
