@@ -306,7 +306,9 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
                                                     const char *head_base, const int32_t *bt_row, int p_begin,
                                                     int p_end, int L, const bf16x8 (&qreg)[D / 32],
                                                     f32x4 (&oacc)[D / 16], float &m_run, float &l_part, int vis,
-                                                    int lo, int tid) {
+                                                    int lo, int tid,
+                                                    u32x4 (&st1)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
+                                                    bool preloaded, int next_pid) {
     using C = DecodeCfg<D, F8>;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -371,15 +373,22 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
         }
     } else {
         // One page in flight per workgroup; several workgroups per CU overlap.
-        u32x4 st[C::CH_PER_THREAD];
-        refill(st, p_begin);
-        int pid = load_invariant_i32(bt_row + min(p_begin + 1, p_last));
+        // The stage st1 is the caller's: it may arrive holding page p_begin
+        // (loaded during the previous piece's last page) and, given the next
+        // piece's first page id, leave holding that page instead of a reload
+        // of the last one, so a piece boundary does not restart the stream.
+        auto pid_after = [&](int q) {   // id of the page to load once page q - 1 is stored
+            const int id = load_invariant_i32(bt_row + min(q, p_last));
+            return (q > p_last && next_pid >= 0) ? next_pid : id;
+        };
+        if (!preloaded) refill(st1, p_begin);
+        int pid = pid_after(p_begin + 1);
         for (int p = p_begin; p < p_end; ++p) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(st, ks, vs, tid, L - p * kPage);
+            store_page<D, F8>(st1, ks, vs, tid, L - p * kPage);
             __syncthreads();
-            load_id(st, pid);
-            pid = load_invariant_i32(bt_row + min(p + 2, p_last));
+            load_id(st1, pid);
+            pid = pid_after(p + 2);
             compute_page(p);
         }
     }
@@ -454,8 +463,9 @@ void paged_decode_split_kernel(const AttnArgs a) {
     float l_part = 0.f;        // this lane's share of the running sum
 
 
+    u32x4 st1[C::CH_PER_THREAD];
     decode_stream_pages<D, F8>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part, vis, lo,
-                               tid);
+                               tid, st1, false, -1);
 
     // ---- merge the four waves' (m, l, O) in LDS, write ------------------
     const bool split = a.max_splits > 1;
@@ -622,6 +632,11 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
     int b = __builtin_amdgcn_readfirstlane(s_first);
     int p = __builtin_amdgcn_readfirstlane((s_L[b] + kPage - 1) / kPage - (s_F[b + 1] - s_F[b]) + (u0 - s_F[b]));
     int left = nunits;
+    // With one register stage the next piece's first page is loaded during
+    // the current piece's last page (the stage is carried across pieces).
+    constexpr bool kCarry = C::STAGES == 1;
+    u32x4 st1[C::CH_PER_THREAD];
+    bool preloaded = false;
     while (true) {   // uniform
         const int L = __builtin_amdgcn_readfirstlane(s_L[b]);
         const int n = __builtin_amdgcn_readfirstlane(s_n[b]);
@@ -629,6 +644,16 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
         const int F0 = __builtin_amdgcn_readfirstlane(s_F[b]);
         const int np = __builtin_amdgcn_readfirstlane(s_F[b + 1]) - F0;
         const int cnt = min(left, (L + kPage - 1) / kPage - p);
+        // The next piece, if any: the next sequence with pages, from its first page.
+        int b2 = b, p2 = 0, next_pid = -1;
+        if (left > cnt) {
+            do {
+                ++b2;
+            } while (s_F[b2 + 1] == s_F[b2]);   // a later sequence with pages exists: left > cnt
+            b2 = __builtin_amdgcn_readfirstlane(b2);
+            p2 = __builtin_amdgcn_readfirstlane((s_L[b2] + kPage - 1) / kPage - (s_F[b2 + 1] - s_F[b2]));
+            if constexpr (kCarry) next_pid = load_invariant_i32(a.block_table + (int64_t)b2 * a.bt_stride + p2);
+        }
         const int rows = min(n * G, 16);
         const bool row_ok = row < rows;
         const int qi = row / G;
@@ -649,7 +674,7 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
         float m_run = -INFINITY;
         float l_part = 0.f;
         decode_stream_pages<D, F8>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p, p + cnt, L,
-                                   qreg, oacc, m_run, l_part, vis, lo, tid);
+                                   qreg, oacc, m_run, l_part, vis, lo, tid, st1, preloaded, next_pid);
         // The piece: the whole sequence (written out) or split slot
         // r - floor(F_b / C) of its ns pieces.
         const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
@@ -657,16 +682,15 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
                                   r - F0 / Cr, false, tid);
         left -= cnt;
         if (left <= 0) break;
-        // Wait for the piece's stores before the next piece's loads: while
-        // stores are in flight the compiler cannot count loads exactly
-        // (stores and loads share the counter) and would drain the ring at
-        // every page.
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
-        do {
-            ++b;
-        } while (s_F[b + 1] == s_F[b]);       // a later sequence with pages exists: left > 0
-        b = __builtin_amdgcn_readfirstlane(b);
-        p = __builtin_amdgcn_readfirstlane((s_L[b] + kPage - 1) / kPage - (s_F[b + 1] - s_F[b]));
+        // Deeper rings wait for the piece's stores before the next piece's
+        // loads: while stores are in flight the compiler cannot count loads
+        // exactly (stores and loads share the counter) and would drain the
+        // ring at every page.  A one-stage ring waits for all loads at each
+        // page anyway, and its next page is already in flight.
+        if constexpr (!kCarry) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+        b = b2;
+        p = p2;
+        preloaded = kCarry;
     }
 }
 
