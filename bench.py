@@ -111,30 +111,32 @@ def _step_distribution(fn, steps):
             "min": round(ts[0], 4), "max": round(ts[-1], 4)}
 
 
-def stream_read_ceiling(nbytes, launches=50, grids=(512, 1024, 2048)):
+def stream_read_ceiling(nbytes, launches=50, configs=((256, 8), (512, 4), (512, 8), (1024, 4), (2048, 4))):
     """The on-box read ceiling: GB/s of the library's plain streaming-read
-    kernel over a buffer of nbytes (best over a few grid sizes)."""
+    kernel over a buffer of nbytes (best over a few grid sizes and load
+    depths)."""
     import paged_kv_gqa_fwd_amd as pa
     n = (nbytes + 15) // 16 * 16
     buf = torch.ones(n, dtype=torch.uint8, device="cuda")
-    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    sink = torch.empty(max(g for g, _ in configs) * 256, dtype=torch.int32, device="cuda")
     best = None
-    for g in grids:
+    for g, depth in configs:
         for _ in range(10):
-            pa.stream_read(buf, g, sink)
+            pa.stream_read(buf, g, sink, depth=depth)
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record()
         for _ in range(launches):
-            pa.stream_read(buf, g, sink)
+            pa.stream_read(buf, g, sink, depth=depth)
         t1.record()
         torch.cuda.synchronize()
         gbs = n / (t0.elapsed_time(t1) / launches * 1e-3) / 1e9
         if best is None or gbs > best[0]:
-            best = (gbs, g)
+            best = (gbs, g, depth)
     del buf, sink
     torch.cuda.empty_cache()
-    return {"GBps": round(best[0], 2), "grid": best[1], "bytes": n, "launches": launches}
+    return {"GBps": round(best[0], 2), "grid": best[1], "loads_in_flight_per_thread": best[2], "bytes": n,
+            "launches": launches}
 
 
 def _kernel_times(fn, steps):

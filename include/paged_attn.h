@@ -398,16 +398,18 @@ int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *com
 
 /*
  * attn_stream_read -- measurement utility: read `bytes` of device memory at
- * `buf` once with 16-byte loads (grid-stride loop, `grid` workgroups of 256
- * threads) and nothing else, asynchronously on `stream`.  The rate it
- * reaches is the on-box ceiling of a plain HBM read stream, the practical
- * denominator beside the 8 TB/s peak for the HBM-bound attention kernels.
- * sink: device uint32 [grid * 256], overwritten (each thread's XOR of what
- * it read, so no load can be elided).  buf 16-byte aligned, bytes a multiple
- * of 16, 1 <= grid <= 65535; errors: ATTN_ERR_NULL, ATTN_ERR_ALIGN,
- * ATTN_ERR_SHAPE, ATTN_ERR_HIP.  Caller-owned memory; nothing is allocated.
+ * `buf` once with 16-byte non-temporal loads (grid-stride loop, `grid`
+ * workgroups of 256 threads, `depth` = 4 or 8 loads in flight per thread)
+ * and nothing else, asynchronously on `stream`.  The best rate over a few
+ * grid sizes and depths is the on-box ceiling of a plain HBM read stream,
+ * the practical denominator beside the 8 TB/s peak for the HBM-bound
+ * attention kernels.  sink: device uint32 [grid * 256], overwritten (each
+ * thread's XOR of what it read, so no load can be elided).  buf 16-byte
+ * aligned, bytes a multiple of 16, 1 <= grid <= 65535; errors:
+ * ATTN_ERR_NULL, ATTN_ERR_ALIGN, ATTN_ERR_SHAPE, ATTN_ERR_HIP.  Caller-owned
+ * memory; nothing is allocated.
  */
-int attn_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, void *stream);
+int attn_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, int32_t depth, void *stream);
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char *attn_status_string(int status);

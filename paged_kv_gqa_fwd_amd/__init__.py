@@ -157,7 +157,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     dp, ip = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)
     lib.attn_kernel_timing_read.argtypes = [dp, ip, dp, ip, dp, ip]
     lib.attn_kernel_timing_read.restype = ctypes.c_int
-    lib.attn_stream_read.argtypes = [p, sz, p, i32, p]
+    lib.attn_stream_read.argtypes = [p, sz, p, i32, i32, p]
     lib.attn_stream_read.restype = ctypes.c_int
     qd_p = ctypes.POINTER(attn_quant_dims)
     lib.attn_quant_layout_of.argtypes = [qd_p, ctypes.POINTER(attn_quant_layout)]
@@ -404,7 +404,7 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
 
 
 def stream_read(buf: torch.Tensor, grid: int = 512, sink: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                stream: Optional[torch.cuda.Stream] = None, depth: int = 4) -> torch.Tensor:
     """Read the bytes of a contiguous GPU tensor once through
     ``attn_stream_read`` (the plain HBM read stream used as the on-box read
     ceiling).  Returns the sink (uint32 [grid * 256], overwritten)."""
@@ -417,7 +417,8 @@ def stream_read(buf: torch.Tensor, grid: int = 512, sink: Optional[torch.Tensor]
     if sink.numel() < grid * 256 or not sink.is_cuda:
         raise ValueError("sink must be a GPU tensor of at least grid * 256 int32")
     st = stream if stream is not None else torch.cuda.current_stream(buf.device)
-    rc = lib.attn_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), int(grid), ctypes.c_void_p(st.cuda_stream))
+    rc = lib.attn_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), int(grid), int(depth),
+                              ctypes.c_void_p(st.cuda_stream))
     if rc != ATTN_OK:
         raise AttnError(rc)
     return sink

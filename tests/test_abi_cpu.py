@@ -413,11 +413,12 @@ def test_quant_calls_validate_before_launch(pa):
 
 def test_stream_read_validation(pa):
     lib = pa.load_library()
-    assert lib.attn_stream_read(None, 16, FAKE, 1, None) == E_NULL
-    assert lib.attn_stream_read(FAKE, 16, None, 1, None) == E_NULL
-    assert lib.attn_stream_read(FAKE + 8, 16, FAKE, 1, None) == E_ALIGN     # buffer not 16-byte aligned
-    assert lib.attn_stream_read(FAKE, 24, FAKE, 1, None) == E_ALIGN         # not a multiple of 16 bytes
-    assert lib.attn_stream_read(FAKE, 16, FAKE + 2, 1, None) == E_ALIGN     # sink not 4-byte aligned
-    assert lib.attn_stream_read(FAKE, 16, FAKE, 0, None) == E_SHAPE
-    assert lib.attn_stream_read(FAKE, 16, FAKE, 65536, None) == E_SHAPE
-    assert lib.attn_stream_read(FAKE, 0, FAKE, 1, None) == OK               # nothing to read: no launch
+    assert lib.attn_stream_read(None, 16, FAKE, 1, 4, None) == E_NULL
+    assert lib.attn_stream_read(FAKE, 16, None, 1, 4, None) == E_NULL
+    assert lib.attn_stream_read(FAKE + 8, 16, FAKE, 1, 4, None) == E_ALIGN     # buffer not 16-byte aligned
+    assert lib.attn_stream_read(FAKE, 24, FAKE, 1, 4, None) == E_ALIGN         # not a multiple of 16 bytes
+    assert lib.attn_stream_read(FAKE, 16, FAKE + 2, 1, 4, None) == E_ALIGN     # sink not 4-byte aligned
+    assert lib.attn_stream_read(FAKE, 16, FAKE, 0, 4, None) == E_SHAPE
+    assert lib.attn_stream_read(FAKE, 16, FAKE, 65536, 4, None) == E_SHAPE
+    assert lib.attn_stream_read(FAKE, 16, FAKE, 1, 6, None) == E_SHAPE        # depth 4 or 8
+    assert lib.attn_stream_read(FAKE, 0, FAKE, 1, 8, None) == OK               # nothing to read: no launch

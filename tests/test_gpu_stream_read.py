@@ -17,13 +17,14 @@ def _gpu_ready():
     pa.load_library()
 
 
+@pytest.mark.parametrize("depth", [4, 8])
 @pytest.mark.parametrize("n_words,grid", [(4, 1), (4 * 1000 + 4, 3), (1 << 20, 512), ((1 << 22) + 12, 2048)])
-def test_every_chunk_read_once(n_words, grid):
+def test_every_chunk_read_once(n_words, grid, depth):
     import paged_kv_gqa_fwd_amd as pa
     g = torch.Generator().manual_seed(n_words)
     host = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_words,), dtype=torch.int64, generator=g).to(torch.int32)
     buf = host.cuda()
-    sink = pa.stream_read(buf, grid)
+    sink = pa.stream_read(buf, grid, depth=depth)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink[: grid * 256].cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
