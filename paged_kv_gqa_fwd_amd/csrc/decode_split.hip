@@ -9,13 +9,15 @@
 // with its i32 counter scratch (ops.decode.impl.scratch.counter), by the
 // last workgroup of each (sequence, KV head) to finish its split.
 //
-// Design (MI355X): one workgroup of 4 wave64 per (KV head, sequence, split).
-// The split's pages stream through LDS with 16-byte coalesced loads, staged
-// in registers two pages ahead.  The G q heads x n query tokens of the KV
-// head (<= 16 rows) form the N side of the MFMA and the keys the M side
-// ("swap AB"), so the score tile's C layout is directly the B operand of the
-// P.V MFMA.  Each wave owns 16 keys of every page and keeps its own online
-// softmax state; the four waves merge in LDS at the end.
+// Design (MI355X): one workgroup of 4 wave64 per (KV head, split); the
+// splits are either fixed runs of pages of one sequence or, by default,
+// equal ranges of the whole batch's pages (the balanced kernel below).  The
+// pages stream through LDS with 16-byte coalesced non-temporal loads, staged
+// in registers one or two pages ahead.  The G q heads x n query tokens of
+// the KV head (<= 16 rows) form the N side of the MFMA and the keys the M
+// side ("swap AB"), so the score tile's C layout is directly the B operand
+// of the P.V MFMA.  Each wave owns 16 keys of every page and keeps its own
+// online softmax state; the four waves merge in LDS at the end.
 #include "attn_device.h"
 
 namespace pa {
@@ -75,24 +77,6 @@ __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_P
         const int key = c / (2 * C::DC);
         const char *src = head_base + (page_off + (int64_t)key * kv_ss + kv * kv_skv) * C::EB + dc * 16;
         stage[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
-    }
-}
-
-// The same loads, issued only for slots before `valid` (the rest stage as
-// zeros); the count of loads issued then depends on the data.
-template <int D, bool F8>
-__device__ __forceinline__ void load_page_valid(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
-                                                const char *head_base, int64_t page_off,
-                                                int64_t kv_ss, int64_t kv_skv, int tid, int valid) {
-    using C = DecodeCfg<D, F8>;
-#pragma unroll
-    for (int it = 0; it < C::CH_PER_THREAD; ++it) {
-        const int c = it * kThreads + tid;
-        const int dc = c % C::DC;
-        const int kv = (c / C::DC) & 1;
-        const int key = c / (2 * C::DC);
-        const char *src = head_base + (page_off + (int64_t)key * kv_ss + kv * kv_skv) * C::EB + dc * 16;
-        stage[it] = key < valid ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
