@@ -30,7 +30,10 @@
 //    this replaced spent half of its LDS cycles in conflicts).
 //  * The 32-key steps are software pipelined: the P.V MFMAs of step j-1
 //    run while the VALU takes the row max of step j, and the Q.K MFMAs of
-//    step j+1 run while the VALU exponentiates step j.
+//    step j+1 run while the VALU exponentiates step j.  The first LDS
+//    operands of each MFMA block are read during the block before it, and
+//    the one workgroup barrier per page sits after the Q.K block of the
+//    page's first step, so no block opens on an LDS round trip.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with keys on M: each lane owns
 //    one query row per block, so row max / row sum are in-lane plus one
 //    permlane32 swap.  The S^T C layout is directly the B operand of
@@ -300,6 +303,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         }
     };
 
+    // The first PF operands of a section are read during the section before
+    // it, so that neither MFMA block starts on an LDS round trip.
+    bf16x8 vcar[PF], kcar[PF];
     bf16x8 pb[C::RB][2];
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) pb[rb][0] = pb[rb][1] = bf16x8{};
@@ -325,10 +331,13 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const uint16_t *vt = vstage(j > j0 ? j - 1 : j0);
             bf16x8 vop[PF + 1];
 #pragma unroll
-            for (int k = 0; k < PF; ++k) vop[k] = vread(vt, k);
+            for (int k = 0; k < PF; ++k) vop[k] = vcar[k];
 #pragma unroll
             for (int k = 0; k < NPV; ++k) {
-                if (k + PF < NPV) vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
+                if (k + PF < NPV)
+                    vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
+                else
+                    kcar[k + PF - NPV] = kread(kstage(j + 1), k + PF - NPV);   // B(j)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
@@ -363,17 +372,6 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 for (int i = 0; i < D / 32; ++i) oacc[rb][i] *= alpha[rb];
             }
         }
-        // ---- page boundary: publish page t+1, refill with page t+1+LEAD
-        const int t = j >> 1;
-        if ((j & 1) && t + 1 < ntiles) {
-            wait_page(t + 1);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            if (t + 1 + C::LEAD < ntiles) {
-                issue_page(t + 1 + C::LEAD);
-                issued = t + 1 + C::LEAD;
-            }
-        }
         // ---- B(j): S_{j+1} = K_{j+1} Q^T on the MFMA pipe, two K operands
         // ahead, with P_j = exp2(S_j scale - m) on the VALU.  After the last
         // step the product reads a stale stage (in bounds) and is discarded.
@@ -381,7 +379,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const uint16_t *kp = kstage(j + 1);
             bf16x8 kop[PF + 1];
 #pragma unroll
-            for (int k = 0; k < PF; ++k) kop[k] = kread(kp, k);
+            for (int k = 0; k < PF; ++k) kop[k] = kcar[k];
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb) snext[rb] = f32x16{};
             float pf[NEL];
@@ -390,7 +388,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int rb = 0; rb < C::RB; ++rb) psum[rb] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                if (ks + PF < NKS) kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
+                if (ks + PF < NKS)
+                    kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
+                else
+                    vcar[ks + PF - NKS] = vread(vstage(j), ks + PF - NKS);   // A(j+1)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
@@ -424,6 +425,20 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 asm volatile("" ::"v"(pb[rb][0]), "v"(pb[rb][1]), "v"(l_part[rb]));
             }
         }
+        // ---- page boundary after B(2t): publish page t+1 (first read by
+        // A(2t+1)'s look-ahead into B(2t+1)'s K operands), then refill the
+        // slots of K page t (last read by B(2t)) and V page t-1 (last read
+        // by A(2t)) with page t+1+LEAD.
+        const int t = j >> 1;
+        if (!(j & 1) && t + 1 < ntiles) {
+            wait_page(t + 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            if (t + 1 + C::LEAD < ntiles) {
+                issue_page(t + 1 + C::LEAD);
+                issued = t + 1 + C::LEAD;
+            }
+        }
     };
 
     f32x16 sA[C::RB], sB[C::RB];
@@ -431,6 +446,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         wait_page(t0);
         __builtin_amdgcn_s_barrier();
         qk(j0, sA);
+#pragma unroll
+        for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
         // Two steps per page; the S registers alternate roles between them.
         for (int t = t0; t < ntiles; ++t) {
             step(2 * t, sA, sB);
