@@ -12,7 +12,9 @@
  *     out[t, h, :] = sum_j softmax_j(scale * <q[t, h, :], K_j>) * V_j
  *
  * Key j lives in page block_table[b, j / P], slot j % P of the pool.  Rows
- * with no visible key are written as zeros.
+ * with no visible key are written as zeros.  The slots of a sequence's last
+ * page past L_b, and pages its table does not name, may hold any bits
+ * (NaN and infinities included): none reaches the result.
  *   - Scaled dot-product attention over a paged KV cache, causal or unmasked,
  *     with ragged lengths and grouped q heads: Mojo SM100MHA2Q API docs
  *     (struct summary; parameters KVLUTType, MaskType, ValidLengthType,
