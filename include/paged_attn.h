@@ -69,8 +69,8 @@ typedef struct attn_paged_dims {
     int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0, G = Hq / Hkv */
     int32_t head_dim;          /* D: 128 or 256 */
     int32_t page_size;         /* P: 64 (slots per page) */
-    int32_t num_pages;         /* NP: pages in the pool (valid ids are [0, NP)) */
-    int32_t max_pages_per_seq; /* MP: block-table columns; every L_b <= MP * P */
+    int32_t num_pages;         /* NP >= 1: pages in the pool (valid ids are [0, NP)) */
+    int32_t max_pages_per_seq; /* MP >= 1: block-table columns; every L_b <= MP * P */
     int64_t num_tokens;        /* rows of q and out (>= cu_q[n_seqs]) */
     int64_t q_stride_token;    /* q[t, h, d] at q + t*q_stride_token + h*q_stride_head + d */
     int64_t q_stride_head;
