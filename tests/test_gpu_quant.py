@@ -96,6 +96,28 @@ def test_quant_prep_and_attention(oracle_mod, name, B, N, H, causal, scale, koff
     _compare(out, ref, name)
 
 
+def test_quant_random_shapes(oracle_mod):
+    """Seeded random shapes: batch 1-2, 1-800 tokens (single tokens, partial
+    64-token tiles), 1-4 heads, causal or not, scale sign and size, K channel
+    offsets; preparation bit-exact and attention within the quantised bar."""
+    import random
+    import paged_kv_gqa_fwd_amd as pa
+    rng = random.Random(4711)
+    for i in range(12):
+        B, N, H = rng.randint(1, 2), rng.choice([1, 2, 63, 65, rng.randint(3, 800)]), rng.randint(1, 4)
+        causal = rng.random() < 0.5
+        scale = rng.choice([1.0, -1.0]) * rng.uniform(0.02, 0.2)
+        koff = rng.choice([0.0, 2.0])
+        name = "random %d: B=%d N=%d H=%d causal=%d scale=%.3f koff=%.0f" % (i, B, N, H, causal, scale, koff)
+        q, k, v = workloads.dense_qkv(5000 + i, B, N, H, k_channel_offset_var=koff, device="cuda")
+        prep = _check_prep(q, k, v, oracle_mod, name)
+        ref = oracle_mod.quant_attn(prep, scale, causal)
+        log("  gpu quant attention: %s" % name)
+        out = pa.quant_attention(q, k, v, scale, causal)
+        torch.cuda.synchronize()
+        _compare(out, ref, name)
+
+
 def test_quant_strided_inputs(oracle_mod):
     """q/k/v as strided views (K and V interleaved, as in a paged pool), out
     with a padded head stride."""
