@@ -33,7 +33,10 @@
 //    step j+1 run while the VALU exponentiates step j.  The first LDS
 //    operands of each MFMA block are read during the block before it, and
 //    the one workgroup barrier per page sits after the Q.K block of the
-//    page's first step, so no block opens on an LDS round trip.
+//    page's first step, so no block opens on an LDS round trip.  At D = 256
+//    (one page of lead) the barrier waits for the next page's K rows only:
+//    its V rows, first read a page later, are issued after them, spread over
+//    the steps between two barriers.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with keys on M: each lane owns
 //    one query row per block, so row max / row sum are in-lane plus one
 //    permlane32 swap.  The S^T C layout is directly the B operand of
@@ -69,6 +72,12 @@ struct PfCfg {
     static constexpr int LEAD = D == 128 ? 2 : 1;
     static constexpr int NK = LEAD + 1;
     static constexpr int NV = LEAD + 2;
+    // D = 256 (one page of lead): a page's V rows are first read a page
+    // after its K rows, so the refill issues K at the page barrier and
+    // spreads V over the next two steps (VPH loads per MFMA phase); the
+    // barrier then waits for K only.
+    static constexpr bool SPLITV = D == 256;
+    static constexpr int VPH = LOADS / 4;
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
@@ -107,6 +116,29 @@ __device__ __forceinline__ void pf_load_page(uint16_t *lds_k, uint16_t *lds_v, c
         const int slot = (i * C::THREADS + w * 64) * 8;   // wave-uniform LDS element offset
         dma16(lds_address(lds_k + slot), page_base, ok ? pl.kof[i] : pl.kof0[i]);
         dma16(lds_address(lds_v + slot), vbase, ok ? pl.vof[i] : pl.vof0[i]);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void pf_load_k(uint16_t *lds_k, const uint16_t *page_base, const PageLoad<D> &pl,
+                                          int w, int valid) {
+    using C = PfCfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int slot = (i * C::THREADS + w * 64) * 8;
+        dma16(lds_address(lds_k + slot), page_base, pl.key[i] < valid ? pl.kof[i] : pl.kof0[i]);
+    }
+}
+
+// V loads i0 .. i0+N-1 of a page (vbase = the page's V rows).
+template <int D, int N>
+__device__ __forceinline__ void pf_load_v(uint16_t *lds_v, const uint16_t *vbase, const PageLoad<D> &pl, int w,
+                                          int valid, int i0) {
+    using C = PfCfg<D>;
+#pragma unroll
+    for (int i = i0; i < i0 + N; ++i) {
+        const int slot = (i * C::THREADS + w * 64) * 8;
+        dma16(lds_address(lds_v + slot), vbase, pl.key[i] < valid ? pl.vof[i] : pl.vof0[i]);
     }
 }
 
@@ -203,8 +235,23 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     }
     auto issue_page = [&](int t) {
         const int pid = load_page_id(bt_row, t);
-        pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, pl,
-                        a.kv_skv, w, L - t * kPage);
+        if constexpr (C::SPLITV) {   // all of K, then all of V
+            pf_load_k<D>(sk[t % C::NK], head_base + (int64_t)pid * a.kv_sp, pl, w, L - t * kPage);
+            pf_load_v<D, C::LOADS>(sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w,
+                                   L - t * kPage, 0);
+        } else {
+            pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, pl,
+                            a.kv_skv, w, L - t * kPage);
+        }
+    };
+    // SPLITV: the page whose V rows are being issued over the two steps
+    // after its K rows (part q of 4 during phase q of those steps).
+    const uint16_t *vp_base = head_base;
+    uint16_t *vp_slot = sv[0];
+    int vp_valid = 0;
+    bool vp_on = false;
+    auto issue_v_part = [&](int q) {
+        if (C::SPLITV && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, vp_valid, q * C::VPH);
     };
     // Wait until page t has landed in LDS: pages t+1 .. `issued` were
     // issued after it and may stay in flight (loads complete in issue order).
@@ -331,9 +378,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const uint16_t *vt = vstage(j > j0 ? j - 1 : j0);
             bf16x8 vop[PF + 1];
 #pragma unroll
-            for (int k = 0; k < PF; ++k) vop[k] = vcar[k];
+            for (int k = 0; k < PF; ++k) vop[k] = C::SPLITV ? vread(vt, k) : vcar[k];
 #pragma unroll
             for (int k = 0; k < NPV; ++k) {
+                if (k == NPV / 2) issue_v_part(2 * (1 - (j & 1)));   // A(2t+1): part 0, A(2t+2): part 2
                 if (k + PF < NPV)
                     vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
                 else
@@ -388,9 +436,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int rb = 0; rb < C::RB; ++rb) psum[rb] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
+                if (ks == NKS / 2) issue_v_part(2 * (1 - (j & 1)) + 1);   // B(2t+1): part 1, B(2t+2): part 3
                 if (ks + PF < NKS)
                     kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
-                else
+                else if constexpr (!C::SPLITV)
                     vcar[ks + PF - NKS] = vread(vstage(j), ks + PF - NKS);   // A(j+1)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
@@ -430,7 +479,30 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         // slots of K page t (last read by B(2t)) and V page t-1 (last read
         // by A(2t)) with page t+1+LEAD.
         const int t = j >> 1;
-        if (!(j & 1) && t + 1 < ntiles) {
+        if constexpr (C::SPLITV) {
+            // K page t+1 has landed (only V page t+1, issued after it, may
+            // be in flight; its first reader is A(2t+3), after the next
+            // barrier); the refill issues K page t+2 now and its V over the
+            // next two steps.  After the last page's first step every load
+            // is waited for (its V rows are read next).
+            if (!(j & 1)) {
+                if (t + 1 < ntiles)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                vp_on = t + 2 < ntiles;
+                if (vp_on) {
+                    const int pid = load_page_id(bt_row, t + 2);
+                    const uint16_t *pb2 = head_base + (int64_t)pid * a.kv_sp;
+                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
+                    vp_base = pb2 + a.kv_skv;
+                    vp_slot = sv[(t + 2) % C::NV];
+                    vp_valid = L - (t + 2) * kPage;
+                }
+            }
+        } else if (!(j & 1) && t + 1 < ntiles) {
             wait_page(t + 1);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -446,8 +518,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         wait_page(t0);
         __builtin_amdgcn_s_barrier();
         qk(j0, sA);
+        if constexpr (!C::SPLITV)
 #pragma unroll
-        for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
+            for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
         // Two steps per page; the S registers alternate roles between them.
         for (int t = t0; t < ntiles; ++t) {
             step(2 * t, sA, sB);
