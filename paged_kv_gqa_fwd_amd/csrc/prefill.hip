@@ -33,7 +33,9 @@
 //    step j+1 run while the VALU exponentiates step j.  The first LDS
 //    operands of each MFMA block are read during the block before it, and
 //    the one workgroup barrier per page sits after the Q.K block of the
-//    page's first step, so no block opens on an LDS round trip.  At D = 256
+//    page's first step, so no block opens on an LDS round trip; the first
+//    Q.K MFMA of a step goes out before the row-max reduction and rescale
+//    that separate the two blocks.  At D = 256
 //    (one page of lead) the barrier waits for the next page's K rows only:
 //    its V rows, first read a page later, are issued after them, spread over
 //    the steps between two barriers.
@@ -399,6 +401,12 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 }
             }
         }
+        // B(j)'s first Q.K MFMA (its operand was read during A(j)) goes to the
+        // matrix unit now, overlapping the row-max reduction and rescale below.
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb)
+            snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcar[0], qreg[rb][0], f32x16{}, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         float alpha[C::RB], m_use[C::RB];
         bool any_upd = false;
 #pragma unroll
@@ -428,8 +436,6 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             bf16x8 kop[PF + 1];
 #pragma unroll
             for (int k = 0; k < PF; ++k) kop[k] = kcar[k];
-#pragma unroll
-            for (int rb = 0; rb < C::RB; ++rb) snext[rb] = f32x16{};
             float pf[NEL];
             float psum[C::RB];
 #pragma unroll
@@ -444,7 +450,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 // one MFMA, then its share of the VALU work
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
-                    snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % (PF + 1)], qreg[rb][ks], snext[rb], 0, 0, 0);
+                    if (ks > 0)
+                        snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % (PF + 1)], qreg[rb][ks], snext[rb], 0, 0, 0);
                     constexpr int EH = EB / C::RB;
 #pragma unroll
                     for (int e = (ks * C::RB + rb) * EH; e < (ks * C::RB + rb + 1) * EH; ++e) {
