@@ -425,7 +425,7 @@ def main():
                          "sustains on real data, as context for the prefill and quantised rooflines")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
