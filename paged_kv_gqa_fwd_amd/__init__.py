@@ -217,10 +217,10 @@ def make_plan(dims: attn_paged_dims, n_seqs: int, max_q: int, path: int = PATH_A
 
 
 class _CachedWorkspace:
-    """One device workspace per device, grown on demand.  `clean` counts the
-    leading bytes known to be zero: the fused split path needs its counter
-    bytes zero on entry and leaves them zero, while partials written by any
-    split call dirty everything past that call's counter bytes."""
+    """One workspace per (device, stream), grown on demand.  `clean` counts
+    the leading bytes known to be zero: the fused split path needs its
+    counter bytes zero on entry and leaves them zero, while partials written
+    by any split call dirty everything past that call's counter bytes."""
 
     def __init__(self):
         self.buf = None
@@ -230,11 +230,19 @@ class _CachedWorkspace:
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device) -> _CachedWorkspace:
-    key = (str(device),)
+def _workspace(nbytes: int, device, stream: torch.cuda.Stream) -> _CachedWorkspace:
+    """The cached workspace of `stream`.  Calls on one stream run in order, so
+    they may share it; each stream has its own, so that calls on different
+    streams never overwrite each other's partials.  A grown buffer is
+    allocated with `stream` current: the caching allocator then hands the
+    old one to later allocations only in that stream's order, after the
+    kernels already queued on it."""
+    key = (str(device), int(stream.cuda_stream))
     ws = _ws_cache.setdefault(key, _CachedWorkspace())
     if ws.buf is None or ws.buf.numel() < nbytes:
-        ws.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws.buf = None
+        with torch.cuda.stream(stream):
+            ws.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         ws.clean = ws.buf.numel()
     return ws
 
@@ -304,7 +312,7 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     if plan.workspace_bytes:
         if workspace is None:
-            cached = _workspace(plan.workspace_bytes, q.device)
+            cached = _workspace(plan.workspace_bytes, q.device, st)
             workspace = cached.buf
             if cached.clean < plan.counter_bytes:
                 workspace_clear(workspace, plan.counter_bytes, st)
@@ -387,7 +395,7 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     ws_ptr, ws_bytes, cached = None, 0, None
     if plan.workspace_bytes:
-        cached = _workspace(plan.workspace_bytes, q.device)
+        cached = _workspace(plan.workspace_bytes, q.device, st)
         if cached.clean < plan.counter_bytes:
             workspace_clear(cached.buf, plan.counter_bytes, st)
         ws_ptr, ws_bytes = cached.buf.data_ptr(), cached.buf.numel()
@@ -519,11 +527,11 @@ def quant_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: fl
     _check_device_tensor("out", out, torch.bfloat16)
     dims = make_quant_dims(q, k, v, out)
     lay = quant_layout(dims)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     if workspace is None:
-        cached = _workspace(lay.workspace_bytes, q.device)
+        cached = _workspace(lay.workspace_bytes, q.device, st)
         cached.clean = 0   # the quantised intermediates overwrite it
         workspace = cached.buf
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     rc = lib.attn_quant_fwd(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             ctypes.byref(dims), float(scale), int(bool(causal)), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), ctypes.c_void_p(st.cuda_stream))

@@ -177,6 +177,10 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
                                     align_up(rows * 8, kWsAlign);
         }
     } else {
+        // The prefill kernel addresses a page's K/V rows with 32-bit byte
+        // offsets from the page's base (one VGPR per direct-to-LDS load):
+        // 63 slot strides plus one row must stay below 4 GiB.
+        if ((63 * d->kv_stride_slot + d->head_dim) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
         const int64_t bm = pa::prefill_rows(d->head_dim);
         const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;

@@ -85,3 +85,12 @@ def sub_case_rows(case, seq_ids):
         seq_lens=torch.tensor(kv_lens, dtype=torch.int32), cu_q=torch.tensor(cu_new, dtype=torch.int32),
         q_lens=q_lens, kv_lens=kv_lens)
     return sub, q_rows
+
+
+def dit_sample_rows(n_tokens: int, seed: int = 5) -> np.ndarray:
+    """A seeded sample of one in sixteen token rows of the DiT shape (random
+    rows plus both ends and the 64- and 256-row tile boundaries)."""
+    k = -(-n_tokens // 16)
+    pick = set(torch.randperm(n_tokens, generator=torch.Generator().manual_seed(seed))[:k].tolist())
+    pick |= {0, 1, 63, 64, 127, 128, 255, 256, n_tokens - 51, n_tokens - 50, n_tokens - 1}
+    return np.array(sorted(pick), dtype=np.int64)

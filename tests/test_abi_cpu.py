@@ -177,6 +177,34 @@ def test_plan_paths_and_sizes(pa):
     assert p5.path == mod.PATH_SPLIT_DECODE and p5.grid_z * 2 * 128 >= 4 * 256
 
 
+def test_prefill_rejects_slot_strides_past_32_bit_offsets(pa):
+    """The prefill kernel addresses the 64 slots of a page with 32-bit byte
+    offsets from the page base: a slot stride with (63 * stride + D) * 2 past
+    2^32 - 1 is refused on that path (nothing launched), while the split-decode
+    paths (64-bit addressing) still plan it.  A slot-outermost pool over many
+    pages is such a layout."""
+    import paged_kv_gqa_fwd_amd as mod
+    D, hkv, hq = 128, 8, 32
+    limit = ((1 << 32) - 1) // 2            # (63 s + D) <= limit elements
+    s_ok = (limit - D) // 63 // 8 * 8       # largest multiple of 8 that fits
+    s_bad = s_ok + 8
+    assert (63 * s_ok + D) * 2 <= (1 << 32) - 1 < (63 * s_bad + D) * 2
+    for s, expect in ((s_ok, OK), (s_bad, E_UNSUP)):
+        d = dims(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_stride_slot=s, kv_stride_page=8,
+                 kv_stride_head=2 * D, kv_stride_kv=D, num_tokens=4096)
+        plan = mod.attn_paged_plan()
+        opt = mod.attn_paged_options(None, 0, mod.PATH_PREFILL, 0, 0, 1.0, 1.0)
+        rc = pa.load_library().attn_paged_make_plan_opt(ctypes.byref(d), 4, 64, ctypes.byref(opt),
+                                                       ctypes.byref(plan))
+        assert rc == expect, (s, rc)
+        if expect != OK:
+            # AUTO takes prefill for 64 rows x G 4 > 16: the call is refused
+            # before any launch
+            assert call(pa, d, n_seqs=4, max_q=64) == E_UNSUP
+        # decode-shaped calls keep their 64-bit split path
+        assert mod.make_plan(d, 4, 1).path == mod.PATH_SPLIT_BALANCED
+
+
 def test_plan_balanced(pa):
     import paged_kv_gqa_fwd_amd as mod
     d = dims(max_pages_per_seq=128, bt_stride=128)        # 32/8 heads, D 128

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads
-from parity_util import log
+from parity_util import dit_sample_rows, log
 
 pytestmark = pytest.mark.gpu
 
@@ -135,10 +135,11 @@ def test_quant_strided_inputs(oracle_mod):
     assert not big[:, :, 0].any() and not big[:, :, :, 128:].any()
 
 
-def test_quant_dit_full_size_sampled(oracle_mod):
+def test_quant_dit_full_size_sampled_1in16(oracle_mod):
     """The full video-DiT shape [1, 37810, 56, 128] (non-causal, K channel
     offsets), in the benchmark's launch configuration: preparation checked
-    bit-exactly in full, attention on sampled query tokens."""
+    bit-exactly in full, attention on a seeded sample of one in sixteen query
+    tokens (all 56 heads each) against the emulating oracle."""
     import paged_kv_gqa_fwd_amd as pa
     case = workloads.dit_self_attn(device="cuda")
     q, k, v = workloads.dense_from_case(case)
@@ -147,14 +148,16 @@ def test_quant_dit_full_size_sampled(oracle_mod):
     out = pa.quant_attention(q, k, v, case.scale, False)
     torch.cuda.synchronize()
     N = q.shape[1]
-    rows = sorted({0, 1, 63, 64, 127, 128, N - 51, N - 50, N - 1} |
-                  set(torch.randint(0, N, (7,), generator=torch.Generator().manual_seed(5)).tolist()))
+    rows = dit_sample_rows(N)
     mask = np.zeros(N, dtype=np.uint8)
     mask[rows] = 1
-    ref = oracle_mod.quant_attn(prep, case.scale, False, row_mask=mask)
-    _compare(out, ref, "dit full, %d sampled tokens" % len(rows), rows=np.array(rows))
+    got = out[:, torch.from_numpy(rows).cuda()].cpu()
+    scale = case.scale
     del case, q, k, v, out
     torch.cuda.empty_cache()
+    log("  quantised oracle over %d sampled tokens" % rows.size)
+    ref = oracle_mod.quant_attn(prep, scale, False, row_mask=mask)
+    _compare(got, ref[:, rows], "dit full, %d sampled tokens (1 in 16)" % rows.size)
 
 
 def test_quant_run_to_run_bitwise():

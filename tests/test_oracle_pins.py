@@ -297,3 +297,73 @@ def test_head_major_layout_is_same_attention(oracle_mod):
     b = oracle_mod.paged_attn(case.q, case.kv.contiguous(), case.block_table, case.seq_lens, case.cu_q,
                               case.scale, True)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------ dense (matmul) form of the oracle
+DENSE_CASES = SMALL_CASES + [
+    dict(q_lens=[0, 33, 1, 130], kv_lens=[0, 200, 64, 300], hq=24, hkv=4, d=256, causal=True),
+    dict(q_lens=[50], kv_lens=[50], hq=8, hkv=8, d=128, causal=False),
+    dict(q_lens=[9, 3], kv_lens=[0, 2], hq=8, hkv=1, d=128, causal=True),   # L = 0 and n > L rows
+]
+
+
+@pytest.mark.parametrize("idx", range(len(DENSE_CASES)))
+def test_dense_form_matches_c_oracle(oracle_mod, idx):
+    """The matmul form (oracle/dense.py) against the C loop: two independent
+    implementations of the definition agree to fp64 rounding on every row,
+    also over a poisoned pool (unused pages and slots past L never read)."""
+    from oracle import dense
+    c = DENSE_CASES[idx]
+    case = workloads.make_case("dense", 2000 + idx, c["q_lens"], c["kv_lens"], c["hq"], c["hkv"], c["d"],
+                               causal=c["causal"], extra_pages=2, poison=True)
+    ref = run_oracle(oracle_mod, case)
+    rows, got = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                      case.scale, case.causal)
+    assert np.array_equal(rows, np.arange(sum(c["q_lens"])))
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    # a row subset gives the same rows (to rounding: its products are shaped differently)
+    pick = rows[::3]
+    r2, g2 = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                   case.scale, case.causal, rows=pick[::-1])
+    assert np.array_equal(r2, pick)
+    np.testing.assert_allclose(g2, got[pick], rtol=0, atol=1e-13)
+
+
+def test_dense_form_chunked_rows_and_two_layer_pool(oracle_mod):
+    """Row chunks (a tiny score budget) and the manifest's two-layer pool view
+    change nothing."""
+    from oracle import dense
+    case = workloads.tiny_mixed()
+    ref = run_oracle(oracle_mod, case)
+    _, a = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                 case.scale, case.causal)
+    _, b = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                 case.scale, case.causal, max_scores=1000)
+    np.testing.assert_allclose(a, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-13)
+
+
+def test_dense_form_closed_forms():
+    """Closed forms: a single visible key gives its V row exactly; constant V
+    gives that row; scale 0 gives the mean of the visible V rows."""
+    from oracle import dense
+    case = workloads.make_case("onek", 6, [4, 1], [4, 1], 4, 2, 16, causal=True)
+    _, got = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                   case.scale, True)
+    for b, t in ((0, 0), (1, 4)):
+        pg = int(case.block_table[b, 0])
+        for h in range(4):
+            assert np.array_equal(got[t, h], case.kv[pg, 0, h // 2, 1, :].double().numpy())
+    case = workloads.make_case("cv", 5, [3, 1], [100, 300], 8, 2, 32, causal=True)
+    row = torch.randn(32, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    case.kv[:, :, :, 1, :] = row
+    _, got = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q,
+                                   case.scale, True)
+    np.testing.assert_allclose(got, np.broadcast_to(row.double().numpy(), got.shape), rtol=0, atol=1e-13)
+    case = workloads.make_case("s0", 8, [5], [70], 4, 1, 16, causal=True)
+    _, got = dense.paged_attn_rows(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, 0.0, True)
+    dk = _dense_kv(case)[0][1][:, 0, :]     # V rows [L, D]
+    for i in range(5):
+        vis = 70 - 5 + i + 1
+        np.testing.assert_allclose(got[i, 0], dk[:vis].mean(axis=0), rtol=0, atol=1e-13)

@@ -60,6 +60,41 @@ def test_e4m3_decoder_matches_torch():
 
 
 # --------------------------------------------------------------- int8 blocks
+def test_int8_codes_round_half_to_even_like_torch_round():
+    """Exact ties: blocks whose amax is 127 * 2^e have a power-of-two scale,
+    so x * (1/s) is exact and every x placed at (k + 1/2) * s is a true tie.
+    The codes must equal torch.round (half to even) plus the +-127 clamp;
+    rounding ties away from zero, or truncating, fails here.  Q is quantised
+    as it is (no smoothing), so the Q codes are checked."""
+    B, H, D = 1, 2, 128
+    N = 64 * 4
+    q = torch.zeros(B, N, H, D)
+    g = torch.Generator().manual_seed(7)
+    for blk, e in enumerate((0, -1, 1, -3)):
+        s = 2.0 ** e
+        j0 = 64 * blk
+        for h in range(H):
+            k = torch.randint(-126, 126, (64, D), generator=g).float()
+            x = (k + 0.5) * s                       # every element a tie
+            x[0, 0] = 127.0 * s                     # the block's amax: scale = s exactly
+            x[1, :8] = torch.tensor([0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, -126.5]) * s
+            q[0, j0:j0 + 64, h, :] = x
+    qb = q.to(torch.bfloat16)
+    assert torch.equal(qb.float(), q), "the ties must be exact bf16 values"
+    kz = torch.zeros_like(qb)
+    vz = torch.zeros_like(qb)
+    p = oracle.quant_prep(qb, kz, vz)
+    for blk, e in enumerate((0, -1, 1, -3)):
+        s = 2.0 ** e
+        assert p["sq"][0, :, blk].tolist() == [s] * H
+        x = q[0, 64 * blk:64 * blk + 64].permute(1, 0, 2)            # [H, 64, D]
+        want = torch.clamp(torch.round(x / s), -127, 127).to(torch.int8).numpy()
+        got = p["qi"][0, 64 * blk:64 * blk + 64].transpose(1, 0, 2)   # [H, 64, D]
+        assert np.array_equal(got, want), "block %d" % blk
+    # the hand-placed ties: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, 126.5 -> 126
+    assert p["qi"][0, 1, 0, :8].tolist() == [0, 0, 2, -2, 2, -2, 126, -126]
+
+
 def test_int8_block_error_bound_and_amax():
     B, N, H, D = 1, 200, 3, 128     # 4 blocks, the last one 8 rows
     q = _rand_bf16((B, N, H, D), 1, scale=3.0)
