@@ -240,6 +240,37 @@ int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int3
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_paged_fwd_noalloc -- attn_paged_fwd_opt for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace.  The split-KV
+ * partials (and the single-launch merge's counters) live in a library-owned
+ * device array of ATTN_NOALLOC_SCRATCH_BYTES per GPU, part of the library's
+ * code object: each GPU the library runs on holds it until the process ends.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   opt     as for attn_paged_fwd_opt, or NULL for no options (automatic
+ *           path, bf16 cache).
+ *   Every other argument as for attn_paged_fwd_opt; the caller still owns
+ *   q, out and the cache.
+ * The plan is the automatic one except that the balanced split path budgets
+ * its partials to half the array, so results can differ from
+ * attn_paged_fwd_opt's by accumulation order (within the same tolerance).
+ * A plan whose partials still exceed the array returns ATTN_ERR_WORKSPACE
+ * before anything is launched.  Merge counters are cleared by a kernel
+ * before each call that needs them (no memset node).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams or threads) race and give wrong results; calls in stream order do
+ * not.  The first call on a GPU looks up the array's device address with
+ * that GPU current (ATTN_ERR_HIP if that fails).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)   /* 64 MiB per GPU */
+
+int attn_paged_fwd_noalloc(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                           const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                           float scale, int32_t causal, const attn_paged_dims *dims,
+                           const attn_paged_options *opt, void *stream);
+
+/* ---------------------------------------------------------------------------
  * KV-cache write: the step's new K and V rows into the paged pool, the step
  * that runs just before attention (metrale blueprint graph.json: node
  * l3.attn.kv_write precedes l3.attn.attend; page layout of kern-kernels

@@ -134,6 +134,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_paged_make_plan_opt.restype = ctypes.c_int
     lib.attn_paged_fwd_opt.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, opt_p, p, sz, p]
     lib.attn_paged_fwd_opt.restype = ctypes.c_int
+    lib.attn_paged_fwd_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, i32, dims_p, opt_p, p]
+    lib.attn_paged_fwd_noalloc.restype = ctypes.c_int
     lib.attn_paged_make_plan.restype = ctypes.c_int
     lib.attn_paged_workspace_bytes.argtypes = [dims_p, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_paged_workspace_bytes.restype = ctypes.c_int
@@ -326,6 +328,40 @@ def paged_attention(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.T
         raise AttnError(rc)
     if cached is not None:
         cached.clean = plan.counter_bytes
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_noalloc(q: torch.Tensor, kv_pool: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int, scale: float,
+                            out: torch.Tensor, causal: bool = True, path: int = PATH_AUTO,
+                            pages_per_split: int = 0, stream: Optional[torch.cuda.Stream] = None,
+                            sinks: Optional[torch.Tensor] = None, window: int = 0,
+                            k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """``attn_paged_fwd_noalloc``: the paged call with no workspace; its
+    partials live in the library's per-GPU scratch array.  ``out`` must be
+    given (nothing is allocated here either).  Calls that overlap in time on
+    one GPU race on the shared scratch."""
+    lib = load_library()
+    kv_dtype = KV_FP8_E4M3 if kv_pool.dtype == torch.uint8 else KV_BF16
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv_pool", kv_pool, torch.uint8 if kv_dtype else torch.bfloat16),
+                        ("block_table", block_table, torch.int32), ("seq_lens", seq_lens, torch.int32),
+                        ("cu_q", cu_q, torch.int32), ("out", out, torch.bfloat16)):
+        _check_device_tensor(name, t, dt)
+    n_seqs = seq_lens.numel()
+    dims = make_dims(q, kv_pool, block_table, out)
+    sinks_ptr = sinks.data_ptr() if sinks is not None else None
+    opt = attn_paged_options(sinks_ptr, int(window), int(path), int(pages_per_split), kv_dtype, float(k_scale),
+                             float(v_scale))
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.attn_paged_fwd_noalloc(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(), block_table.data_ptr(),
+                                    seq_lens.data_ptr(), cu_q.data_ptr(), n_seqs, int(max_q), float(scale),
+                                    int(bool(causal)), ctypes.byref(dims), ctypes.byref(opt),
+                                    ctypes.c_void_p(st.cuda_stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc)
     return out
 
 

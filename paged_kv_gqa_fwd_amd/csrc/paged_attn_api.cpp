@@ -90,7 +90,8 @@ bool balanced_fits(const attn_paged_dims *d, int32_t n_seqs, int64_t mq, int32_t
 size_t bal_lead_bytes(int32_t n_seqs) { return align_up((size_t)std::max<int32_t>(n_seqs, 1) * 4, kWsAlign); }
 
 int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
-              int32_t pps, int32_t window, attn_paged_plan *plan, int32_t kv_dtype = ATTN_KV_BF16) {
+              int32_t pps, int32_t window, attn_paged_plan *plan, int32_t kv_dtype = ATTN_KV_BF16,
+              size_t bal_budget = kBalPartialBudget) {
     int rc = validate_dims(d, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
     if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
@@ -140,7 +141,7 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
                                             kGridYZMax);
         const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads;
         const size_t per_split = rows * ((size_t)d->head_dim + 2) * 4;
-        const int64_t s_cap = std::max<int64_t>(1, std::min<int64_t>((int64_t)(kBalPartialBudget / per_split), R));
+        const int64_t s_cap = std::max<int64_t>(1, std::min<int64_t>((int64_t)(bal_budget / per_split), R));
         int64_t c_min = (MP + s_cap - 1) / s_cap;
         c_min = std::max<int64_t>(c_min, pps);
         const int64_t S = (MP - 1) / c_min + 2;
@@ -226,8 +227,8 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
                   size_t workspace_bytes, int32_t path_hint, int32_t pps, const float *sinks,
                   int32_t window, attn_paged_plan &plan, pa::AttnArgs &a, int32_t kv_dtype = ATTN_KV_BF16,
-                  float k_scale = 1.f, float v_scale = 1.f) {
-    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan, kv_dtype);
+                  float k_scale = 1.f, float v_scale = 1.f, size_t bal_budget = kBalPartialBudget) {
+    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan, kv_dtype, bal_budget);
     if (rc != ATTN_OK) return rc;
     if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
     if (kv_dtype == ATTN_KV_BF16) k_scale = v_scale = 1.f;   // the scales belong to an fp8 cache only
@@ -549,6 +550,51 @@ int quant_attend_impl(void *out, const attn_quant_dims *d, float scale, int32_t 
     return ATTN_OK;
 }
 
+// ---- allocation-free entry point ------------------------------------------
+// The split-KV partials of attn_paged_fwd_noalloc live in this library-owned
+// device array (one copy per GPU, resident from the code object's load on
+// that GPU until the process ends).  Host code never passes the array's name
+// to a kernel: it is a host-side stand-in, not a device address.  The device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that pointer is used.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+// The balanced plan's partial budget under the scratch bound: the plan may
+// exceed its budget by two splits' worth plus the piece counts, so half the
+// scratch leaves room for that.
+constexpr size_t kScratchBalBudget = kScratchBytes / 2;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;   // per device index; null until first use
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the null stream).
+int scratch_pointer(hipStream_t stream, void **ptr) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t sd;
+        if (hipStreamGetDevice(stream, &sd) != hipSuccess) return ATTN_ERR_HIP;
+        dev = (int)sd;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return ATTN_ERR_HIP;
+    }
+    if (dev < 0) return ATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_HIP;
+        if (e != hipSuccess || !p) return ATTN_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -600,6 +646,45 @@ int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int3
     return paged_fwd_impl(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
                           workspace, workspace_bytes, stream, opt->path_hint, opt->pages_per_split, opt->sinks,
                           opt->window, opt->kv_dtype, opt->k_scale, opt->v_scale);
+}
+
+int attn_paged_fwd_noalloc(void *out, const void *q, const void *kv_pool, const int32_t *block_table,
+                           const int32_t *seq_lens, const int32_t *cu_q, int32_t n_seqs, int32_t max_q,
+                           float scale, int32_t causal, const attn_paged_dims *dims,
+                           const attn_paged_options *opt, void *stream) {
+    attn_paged_options o{nullptr, 0, ATTN_PATH_AUTO, 0, ATTN_KV_BF16, 1.f, 1.f};
+    if (opt) o = *opt;
+    // Everything is validated, and the plan's partials checked against the
+    // scratch size, before any HIP call; a 256-aligned stand-in takes the
+    // workspace's place until the scratch address is known.
+    attn_paged_plan plan;
+    pa::AttnArgs a;
+    void *const stand_in = reinterpret_cast<void *>(uintptr_t(kWsAlign));
+    int rc = make_plan(dims, n_seqs, max_q, o.path_hint, o.pages_per_split, o.window, &plan, o.kv_dtype,
+                       kScratchBalBudget);
+    if (rc != ATTN_OK) return rc;
+    if (plan.workspace_bytes > kScratchBytes) return ATTN_ERR_WORKSPACE;
+    rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
+                       stand_in, kScratchBytes, o.path_hint, o.pages_per_split, o.sinks, o.window, plan, a,
+                       o.kv_dtype, o.k_scale, o.v_scale, kScratchBalBudget);
+    if (rc != ATTN_OK || n_seqs == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        rc = scratch_pointer(st, &ws);
+        if (rc != ATTN_OK) return rc;
+        rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims, ws,
+                           kScratchBytes, o.path_hint, o.pages_per_split, o.sinks, o.window, plan, a, o.kv_dtype,
+                           o.k_scale, o.v_scale, kScratchBalBudget);
+        if (rc != ATTN_OK) return rc;
+        // The single-launch merge needs its counters at zero; earlier calls
+        // on this GPU may have left partials in those bytes.  A kernel, not a
+        // memset node, so that a captured graph replays it correctly.
+        if (plan.counter_bytes > 0 &&
+            pa::launch_workspace_clear(static_cast<uint32_t *>(ws), plan.counter_bytes / 4, st) != hipSuccess)
+            return ATTN_ERR_HIP;
+    }
+    return paged_launch(plan, a, dims->head_dim, st);
 }
 
 int attn_paged_kv_write(void *kv_pool, const void *k_new, const void *v_new, const int32_t *block_table,

@@ -450,3 +450,31 @@ def test_stream_read_validation(pa):
     assert lib.attn_stream_read(FAKE, 16, FAKE, 65536, 4, None) == E_SHAPE
     assert lib.attn_stream_read(FAKE, 16, FAKE, 1, 6, None) == E_SHAPE        # depth 4 or 8
     assert lib.attn_stream_read(FAKE, 0, FAKE, 1, 8, None) == OK               # nothing to read: no launch
+
+
+def test_noalloc_validates_before_any_hip_call(pa):
+    """attn_paged_fwd_noalloc: argument errors and plans whose partials exceed
+    the scratch array are refused on the host, before any HIP call (so these
+    run without a GPU); n_seqs = 0 is a no-op."""
+    import paged_kv_gqa_fwd_amd as mod
+    lib = pa.load_library()
+
+    def noalloc(d, n_seqs=4, max_q=1, opt=None, **ptrs):
+        p = dict(out=FAKE, q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, cq=FAKE)
+        p.update(ptrs)
+        return lib.attn_paged_fwd_noalloc(p["out"], p["q"], p["kv"], p["bt"], p["sl"], p["cq"], n_seqs, max_q,
+                                          0.1, 1, ctypes.byref(d) if d is not None else None,
+                                          ctypes.byref(opt) if opt is not None else None, None)
+
+    assert noalloc(None) == E_NULL
+    assert noalloc(dims(head_dim=64)) == E_UNSUP
+    assert noalloc(dims(q_stride_head=100)) == E_STRIDE
+    assert noalloc(dims(), q=None) == E_NULL
+    assert noalloc(dims(), out=FAKE + 2) == E_ALIGN
+    assert noalloc(dims(), n_seqs=0, out=None, q=None) == OK
+    # 1024 sequences x 32 heads x 16 one-page splits x D 128 of f32 partials
+    # (256 MiB) cannot fit the 64 MiB array
+    big = dims(max_pages_per_seq=16, bt_stride=16, num_tokens=1024)
+    opt = mod.attn_paged_options(None, 0, mod.PATH_SPLIT_DECODE, 1, 0, 1.0, 1.0)
+    assert mod.make_plan(big, 1024, 1, mod.PATH_SPLIT_DECODE, 1).workspace_bytes > mod.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big, n_seqs=1024, opt=opt) == E_WS
