@@ -32,9 +32,11 @@ def _bits(t):
 
 
 def _cached_counters(case):
-    """The counter bytes of the binding's cached workspace for this case."""
+    """The counter bytes of the binding's cached workspace for this case (one
+    per (device, stream); the tests run on the current stream)."""
     import paged_kv_gqa_fwd_amd as pa
-    ws = pa._ws_cache[(str(torch.device("cuda", torch.cuda.current_device())),)]
+    key = (str(torch.device("cuda", torch.cuda.current_device())), int(torch.cuda.current_stream().cuda_stream))
+    ws = pa._ws_cache[key]
     return ws.buf
 
 

@@ -81,6 +81,7 @@ def test_chunked_prefill_reduced(oracle_mod):
     _check(oracle_mod, case, "chunked_prefill(reduced)")
 
 
+@pytest.mark.timeout(900)
 def test_chunked_prefill_full_all_rows():
     """Full 8-sequence chunked prefill (24/4 heads, D 256, causal over prior
     context plus the chunk) in the benchmark's launch configuration; every
@@ -102,6 +103,7 @@ def test_dit_reduced(oracle_mod):
     _check(oracle_mod, case, "dit(1000 tokens, 8 heads)")
 
 
+@pytest.mark.timeout(900)
 def test_dit_full_sampled_1in16():
     """Full 37810-token, 56-head non-causal workload in the benchmark's launch
     configuration; a seeded sample of one in sixteen token rows (all 56 heads

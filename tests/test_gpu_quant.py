@@ -135,6 +135,7 @@ def test_quant_strided_inputs(oracle_mod):
     assert not big[:, :, 0].any() and not big[:, :, :, 128:].any()
 
 
+@pytest.mark.timeout(900)
 def test_quant_dit_full_size_sampled_1in16(oracle_mod):
     """The full video-DiT shape [1, 37810, 56, 128] (non-causal, K channel
     offsets), in the benchmark's launch configuration: preparation checked
