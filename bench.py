@@ -7,9 +7,15 @@ synthetic, seeded input already resident in HBM.
 Default workload: the decode batch (64 sequences x 1 query token, 32 q / 8 KV
 heads, head_dim 128, page 64, KV lengths uniform in [1024, 8192], causal),
 reported as achieved HBM GB/s of algorithmic bytes (K and V read once per KV
-head, plus Q and the output).  Secondary lines (long-context decode, chunked
-prefill, DiT non-causal) are reported alongside, prefill ones in TFLOP/s of
-algorithmic FLOPs (4 * D per visible (query, q head, key) triple).
+head, plus Q and the output).  Secondary lines (the tiny mixed call's latency,
+long-context decode on both pool layouts, chunked prefill, DiT non-causal,
+the quantised DiT path, and variants) are timed first, each after a
+time-bounded warmup, then the primary line (W warmup steps, K timed steps).
+Prefill lines are in TFLOP/s of algorithmic FLOPs (4 * D per visible
+(query, q head, key) triple).  Every line carries its roofline block; the
+primary line and the tiny, long-decode, chunked-prefill, DiT and quantised
+lines carry the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 
 Prints ONE JSON line on stdout.
 """
@@ -155,21 +161,41 @@ def _kernel_times(fn, steps):
     return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
 
 
-# Nominal ms per step of each workload on MI355X: bounds the secondary lines'
-# step counts so that each times about a third of a second.
-NOMINAL_MS = {"decode_batch": 0.25, "long_decode": 1.5, "chunked_prefill": 4.0, "dit_self_attn": 40.0,
-              "dit_quant": 25.0, "tiny_mixed": 0.05}
+def _warm(fn, min_steps, min_seconds=0.3):
+    """Untimed calls until at least min_steps were made and min_seconds of
+    GPU time passed (the clocks settle only after a few hundred ms of load).
+    Returns the mean ms per call of the last batch, an estimate for sizing
+    the timed region."""
+    done, t_start, per = 0, time.perf_counter(), None
+    batch = max(1, min_steps)
+    while True:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / batch * 1e3
+        done += batch
+        if done >= min_steps and time.perf_counter() - t_start >= min_seconds:
+            return per
+        batch = max(1, min(1000, int(0.1e3 / max(per, 1e-3))))
 
 
-def sec_counts(name, steps, warmup):
-    per = NOMINAL_MS.get(name.split("+")[0], 1.0)
-    return max(3, min(steps // 2, int(300.0 / per))), max(1, min(warmup // 2, int(100.0 / per)))
+def _secondary_steps(per_ms, steps, seconds=0.4):
+    """Timed steps of a secondary line: about `seconds` of work, at least 3,
+    at most the primary line's K."""
+    return max(3, min(steps, int(seconds * 1e3 / max(per_ms, 1e-3))))
 
 
-def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
+def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout=None, secondary=True):
+    """Time one workload: W warmup calls (time-bounded for secondary lines),
+    then K timed calls; a second pass of calls with the library's per-launch
+    events gives the kernel times, a third the per-step distribution."""
     import paged_kv_gqa_fwd_amd as pa
-    log("[bench] generating %s%s%s" % (name, " (window %d)" % window if window else "", " (fp8 cache)" if fp8 else ""))
-    case = workloads.WORKLOADS[name](device="cuda")
+    log("[bench] generating %s%s%s%s" % (name, " (window %d)" % window if window else "", " (fp8 cache)" if fp8 else "",
+                                       " (%s pool)" % layout if layout else ""))
+    kw = {"layout": layout} if layout else {}
+    case = workloads.WORKLOADS[name](device="cuda", **kw)
     kscale = 1.0
     if fp8:
         # e4m3 codes of 2x the bf16 pool values; scales 1/2 keep the values
@@ -185,13 +211,18 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False):
         pa.paged_attention(*args, out=out, path=path, pages_per_split=pps, window=window, k_scale=kscale,
                            v_scale=kscale)
 
-    for _ in range(warmup):
-        step()
+    if secondary:
+        per = _warm(step, warmup)
+        steps = _secondary_steps(per, steps)
+    else:
+        for _ in range(warmup):
+            step()
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, _ = _kernel_times(step, steps)
     dist = _step_distribution(step, steps)
+    suffix = ("+window%d" % window if window else "") + ("+fp8" if fp8 else "") + ("+%s" % layout if layout else "")
     res = {
-        "workload": name + ("+window%d" % window if window else "") + ("+fp8" if fp8 else ""), "case": case,
+        "workload": name + suffix, "case": case, "steps": steps,
         "ms_per_step": step_ms, "step_ms_dist": dist,
         "main_kernel_ms": main_ms, "combine_kernel_ms": comb_ms,
         "path": {pa.PATH_SPLIT_DECODE: "split_decode+combine", pa.PATH_SPLIT_FUSED: "split_decode+merge",
@@ -217,19 +248,22 @@ def run_write(name, steps, warmup):
         pa.paged_attention_write(case.q, k_new, v_new, case.kv, case.block_table, case.seq_lens, case.cu_q,
                                  max(case.max_q, 1), case.scale, case.causal, out=out)
 
-    for _ in range(warmup):
-        step()
+    steps = _secondary_steps(_warm(step, warmup), steps)
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, write_ms = _kernel_times(step, steps)
     written = sum(min(n, L) for n, L in zip(case.q_lens, case.kv_lens))
     wbytes = 2 * written * case.num_kv_heads * 2 * case.head_dim * 2
-    return {"workload": name + "+kv_write", "value": round(wbytes / (write_ms * 1e-3) / 1e9, 2),
+    gbs = wbytes / (write_ms * 1e-3) / 1e9
+    return {"workload": name + "+kv_write", "value": round(gbs, 2),
             "unit": "GB/s (write kernel)", "write_bytes": wbytes, "write_kernel_ms": round(write_ms, 4),
-            "ms_per_step": round(step_ms, 4), "attention_ms": round(main_ms + comb_ms, 4),
-            "path": "kv_write + attention"}
+            "ms_per_step": round(step_ms, 4), "steps": steps, "attention_ms": round(main_ms + comb_ms, 4),
+            "path": "kv_write + attention",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "paged_kv_write_kernel",
+                         "kernel_ms": round(write_ms, 4)}}
 
 
-def run_quant(steps, warmup):
+def run_quant(steps, warmup, cpu_seconds=0.0):
     """The quantised path (attn_quant_fwd: preparation + fused int8/fp8 loop)
     on the video-DiT shape, same seeded Q/K/V as the bf16 DiT workload."""
     import paged_kv_gqa_fwd_amd as pa
@@ -241,17 +275,27 @@ def run_quant(steps, warmup):
     def step():
         pa.quant_attention(q, k, v, case.scale, False, out=out)
 
-    for _ in range(warmup):
-        step()
+    steps = _secondary_steps(_warm(step, warmup), steps)
     step_ms = _time_steps(step, steps)
     main_ms, _, prep_ms = _kernel_times(step, steps)
+    dist = _step_distribution(step, steps)
     flops = algorithmic_flops(case)
-    return {"workload": "dit_quant", "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
-            "unit": "TFLOP/s", "ms_per_step": round(step_ms, 4),
-            "mainloop_ms": round(main_ms, 4), "prep_ms": round(prep_ms, 4),
-            "mainloop_TOPS": round(flops / (main_ms * 1e-3) / 1e12, 2),
-            "frac_of_int8_fp8_peak": round(flops / (step_ms * 1e-3) / 1e12 / Q8_PEAK_TOPS, 4),
-            "path": "quant (int8 QK, fp8 PV)"}
+    tops = flops / (step_ms * 1e-3) / 1e12
+    loop_tops = flops / (main_ms * 1e-3) / 1e12
+    res = {"workload": "dit_quant", "value": round(tops, 2),
+           "unit": "TOPS (int8 Q.K ops + fp8 P.V FLOPs)", "ms_per_step": round(step_ms, 4), "steps": steps,
+           "mainloop_ms": round(main_ms, 4), "prep_ms": round(prep_ms, 4),
+           "mainloop_TOPS": round(loop_tops, 2),
+           "frac_of_int8_fp8_peak": round(tops / Q8_PEAK_TOPS, 4),
+           "path": "quant (int8 QK, fp8 PV)", "step_ms_dist": dist,
+           "roofline": {"bound": "mfma", "achieved": round(loop_tops, 2), "peak": Q8_PEAK_TOPS, "unit": "TOPS",
+                        "frac": round(loop_tops / Q8_PEAK_TOPS, 4), "traffic": None,
+                        "kernel": "quant_attn_kernel", "kernel_ms": round(main_ms, 4)}}
+    if cpu_seconds > 0:
+        log("[bench] timing the quantised CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_quant_baseline(case, cpu_seconds)
+        log("[bench] cpu baseline %s" % json.dumps(res["cpu_baseline"]))
+    return res
 
 
 def measured_traffic(kernel_files, profile_name):
@@ -275,61 +319,188 @@ def measured_traffic(kernel_files, profile_name):
     return round((fetch + write) * 1024.0)
 
 
+def _roofline(res, bound):
+    """Roofline block of a line's dominant kernel: algorithmic bytes (or
+    FLOPs) per launch over its average launch duration from the library's
+    HIP events on the launch stream."""
+    name = res["workload"]
+    kern = ("paged_decode_balanced_kernel" if res["path"].startswith("balanced") else
+            "paged_decode_split_kernel" if "split" in res["path"] else "paged_prefill_kernel")
+    if bound == "hbm":
+        ach = res["bytes"] / (res["main_kernel_ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kern,
+                "kernel_ms": round(res["main_kernel_ms"], 4)}
+    ach = res["flops"] / (res["main_kernel_ms"] * 1e-3) / 1e12
+    traffic = None
+    if name == "chunked_prefill" or name == "dit_self_attn":
+        traffic = measured_traffic(["prefill.hip", "attn_device.h", "lds_stream.h"],
+                                   "paged_prefill_kernel__%s.traffic.json" % name)
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kern,
+            "kernel_ms": round(res["main_kernel_ms"], 4)}
+
+
 def summarize(res):
     name = res["workload"]
-    if BOUND[name.split("+")[0]] == "hbm":
+    base = name.split("+")[0]
+    if base == "tiny_mixed":
+        # the manifest's tiny mixed call: its working set (about 3 MB) sits in
+        # the caches, so the line reports latency
+        us = res["ms_per_step"] * 1e3
+        return {"workload": name, "value": round(us, 2), "unit": "us per call (latency)",
+                "ms_per_step": round(res["ms_per_step"], 4), "steps": res["steps"],
+                "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"],
+                "step_ms_dist": res.get("step_ms_dist"),
+                "algorithmic_flops": res["flops"], "algorithmic_bytes": res["bytes"],
+                "roofline": _roofline(res, "hbm")}
+    if BOUND[base] == "hbm":
         val = res["bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
         kern = res["bytes"] / (res["main_kernel_ms"] * 1e-3) / 1e9
         return {"workload": name, "value": round(val, 2), "unit": "GB/s",
                 "frac_of_peak": round(val / HBM_PEAK_GBS, 4), "ms_per_step": round(res["ms_per_step"], 4),
-                "main_kernel_ms": round(res["main_kernel_ms"], 4),
+                "steps": res["steps"], "main_kernel_ms": round(res["main_kernel_ms"], 4),
                 "combine_kernel_ms": round(res["combine_kernel_ms"], 4),
                 "main_kernel_GBps": round(kern, 2), "path": res["path"],
                 "pages_per_split": res["pages_per_split"], "max_splits": res["max_splits"],
-                "step_ms_dist": res.get("step_ms_dist")}
+                "step_ms_dist": res.get("step_ms_dist"), "roofline": _roofline(res, "hbm")}
     val = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
     return {"workload": name, "value": round(val, 2), "unit": "TFLOP/s",
             "frac_of_peak": round(val / BF16_PEAK_TFLOPS, 4), "ms_per_step": round(res["ms_per_step"], 4),
-            "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"],
-            "step_ms_dist": res.get("step_ms_dist")}
+            "steps": res["steps"], "main_kernel_ms": round(res["main_kernel_ms"], 4), "path": res["path"],
+            "step_ms_dist": res.get("step_ms_dist"), "roofline": _roofline(res, "mfma")}
 
 
-def cpu_baseline(res, max_seconds=20.0):
-    """Time the fp64 CPU oracle on a bounded sample of the primary workload
-    (a prefix of its sequences) and report the same metric's unit."""
-    import oracle
-    from dataclasses import replace
-    case = res["case"]
-    name = res["workload"]
-    nthreads = oracle.num_threads()
-    # grow the sample (a prefix of the batch) until one pass takes a few
-    # seconds or covers the batch, then repeat passes to ~max_seconds in total
-    k = 1
+# ---------------------------------------------------------------- CPU oracle
+def _grow_and_time(run, max_seconds, start=1, limit=None):
+    """Time run(k) on growing samples k (doubling from `start`, at most
+    `limit`) until one pass takes a quarter of max_seconds or the sample is
+    the whole workload, then repeat passes to about max_seconds in total.
+    Returns (k, seconds per pass, passes)."""
+    k = start
     while True:
-        sub = _prefix_case(case, k)
         t = time.perf_counter()
-        oracle.paged_attn(sub.q, sub.kv, sub.block_table, sub.seq_lens, sub.cu_q, sub.scale,
-                          sub.causal)
+        run(k)
         t_one = time.perf_counter() - t
-        if t_one > max_seconds / 4 or k >= case.n_seqs:
+        if t_one > max_seconds / 4 or (limit is not None and k >= limit):
             break
-        k = min(case.n_seqs, k * 2)
+        k = k * 2 if limit is None else min(limit, k * 2)
     reps = max(1, min(50, int(max_seconds / max(t_one, 1e-3))))
     t = time.perf_counter()
     for _ in range(reps):
-        oracle.paged_attn(sub.q, sub.kv, sub.block_table, sub.seq_lens, sub.cu_q, sub.scale,
-                          sub.causal)
-    t_used = (time.perf_counter() - t) / reps
-    if BOUND[name] == "hbm":
-        val = algorithmic_bytes(sub) / t_used / 1e9
-        unit = "GB/s"
-    else:
-        val = algorithmic_flops(sub) / t_used / 1e12
-        unit = "TFLOP/s"
-    return {"value": round(val, 4), "unit": unit, "cores": nthreads, "kind": "oracle",
-            "sample": "first %d of %d sequences of the %s workload, %d timed passes of %.3f s each "
-                      "(fp64 oracle, OpenMP threads=%d)" % (k, case.n_seqs, name, reps, t_used, nthreads),
-            "cpu": _cpu_model(), "nproc": os.cpu_count()}
+        run(k)
+    return k, (time.perf_counter() - t) / reps, reps
+
+
+def _oracle_info():
+    import oracle
+    return {"cores": oracle.num_threads(), "kind": "oracle", "cpu": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def cpu_decode_baseline(case, name, max_seconds):
+    """ORACLE-P on a prefix of the batch's sequences, in GB/s of the
+    prefix's algorithmic bytes."""
+    import oracle
+    state = {}
+
+    def run(k):
+        state["sub"] = sub = _prefix_case(case, k)
+        oracle.paged_attn(sub.q, sub.kv, sub.block_table, sub.seq_lens, sub.cu_q, sub.scale, sub.causal)
+
+    k, t_used, reps = _grow_and_time(run, max_seconds, 1, case.n_seqs)
+    sub = state["sub"]
+    info = _oracle_info()
+    return dict(value=round(algorithmic_bytes(sub) / t_used / 1e9, 4), unit="GB/s",
+                sample="first %d of %d sequences of the %s workload, %d timed passes of %.3f s each "
+                       "(fp64 oracle, OpenMP threads=%d)" % (k, case.n_seqs, name, reps, t_used, info["cores"]),
+                **info)
+
+
+def cpu_prefill_baseline(case, name, max_seconds, seed=11):
+    """ORACLE-P on a seeded sample of token rows (every head of each), in
+    TFLOP/s of the sample's algorithmic FLOPs (4 D per visible (query, q
+    head, key))."""
+    import numpy as np
+    import oracle
+    c = case.to("cpu")
+    T = sum(c.q_lens)
+    order = torch.randperm(T, generator=torch.Generator().manual_seed(seed)).numpy()
+    state = {}
+
+    def run(k):
+        mask = np.zeros(T, dtype=np.uint8)
+        mask[order[:k]] = 1
+        state["mask"] = mask
+        oracle.paged_attn(c.q, c.kv, c.block_table, c.seq_lens, c.cu_q, c.scale, c.causal, row_mask=mask)
+
+    k, t_used, reps = _grow_and_time(run, max_seconds, 4, T)
+    rows = np.nonzero(state["mask"])[0]
+    vis = 0
+    cu = c.cu_q.tolist()
+    for t in rows.tolist():
+        b = next(i for i in range(c.n_seqs) if cu[i] <= t < cu[i + 1])
+        n, L, i = c.q_lens[b], c.kv_lens[b], t - cu[b]
+        vis += max(0, min(L, L - n + i + 1)) if c.causal else L
+    flops = 4 * c.head_dim * c.num_q_heads * vis
+    info = _oracle_info()
+    del c
+    return dict(value=round(flops / t_used / 1e12, 6), unit="TFLOP/s",
+                sample="%d seeded token rows (all %d heads) of %d in the %s workload, %d timed passes of %.3f s "
+                       "each (fp64 oracle, OpenMP threads=%d)" % (k, case.num_q_heads, T, name, reps, t_used,
+                                                                  info["cores"]), **info)
+
+
+def cpu_quant_baseline(case, max_seconds, seed=11):
+    """ORACLE-Q: its preparation over the whole DiT shape (one pass) plus its
+    attention on a seeded sample of query tokens; the whole path's time is
+    estimated as prep + sample time x (N / sample), reported in T ops/s of
+    the path's algorithmic work."""
+    import numpy as np
+    import oracle
+    q, k, v = (t.cpu() for t in workloads.dense_from_case(case))
+    t = time.perf_counter()
+    prep = oracle.quant_prep(q, k, v)
+    prep_s = time.perf_counter() - t
+    N = q.shape[1]
+    order = torch.randperm(N, generator=torch.Generator().manual_seed(seed)).numpy()
+
+    def run(kk):
+        mask = np.zeros(N, dtype=np.uint8)
+        mask[order[:kk]] = 1
+        oracle.quant_attn(prep, case.scale, False, row_mask=mask)
+
+    kk, t_used, reps = _grow_and_time(run, max(1.0, max_seconds - prep_s), 2, N)
+    full_s = prep_s + t_used * N / kk
+    flops = algorithmic_flops(case)
+    info = _oracle_info()
+    return dict(value=round(flops / full_s / 1e12, 6), unit="TOPS (int8 Q.K ops + fp8 P.V FLOPs)",
+                prep_s=round(prep_s, 3), attention_s_per_token=round(t_used / kk, 6),
+                sample="preparation over all %d tokens (%.2f s) + attention on %d seeded query tokens (all %d "
+                       "heads), %d timed passes of %.3f s; the whole path's time estimated as prep + that x %d/%d "
+                       "(fp64 quantisation-emulating oracle, OpenMP threads=%d)"
+                       % (N, prep_s, kk, case.num_q_heads, reps, t_used, N, kk, info["cores"]), **info)
+
+
+def cpu_baseline(res, max_seconds=20.0):
+    """The fp64 CPU oracle on a bounded sample of a line's workload, in the
+    line's unit (decode: a prefix of the batch; prefill: sampled rows)."""
+    case, name = res["case"], res["workload"]
+    base = name.split("+")[0]
+    if BOUND[base] == "hbm" and base != "tiny_mixed":
+        return cpu_decode_baseline(case, name, max_seconds)
+    if base == "tiny_mixed":
+        import oracle
+        c = case.to("cpu")
+
+        def run(_k):
+            oracle.paged_attn(c.q, c.kv, c.block_table, c.seq_lens, c.cu_q, c.scale, c.causal)
+
+        _, t_used, reps = _grow_and_time(run, max_seconds, 1, 1)
+        info = _oracle_info()
+        return dict(value=round(t_used * 1e6, 1), unit="us per call (latency)",
+                    sample="the whole tiny mixed call, %d timed passes (fp64 oracle, OpenMP threads=%d)"
+                           % (reps, info["cores"]), **info)
+    return cpu_prefill_baseline(case, name, max_seconds)
 
 
 def _cpu_model():
@@ -403,16 +574,48 @@ def calibrate_gemm(n=16384, iters=20):
     print(json.dumps(res), flush=True)
 
 
+SECONDARY = ("tiny_mixed,long_decode,long_decode+slot_major,chunked_prefill,dit_self_attn,dit_quant,"
+             "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096,decode_batch+fp8,long_decode+fp8")
+# secondary lines that carry the CPU oracle (the configurations themselves;
+# their window / fp8 / layout / write variants do not)
+CPU_LINES = {"tiny_mixed": 3.0, "long_decode": 6.0, "chunked_prefill": 6.0, "dit_self_attn": 6.0, "dit_quant": 8.0}
+
+
+def run_secondary(name, args, cpu_on):
+    """One secondary line (time-bounded warmup of at least W calls, about
+    0.4 s of timed calls), with its CPU oracle where CPU_LINES names it."""
+    W, K = args.warmup, args.steps
+    cpu_s = CPU_LINES.get(name, 0.0) if cpu_on else 0.0
+    if name.endswith("+kv_write"):
+        return run_write(name[:-len("+kv_write")], K, W)
+    if name == "dit_quant":
+        return run_quant(K, W, cpu_seconds=cpu_s)
+    kw = {}
+    base = name
+    if name.endswith("+fp8"):
+        base, kw["fp8"] = name[:-len("+fp8")], True
+    elif "+window" in name:
+        base, w = name.split("+window")
+        kw["window"] = int(w)
+    elif name.endswith("+slot_major") or name.endswith("+head_major"):
+        base, kw["layout"] = name.split("+")
+    path = args.path if args.path != 2 and BOUND[base] == "hbm" and base != "tiny_mixed" else 0   # 2 = prefill
+    r = run_workload(base, K, W, path=path, **kw)
+    ss = summarize(r)
+    if cpu_s > 0:
+        log("[bench] timing the CPU oracle on a sample of %s" % name)
+        ss["cpu_baseline"] = cpu_baseline(r, cpu_s)
+    del r
+    return ss
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_batch", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--secondary", default="long_decode,chunked_prefill,dit_self_attn,dit_quant,"
-                                           "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096,"
-                                           "decode_batch+fp8,long_decode+fp8",
-                    help="comma list of extra workloads to time ('' for none)")
+    ap.add_argument("--secondary", default=SECONDARY, help="comma list of extra workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--path", type=int, default=0)
@@ -445,63 +648,23 @@ def main():
         calibrate_gemm()
         return
     torch.manual_seed(0)
-    prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path)
-    s = summarize(prim)
-    log("[bench] %s" % json.dumps(s))
+    cpu_on = not args.no_cpu_baseline
+    # Secondary lines first: the GPU is then under load, at its steady
+    # clocks, when the primary line's W warmup and K timed steps run.
     secondary = []
     for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
-        if name.endswith("+fp8"):
-            r = run_workload(name[:-len("+fp8")], *sec_counts(name, args.steps, args.warmup), fp8=True)
-            ss = summarize(r)
-            log("[bench] %s" % json.dumps(ss))
-            secondary.append(ss)
-            del r
-            torch.cuda.empty_cache()
-            continue
-        if "+window" in name:
-            base, w = name.split("+window")
-            r = run_workload(base, *sec_counts(name, args.steps, args.warmup), window=int(w))
-            ss = summarize(r)
-            log("[bench] %s" % json.dumps(ss))
-            secondary.append(ss)
-            del r
-            torch.cuda.empty_cache()
-            continue
-        if name.endswith("+kv_write"):
-            ss = run_write(name[:-len("+kv_write")], *sec_counts(name, args.steps, args.warmup))
-            log("[bench] %s" % json.dumps(ss))
-            secondary.append(ss)
-            torch.cuda.empty_cache()
-            continue
-        if name == "dit_quant":
-            ss = run_quant(*sec_counts(name, args.steps, args.warmup))
-            log("[bench] %s" % json.dumps(ss))
-            secondary.append(ss)
-            torch.cuda.empty_cache()
-            continue
-        sec_path = args.path if args.path != 2 and BOUND[name] == "hbm" else 0   # 2 = prefill
-        r = run_workload(name, *sec_counts(name, args.steps, args.warmup), path=sec_path)
-        ss = summarize(r)
+        ss = run_secondary(name, args, cpu_on)
         log("[bench] %s" % json.dumps(ss))
         secondary.append(ss)
-        del r
         torch.cuda.empty_cache()
+    prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path, secondary=False)
+    s = summarize(prim)
+    log("[bench] %s" % json.dumps(s))
     bound = BOUND[args.workload]
-    if bound == "hbm":
-        traffic = None
-        kname = ("paged_decode_balanced_kernel" if prim["path"].startswith("balanced") else
-                 "paged_decode_split_kernel" if "split" in prim["path"] else "paged_prefill_kernel")
-        if args.workload == "decode_batch" and "split" in prim["path"]:
-            traffic = measured_traffic(["decode_split.hip", "attn_device.h"],
-                                       "%s__decode_batch.traffic.json" % kname)
-        roof = {"bound": "hbm", "achieved": s["main_kernel_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(s["main_kernel_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "kernel_ms": s["main_kernel_ms"]}
-    else:
-        ach = prim["flops"] / (prim["main_kernel_ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "paged_prefill_kernel", "kernel_ms": s["main_kernel_ms"]}
+    roof = s["roofline"]
+    if bound == "hbm" and args.workload == "decode_batch" and "split" in prim["path"]:
+        roof["traffic"] = measured_traffic(["decode_split.hip", "attn_device.h"],
+                                           "%s__decode_batch.traffic.json" % roof["kernel"])
     ceiling = None
     if bound == "hbm":
         # the practical denominator beside the 8 TB/s peak: a plain read
@@ -511,7 +674,7 @@ def main():
         ceiling["step_frac"] = round(s["value"] / ceiling["GBps"], 4)
         log("[bench] read ceiling %s" % json.dumps(ceiling))
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_on:
         log("[bench] timing the CPU oracle on a sample")
         cpu = cpu_baseline(prim)
         log("[bench] cpu baseline %s" % json.dumps(cpu))
@@ -524,9 +687,9 @@ def main():
         "config": {"workload": DESCR[args.workload], "n_seqs": case.n_seqs,
                    "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
                    "head_dim": case.head_dim, "page_size": 64, "total_kv_tokens": sum(case.kv_lens),
-                   "algorithmic_bytes": prim["bytes"], "path": prim["path"],
+                   "algorithmic_bytes": prim["bytes"], "algorithmic_flops": prim["flops"], "path": prim["path"],
                    "pages_per_split": prim["pages_per_split"], "max_splits": prim["max_splits"]},
-        "frac_of_peak": s["frac_of_peak"],
+        "frac_of_peak": s.get("frac_of_peak"),
         "roofline": roof,
         "read_ceiling": ceiling,
         "step_ms_dist": s.get("step_ms_dist"),
