@@ -51,9 +51,11 @@ DESCR = {
     "dit_self_attn": "DiT self-attention: 1 seq x 37810 tokens, 56 heads (MHA), head_dim 128, "
                      "non-causal, per-channel K offset N(0, 2)",
     "tiny_mixed": "tiny mixed: 2 seqs x 32 queries, 24 q / 4 KV heads, head_dim 256, 22-page pool, causal",
+    "short_batch": "short multi-token runs: 256 seqs x U[2, 8] query tokens, 32 q / 4 KV heads (GQA 8), "
+                   "head_dim 128, page 64, KV lengths U[1024, 8192], causal",
 }
 BOUND = {"decode_batch": "hbm", "long_decode": "hbm", "chunked_prefill": "mfma",
-         "dit_self_attn": "mfma", "tiny_mixed": "hbm"}
+         "dit_self_attn": "mfma", "tiny_mixed": "hbm", "short_batch": "hbm"}
 
 
 def log(msg):
@@ -187,7 +189,7 @@ def _secondary_steps(per_ms, steps, seconds=0.4):
     return max(3, min(steps, int(seconds * 1e3 / max(per_ms, 1e-3))))
 
 
-def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout=None, secondary=True):
+def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout=None, secondary=True, tag=""):
     """Time one workload: W warmup calls (time-bounded for secondary lines),
     then K timed calls; a second pass of calls with the library's per-launch
     events gives the kernel times, a third the per-step distribution."""
@@ -220,7 +222,7 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, _ = _kernel_times(step, steps)
     dist = _step_distribution(step, steps)
-    suffix = ("+window%d" % window if window else "") + ("+fp8" if fp8 else "") + ("+%s" % layout if layout else "")
+    suffix = ("+window%d" % window if window else "") + ("+fp8" if fp8 else "") + ("+%s" % layout if layout else "") + tag
     res = {
         "workload": name + suffix, "case": case, "steps": steps,
         "ms_per_step": step_ms, "step_ms_dist": dist,
@@ -575,7 +577,8 @@ def calibrate_gemm(n=16384, iters=20):
 
 
 SECONDARY = ("tiny_mixed,long_decode,long_decode+slot_major,chunked_prefill,dit_self_attn,dit_quant,"
-             "decode_batch+kv_write,chunked_prefill+kv_write,long_decode+window4096,decode_batch+fp8,long_decode+fp8")
+             "short_batch,short_batch+prefill,decode_batch+kv_write,chunked_prefill+kv_write,"
+             "long_decode+window4096,decode_batch+fp8,long_decode+fp8")
 # secondary lines that carry the CPU oracle (the configurations themselves;
 # their window / fp8 / layout / write variants do not)
 CPU_LINES = {"tiny_mixed": 3.0, "long_decode": 6.0, "chunked_prefill": 6.0, "dit_self_attn": 6.0, "dit_quant": 8.0}
@@ -599,7 +602,13 @@ def run_secondary(name, args, cpu_on):
         kw["window"] = int(w)
     elif name.endswith("+slot_major") or name.endswith("+head_major"):
         base, kw["layout"] = name.split("+")
-    path = args.path if args.path != 2 and BOUND[base] == "hbm" and base != "tiny_mixed" else 0   # 2 = prefill
+    if name.endswith("+prefill"):
+        # the same workload forced onto the prefill kernel: the route that
+        # short query runs took before the short-sequence body
+        base, path = name[:-len("+prefill")], 2
+        kw["tag"] = "+prefill"
+    else:
+        path = args.path if args.path != 2 and BOUND[base] == "hbm" and base != "tiny_mixed" else 0   # 2 = prefill
     r = run_workload(base, K, W, path=path, **kw)
     ss = summarize(r)
     if cpu_s > 0:

@@ -98,7 +98,11 @@ typedef struct attn_paged_plan {
 
 enum {
     ATTN_PATH_AUTO = 0,
-    ATTN_PATH_SPLIT_DECODE = 1, /* split-KV partial kernel + log-sum-exp combine kernel */
+    ATTN_PATH_SPLIT_DECODE = 1, /* split-KV partial kernel + log-sum-exp combine kernel; takes
+                                   up to 64 packed rows G * max_q per (sequence, KV head), in
+                                   blocks of 16 (more than 16 rows: the short-sequence body of
+                                   the Mojo SM100MHA2Q docs' struct summary, short query runs
+                                   routed to a cheaper body than the prefill tile) */
     ATTN_PATH_PREFILL = 2,      /* q-tile kernel with causal tile skipping, one pass */
     ATTN_PATH_SPLIT_FUSED = 3,  /* split-KV kernel whose last split per (sequence, KV head)
                                    merges the partials: one launch (decode.json's single
@@ -115,8 +119,9 @@ enum {
                                    with the cuts placed by length, so ragged batches
                                    keep every workgroup equally busy.  At most
                                    1024 sequences.  AUTO's choice for decode-shaped
-                                   calls (G * max_q <= 16, pages_per_split = 0,
-                                   n_seqs <= 1024). */
+                                   and short calls (G * max_q <= 64, pages_per_split
+                                   = 0, n_seqs <= 1024); longer query runs take
+                                   ATTN_PATH_PREFILL. */
 };
 
 /*
@@ -222,7 +227,7 @@ typedef struct attn_paged_options {
  * (1 byte; dims' kv strides then count bytes and must be multiples of 16),
  * with one scale for all of K and one for all of V (the Mojo SM100MHA2Q docs
  * carry fp8 branches of the KV dtype; per-tensor scales are the reading taken
- * here).  Supported on the split-decode paths (packed rows G * max_q <= 16);
+ * here).  Supported on the split-decode paths (packed rows G * max_q <= 64);
  * a call that would take the prefill path returns ATTN_ERR_UNSUPPORTED.
  * Scales must be finite.
  */

@@ -63,6 +63,16 @@ constexpr int decode_stages_f8(int d) { return d == 128 ? PA_DECODE_F8_STAGES_12
 #endif
 constexpr int decode_waves_per_simd_f8(int d) { return d == 128 ? PA_DECODE_F8_WAVES_128 : PA_DECODE_WAVES_256; }
 constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
+// Resident waves per SIMD of the split-decode kernels (with rb blocks of 16
+// packed rows a wave still holds one block's Q^T and O^T: the same count).
+constexpr int decode_waves(int d, bool f8, int rb) {
+    return rb > 0 && f8 ? decode_waves_per_simd_f8(d) : decode_waves_per_simd(d);
+}
+// Packed rows (G x query tokens of one sequence) the split-decode kernels
+// take: blocks of 16, at most four (the short-sequence body).
+constexpr int kDecodeRowBlock = 16;
+constexpr int kMaxDecodeRowBlocks = 4;
+constexpr int decode_row_blocks(int64_t rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : 4; }
 
 // Arguments shared by the split-KV decode kernel and the prefill kernel.
 struct AttnArgs {
@@ -90,6 +100,7 @@ struct AttnArgs {
     int32_t kv_fp8;             // pool holds OCP e4m3 codes (split path only); strides count bytes
     float v_scale;              // V = v_scale * e4m3(code) (1 for a bf16 pool); k_scale is in scale_log2
     int32_t *seg_splits;        // balanced split path: [B] pieces per sequence (1 = written directly, 0 = no page)
+    int32_t row_blocks;         // split paths: blocks of 16 packed rows per workgroup (1, 2 or 4)
 };
 
 struct CombineArgs {

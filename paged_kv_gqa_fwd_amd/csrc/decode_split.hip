@@ -14,10 +14,14 @@
 // equal ranges of the whole batch's pages (the balanced kernel below).  The
 // pages stream through LDS with 16-byte coalesced non-temporal loads, staged
 // in registers one or two pages ahead.  The G q heads x n query tokens of
-// the KV head (<= 16 rows) form the N side of the MFMA and the keys the M
-// side ("swap AB"), so the score tile's C layout is directly the B operand
-// of the P.V MFMA.  Each wave owns 16 keys of every page and keeps its own
-// online softmax state; the four waves merge in LDS at the end.
+// the KV head form the N side of the MFMA in blocks of 16 rows and the keys
+// the M side ("swap AB"), so the score tile's C layout is directly the B
+// operand of the P.V MFMA.  With RB row blocks (one for decode; two or four
+// for short multi-token runs, the short-sequence body: up to 64 packed
+// rows) the four waves form RB groups of 4 / RB: wave w takes row block
+// w / (4 / RB) and a slice of 16 RB keys of every page, and keeps its own
+// online softmax state; the waves of a row block merge in LDS at the end.
+// Per wave the registers are those of one row block whatever RB is.
 #include "attn_device.h"
 
 namespace pa {
@@ -52,6 +56,15 @@ struct DecodeCfg {
     static constexpr int CH_PER_THREAD = CHUNKS / kThreads;  // D/16 (bf16) or D/32 (fp8)
     static constexpr int LDS_ELEMS = kPage * (KROW + VROW);
 };
+
+
+// Row block and key slice of wave w with RB row blocks: waves
+// KW rb .. KW rb + KW - 1 (KW = 4 / RB) share row block rb and take
+// consecutive slices of 16 RB keys of every page.
+template <int RB>
+__device__ __forceinline__ int decode_row_block(int w) { return w / (4 / RB); }
+template <int RB>
+__device__ __forceinline__ int decode_key_offset(int w) { return (w % (4 / RB)) * 16 * RB; }
 
 // Issue the 16-byte loads of one page (K and V rows of one KV head) into
 // registers.  Chunk c -> key = c / (2 DC), kv = (c / DC) % 2, dc = c % DC:
@@ -129,78 +142,97 @@ __device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8
         store_page_impl<D, F8, true>(stage, ks, vs, tid, valid);
 }
 
-// Per-page work of one wave: keys 16w .. 16w+15 of page p (already in LDS)
-// against the rows whose Q^T fragments are in qreg (lane row = lane % 16,
-// visible keys [lo, vis)); updates the wave's online-softmax state.
-template <int D, bool F8>
+// Per-page work of one wave: the RB blocks of 16 keys starting at key kw0 of
+// page p (already in LDS) against the 16 rows whose Q^T fragments are in
+// qreg (lane row = lane % 16 of the wave's row block, visible keys
+// [lo, vis)); updates the wave's online-softmax state.
+template <int D, bool F8, int RB>
 __device__ __forceinline__ void decode_compute_page(const uint16_t *ks, const uint16_t *vs,
                                                     const bf16x8 (&qreg)[D / 32], f32x4 (&oacc)[D / 16],
                                                     float &m_run, float &l_part, int p, int vis, int lo,
-                                                    float scale_log2, int w, int lane) {
+                                                    float scale_log2, int kw0, int lane) {
     using C = DecodeCfg<D, F8>;
-    // S^T[16 keys x 16 rows] = K Q^T.
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // S^T[16 keys x 16 rows] = K Q^T per key block.
+    f32x4 sacc[RB];
+#pragma unroll
+    for (int kb = 0; kb < RB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        const uint16_t *kp = ks + (16 * w + (lane & 15)) * C::KROW + 8 * (lane >> 4);
+        const uint16_t *kp = ks + (kw0 + (lane & 15)) * C::KROW + 8 * (lane >> 4);
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 32 * kk);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], sacc, 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < RB; ++kb) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(kp + 16 * kb * C::KROW + 32 * kk);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[kk], sacc[kb], 0, 0, 0);
+            }
         }
     }
-    // sacc[i] = score of key p*64 + 16w + 4*(lane/16) + i for this lane's row.
-    const int key0 = p * kPage + 16 * w + 4 * (lane >> 4);
-    float sv[4];
+    // sacc[kb][i] = score of key p*64 + kw0 + 16 kb + 4*(lane/16) + i for this lane's row.
+    const int key0 = p * kPage + kw0 + 4 * (lane >> 4);
+    float sv[RB][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sv[i] = (key0 + i < vis && key0 + i >= lo) ? sacc[i] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[i]);
-    }
+    for (int kb = 0; kb < RB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * kb + i;
+            sv[kb][i] = (key < vis && key >= lo) ? sacc[kb][i] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[kb][i]);
+        }
     mx = fmaxf(mx, shfl_xor_f32(mx, 16));
     mx = fmaxf(mx, shfl_xor_f32(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_fast(m_run - m_use);
     m_run = m_new;
-    bf16x4 pb;
+    i16x4 pop[RB];
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 pr = (__bf16)exp2_fast(sv[i] - m_use);
-        pb[i] = pr;
-        psum += (float)pr;   // the sum uses the same rounded P as the P.V product
+    for (int kb = 0; kb < RB; ++kb) {
+        bf16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const __bf16 pr = (__bf16)exp2_fast(sv[kb][i] - m_use);
+            pb[i] = pr;
+            psum += (float)pr;   // the sum uses the same rounded P as the P.V product
+        }
+        pop[kb] = __builtin_bit_cast(i16x4, pb);
     }
     l_part = l_part * alpha + psum;
     if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
     }
-    // O^T[d, row] += V^T[d, key] P^T[key, row] over this wave's 16 keys.
-    const i16x4 pop = __builtin_bit_cast(i16x4, pb);
-    const uint16_t *vp = vs + (16 * w + 4 * (lane >> 4) + ((lane & 15) >> 2)) * C::VROW + 4 * (lane & 3);
+    // O^T[d, row] += V^T[d, key] P^T[key, row] over this wave's keys.
+    const uint16_t *vp = vs + (kw0 + 4 * (lane >> 4) + ((lane & 15) >> 2)) * C::VROW + 4 * (lane & 3);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-        const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * db));
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < RB; ++kb) {
+            const i16x4 vop = __builtin_bit_cast(i16x4, lds_read_tr16(vp + 16 * kb * C::VROW + 16 * db));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop[kb], oacc[db], 0, 0, 0);
+        }
     }
 }
 
-// Merge the four waves' (m, l, O) of one (sequence, KV head) piece in LDS,
-// then write each of its rows: the unnormalised partial and (max, sum) in
-// split slot split_idx (device-coherent stores when another workgroup of the
-// launch reads them), or, when the piece is the whole sequence, the
-// normalised bf16 output with the row's sink in the normaliser.  Starts with
-// a barrier (all waves done with the K/V tiles); reuses the K/V LDS area.
-template <int D, bool F8>
+// Merge the (m, l, O) of the waves of each row block (4 / RB waves per
+// block) of one (sequence, KV head) piece in LDS, then write each of its
+// rows: the unnormalised partial and (max, sum) in split slot split_idx
+// (device-coherent stores when another workgroup of the launch reads
+// them), or, when the piece is the whole sequence, the normalised bf16
+// output with the row's sink in the normaliser.  Starts with a barrier (all
+// waves done with the K/V tiles); reuses the K/V LDS area.
+template <int D, bool F8, int RB>
 __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *smem, float (&red_m)[4][16],
                                                    float (&red_l)[4][16], const f32x4 (&oacc)[D / 16],
                                                    float m_run, float l_part, int b, int g, int q0, int rows,
                                                    bool split, int split_idx, bool coherent, int tid) {
     using C = DecodeCfg<D, F8>;
+    constexpr int KW = 4 / RB;   // waves per row block
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int row = lane & 15;
+    const int w0 = w - w % KW;   // first wave of this wave's row block
     const int G = a.group;
     float l_row = l_part + shfl_xor_f32(l_part, 16);
     l_row += shfl_xor_f32(l_row, 32);
@@ -211,7 +243,7 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
     __syncthreads();   // also: all waves are done with the K/V tiles
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][row]);
+    for (int k = 0; k < KW; ++k) M = fmaxf(M, red_m[w0 + k][row]);
     const float M_use = (M == -INFINITY) ? 0.f : M;
     const float wgt = exp2_fast(m_run - M_use);
     float *ored = reinterpret_cast<float *>(smem);   // [4 waves][16 rows][D] f32
@@ -227,18 +259,21 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
     __syncthreads();
 
     // Thread -> (rows r = tid / D + k * (256 / D), column d = tid % D).
+    // Packed row r is row r % 16 of row block r / 16, held by waves
+    // KW (r / 16) .. + KW - 1.
     constexpr int RSTEP = kThreads / D;   // 1 (D=256) or 2 (D=128)
     const int d = tid % D;
     for (int r = tid / D; r < rows; r += RSTEP) {
+        const int rw0 = (r / 16) * KW, rr = r % 16;
         float Mr = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) Mr = fmaxf(Mr, red_m[ww][r]);
+        for (int k = 0; k < KW; ++k) Mr = fmaxf(Mr, red_m[rw0 + k][rr]);
         const float Mr_use = (Mr == -INFINITY) ? 0.f : Mr;
         float lsum = 0.f, osum = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            lsum += red_l[ww][r] * exp2_fast(red_m[ww][r] - Mr_use);
-            osum += ored[(ww * 16 + r) * D + d];
+        for (int k = 0; k < KW; ++k) {
+            lsum += red_l[rw0 + k][rr] * exp2_fast(red_m[rw0 + k][rr] - Mr_use);
+            osum += ored[((rw0 + k) * 16 + rr) * D + d];
         }
         if constexpr (F8) osum *= a.v_scale;   // V = v_scale * e4m3(code)
         const int ri = r / G;
@@ -285,7 +320,7 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
 // page is read and zeroed in LDS), page ids come through the scalar cache,
 // read a compute phase ahead, and the ring has one exit.  Otherwise the
 // wait covers every load in flight and the ring drains at each page.
-template <int D, bool F8>
+template <int D, bool F8, int RB>
 __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t *ks, uint16_t *vs,
                                                     const char *head_base, const int32_t *bt_row, int p_begin,
                                                     int p_end, int L, const bf16x8 (&qreg)[D / 32],
@@ -295,9 +330,9 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
                                                     bool preloaded, int next_pid) {
     using C = DecodeCfg<D, F8>;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int kw0 = decode_key_offset<RB>(tid >> 6);
     auto compute_page = [&](int p) {
-        decode_compute_page<D, F8>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, w, lane);
+        decode_compute_page<D, F8, RB>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, kw0, lane);
     };
     const int64_t sp = a.kv_sp;
     const int p_last = p_end - 1;
@@ -378,9 +413,34 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
     }
 }
 
-template <int D, bool F8>
+// This lane's packed row (row lane % 16 of its wave's row block) of a
+// (sequence, KV head) with n query tokens, L keys and `rows` packed rows:
+// its visible key range [lo, vis) and Q^T fragments as the B operand of
+// v_mfma_f32_16x16x32_bf16 (lane holds q[row, 32 kk + 8 (lane / 16) .. +7];
+// zeros for rows past the end).
+template <int D, int RB>
+__device__ __forceinline__ void load_q_rows(const AttnArgs &a, int q0, int n, int L, int g, int rows, int tid,
+                                            bf16x8 (&qreg)[D / 32], int &vis, int &lo) {
+    const int G = a.group;
+    const int lane = tid & 63;
+    const int row = 16 * decode_row_block<RB>(tid >> 6) + (lane & 15);
+    const bool row_ok = row < rows;
+    const int qi = row / G;
+    const int h = g * G + (row - qi * G);
+    vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
+    lo = row_ok ? window_start(L - n + qi, a.window) : 0;   // first key inside the window
+    const uint16_t *qp = a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk);
+        qreg[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+template <int D, bool F8, int RB>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
+__attribute__((amdgpu_waves_per_eu(decode_waves(D, F8, RB))))
 void paged_decode_split_kernel(const AttnArgs a) {
     using C = DecodeCfg<D, F8>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
@@ -396,7 +456,6 @@ void paged_decode_split_kernel(const AttnArgs a) {
     const int b = blockIdx.y;
     const int s = blockIdx.z;
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
 
     const int L = a.seq_lens[b];
     const int q0 = a.cu_q[b];
@@ -414,28 +473,12 @@ void paged_decode_split_kernel(const AttnArgs a) {
     const int p_end = min(npages, p_begin + a.pages_per_split);
     const int G = a.group;
     int rows = n * G;
-    if (rows > 16) rows = 16;
+    if (rows > 16 * RB) rows = 16 * RB;
 
-    // This lane's query row (the N index of the MFMA tiles).
-    const int row = lane & 15;
-    const bool row_ok = row < rows;
-    const int qi = row / G;
-    const int h = g * G + (row - qi * G);
-    const int vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
-    const int lo = row_ok ? window_start(L - n + qi, a.window) : 0;   // first key inside the window
-
-    // Q^T as the B operand of v_mfma_f32_16x16x32_bf16: lane holds
-    // q[row, 32*kk + 8*(lane/16) .. +7] for kk = 0 .. D/32-1.
+    // This lane's query row (the N index of the MFMA tiles) and its Q^T.
+    int vis, lo;
     bf16x8 qreg[D / 32];
-    {
-        const uint16_t *qp = a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh + 8 * (lane >> 4);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk);
-            qreg[kk] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
+    load_q_rows<D, RB>(a, q0, n, L, g, rows, tid, qreg, vis, lo);
 
     const char *head_base = reinterpret_cast<const char *>(a.kv) + (int64_t)g * a.kv_sh * C::EB;
     const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
@@ -446,15 +489,14 @@ void paged_decode_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
     float l_part = 0.f;        // this lane's share of the running sum
 
-
     u32x4 st1[C::CH_PER_THREAD];
-    decode_stream_pages<D, F8>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part, vis, lo,
-                               tid, st1, false, -1);
+    decode_stream_pages<D, F8, RB>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part, vis,
+                                   lo, tid, st1, false, -1);
 
-    // ---- merge the four waves' (m, l, O) in LDS, write ------------------
+    // ---- merge the waves' (m, l, O) in LDS, write -------------------------
     const bool split = a.max_splits > 1;
-    decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, split, s, a.fuse_merge != 0,
-                              tid);
+    decode_merge_write<D, F8, RB>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, split, s,
+                                  a.fuse_merge != 0, tid);
     constexpr int RSTEP = kThreads / D;
     const int d = tid % D;
     if (!split || !a.fuse_merge) return;
@@ -525,9 +567,9 @@ void paged_decode_split_kernel(const AttnArgs a) {
 // LDS prefix sum over at most kBalMaxSeqs sequences), so nothing but the
 // launch orders the two kernels.  Workgroup (0, 0) publishes each
 // sequence's piece count for the combine kernel.
-template <int D, bool F8>
+template <int D, bool F8, int RB>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DecodeCfg<D, F8>::WAVES_PER_SIMD)))
+__attribute__((amdgpu_waves_per_eu(decode_waves(D, F8, RB))))
 void paged_decode_balanced_kernel(const AttnArgs a) {
     using C = DecodeCfg<D, F8>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
@@ -608,7 +650,6 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
     __syncthreads();
 
     const char *head_base = reinterpret_cast<const char *>(a.kv) + (int64_t)g * a.kv_sh * C::EB;
-    const int row = lane & 15;
     f32x4 oacc[D / 16];
     bf16x8 qreg[D / 32];
 
@@ -638,32 +679,20 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
             p2 = __builtin_amdgcn_readfirstlane((s_L[b2] + kPage - 1) / kPage - (s_F[b2 + 1] - s_F[b2]));
             if constexpr (kCarry) next_pid = load_invariant_i32(a.block_table + (int64_t)b2 * a.bt_stride + p2);
         }
-        const int rows = min(n * G, 16);
-        const bool row_ok = row < rows;
-        const int qi = row / G;
-        const int h = g * G + (row - qi * G);
-        const int vis = row_ok ? visible_keys(L, n, qi, a.causal) : 0;
-        const int lo = row_ok ? window_start(L - n + qi, a.window) : 0;
-        {
-            const uint16_t *qp = a.q + (int64_t)(q0 + qi) * a.q_st + (int64_t)h * a.q_sh + 8 * (lane >> 4);
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk);
-                qreg[kk] = __builtin_bit_cast(bf16x8, v);
-            }
-        }
+        const int rows = min(n * G, 16 * RB);
+        int vis, lo;
+        load_q_rows<D, RB>(a, q0, n, L, g, rows, tid, qreg, vis, lo);
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m_run = -INFINITY;
         float l_part = 0.f;
-        decode_stream_pages<D, F8>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p, p + cnt, L,
-                                   qreg, oacc, m_run, l_part, vis, lo, tid, st1, preloaded, next_pid);
+        decode_stream_pages<D, F8, RB>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p, p + cnt,
+                                       L, qreg, oacc, m_run, l_part, vis, lo, tid, st1, preloaded, next_pid);
         // The piece: the whole sequence (written out) or split slot
         // r - floor(F_b / C) of its ns pieces.
         const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
-        decode_merge_write<D, F8>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, ns > 1,
-                                  r - F0 / Cr, false, tid);
+        decode_merge_write<D, F8, RB>(a, smem, red_m, red_l, oacc, m_run, l_part, b, g, q0, rows, ns > 1,
+                                      r - F0 / Cr, false, tid);
         left -= cnt;
         if (left <= 0) break;
         // Deeper rings wait for the piece's stores before the next piece's
@@ -737,22 +766,39 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     for (int e = 0; e < PER; ++e) op[lane + 64 * e] = f32_to_bf16_bits(acc[e] * inv);
 }
 
-template <int D>
-hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    if (a.kv_fp8)
-        hipLaunchKernelGGL((paged_decode_split_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
+// Row blocks of 16 packed rows: one for decode (<= 16 rows), two or four for
+// the short-sequence body (<= 32 / <= 64 rows).
+template <int D, bool F8>
+hipError_t launch_decode_split_rb(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    if (a.row_blocks <= 1)
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 1>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.row_blocks == 2)
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 2>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((paged_decode_split_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 4>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, bool F8>
+hipError_t launch_decode_balanced_rb(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    if (a.row_blocks <= 1)
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 1>), grid, dim3(kThreads), 0, stream, a);
+    else if (a.row_blocks == 2)
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 2>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 4>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
+hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    return a.kv_fp8 ? launch_decode_split_rb<D, true>(a, grid, stream) : launch_decode_split_rb<D, false>(a, grid, stream);
+}
+
+template <int D>
 hipError_t launch_decode_balanced(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    if (a.kv_fp8)
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, false>), grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return a.kv_fp8 ? launch_decode_balanced_rb<D, true>(a, grid, stream)
+                    : launch_decode_balanced_rb<D, false>(a, grid, stream);
 }
 
 template <int D>

@@ -31,7 +31,9 @@ hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
 namespace {
 
 constexpr int kVersion = 10000;          // 1.0.0
-constexpr int kMaxDecodeRows = 16;       // G * max_q rows fit one 16-wide MFMA tile
+// G * max_q packed rows the split-decode kernels take (up to four 16-wide
+// MFMA row blocks: the short-sequence body); more rows take the prefill kernel.
+constexpr int kMaxDecodeRows = pa::kDecodeRowBlock * pa::kMaxDecodeRowBlocks;
 constexpr int kGridYZMax = 65535;
 constexpr size_t kWsAlign = 256;
 // Split sizing for the decode path: aim for about this many rounds of
@@ -134,8 +136,8 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         // Ranges: one per (resident workgroup slot / KV head).  The least
         // range size C_min bounds the pieces of one sequence by
         // floor((MP - 1) / C_min) + 2, which sizes the partial workspace.
-        const int64_t waves = kv_dtype == ATTN_KV_FP8_E4M3 ? pa::decode_waves_per_simd_f8(d->head_dim)
-                                                           : pa::decode_waves_per_simd(d->head_dim);
+        const int64_t waves = pa::decode_waves(d->head_dim, kv_dtype == ATTN_KV_FP8_E4M3,
+                                               pa::decode_row_blocks(mq * G));
         const int64_t slots = kBalRounds * kComputeUnits * waves;
         const int64_t R = std::min<int64_t>(std::max<int64_t>((slots + d->num_kv_heads - 1) / d->num_kv_heads, 1),
                                             kGridYZMax);
@@ -157,7 +159,9 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         int64_t p = pps;
         if (p == 0) {
             // one workgroup per SIMD-wave slot: 4 waves = one per SIMD
-            const int64_t target = kSplitRounds * kComputeUnits * pa::decode_waves_per_simd(d->head_dim);
+            const int64_t target = kSplitRounds * kComputeUnits *
+                                   pa::decode_waves(d->head_dim, kv_dtype == ATTN_KV_FP8_E4M3,
+                                                    pa::decode_row_blocks(mq * G));
             const int64_t bound = MP * std::max<int64_t>(n_seqs, 1) * d->num_kv_heads;
             p = (bound + target - 1) / target;
         }
@@ -281,6 +285,7 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     a.q_negate = scale < 0.f ? 1 : 0;
     a.sinks = sinks;
     a.window = effective_window(dims, window);
+    a.row_blocks = pa::decode_row_blocks((int64_t)std::max<int32_t>(max_q, 1) * G);
     if (plan.workspace_bytes > 0) {
         // [merge counters or pieces per sequence | partial O | partial (m, l)],
         // each 256-byte aligned

@@ -113,8 +113,15 @@ def test_bad_sizes(pa):
 
 
 def test_forced_split_path_row_limit(pa):
-    # G = 4; max_q = 5 -> 20 rows > 16: the split kernel cannot take it
-    assert call(pa, dims(), max_q=5, path=1) == E_UNSUP
+    # G = 4; max_q = 17 -> 68 packed rows > 64 (four blocks of 16): the split
+    # kernels cannot take it; up to 64 rows they plan (the short-sequence body)
+    assert call(pa, dims(), max_q=17, path=1) == E_UNSUP
+    assert call(pa, dims(), max_q=17, path=4) == E_UNSUP
+    import paged_kv_gqa_fwd_amd as mod
+    for mq in (1, 4, 5, 8, 9, 16):
+        p = mod.make_plan(dims(), 4, mq, mod.PATH_AUTO)
+        assert p.path == mod.PATH_SPLIT_BALANCED, (mq, p.path)
+    assert mod.make_plan(dims(), 4, 17, mod.PATH_AUTO).path == mod.PATH_PREFILL
 
 
 def test_workspace_checks(pa):
@@ -198,7 +205,7 @@ def test_prefill_rejects_slot_strides_past_32_bit_offsets(pa):
                                                        ctypes.byref(plan))
         assert rc == expect, (s, rc)
         if expect != OK:
-            # AUTO takes prefill for 64 rows x G 4 > 16: the call is refused
+            # AUTO takes prefill for 64 tokens x G 4 > 64 rows: the call is refused
             # before any launch
             assert call(pa, d, n_seqs=4, max_q=64) == E_UNSUP
         # decode-shaped calls keep their 64-bit split path
@@ -243,8 +250,9 @@ def test_plan_balanced(pa):
     pw = mod.make_plan(d5, 128, 1, window=4096)
     mp_w = (4096 + 1 + 62) // 64 + 1      # 65 pages from row 0's window start
     assert pw.max_splits == (mp_w - 1) // pw.pages_per_split + 2
-    # more query rows than one MFMA tile -> prefill
-    assert mod.make_plan(d, 64, 5).path == mod.PATH_PREFILL
+    # more packed rows than four 16-row MFMA blocks -> prefill
+    assert mod.make_plan(d, 64, 16).path == mod.PATH_SPLIT_BALANCED   # 64 packed rows: the short body
+    assert mod.make_plan(d, 64, 17).path == mod.PATH_PREFILL
 
 
 def test_workspace_bytes_query(pa):
@@ -338,7 +346,8 @@ def test_fp8_cache_options_validate(pa):
     assert mp(f8()) == OK and plan.path == mod.PATH_SPLIT_BALANCED
     assert mp(f8(dtype=2)) == E_UNSUP
     assert mp(f8(path=2)) == E_UNSUP                        # the prefill kernel reads bf16 only
-    assert mp(f8(), max_q=5) == E_UNSUP                     # 20 packed rows: prefill would be needed
+    assert mp(f8(), max_q=16) == OK                         # 64 packed rows: the short-sequence body
+    assert mp(f8(), max_q=17) == E_UNSUP                    # 68 packed rows: prefill would be needed
     assert mp(f8(), dd=dims(max_pages_per_seq=128, bt_stride=128, kv_stride_kv=136)) == E_STRIDE
     assert fo(f8(ks=float("inf"))) == E_SHAPE
     assert fo(f8(vs=float("nan"))) == E_SHAPE

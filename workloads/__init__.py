@@ -270,6 +270,19 @@ def dit_self_attn(device="cpu", seed: int = 105, n_tokens: int = 37810, heads: i
                      causal=False, k_channel_offset_var=2.0, device=device)
 
 
+def short_batch(device="cpu", seed: int = 106, n_seqs: int = 256, q_lo: int = 2, q_hi: int = 8,
+                lo: int = 1024, hi: int = 8192) -> PagedCase:
+    """Short multi-token runs (speculative decoding's verify step, small
+    chunks): 256 sequences x n query tokens uniform in [2, 8] at the tail of
+    KV lengths uniform in [1024, 8192], 32 q / 4 KV heads (G 8, so 16 to 64
+    packed rows per sequence and KV head), head_dim 128, causal."""
+    gen = torch.Generator().manual_seed(seed)
+    q_lens = _uniform_ints(gen, q_lo, q_hi, n_seqs)
+    kv_lens = _uniform_ints(gen, lo, hi, n_seqs)
+    return make_case("short_batch", seed, q_lens, kv_lens, 32, 4, 128, causal=True,
+                     table_cols=math.ceil(hi / PAGE_SIZE), device=device)
+
+
 def new_kv_tokens(case: PagedCase, seed: int, layout: str = "separate"):
     """Seeded K and V rows for the step's new tokens: bf16 [T, Hkv, D] each
     (T = the q rows of the case).  layout "separate" gives two contiguous
@@ -335,4 +348,5 @@ WORKLOADS = {
     "long_decode": long_decode,
     "chunked_prefill": chunked_prefill,
     "dit_self_attn": dit_self_attn,
+    "short_batch": short_batch,
 }
