@@ -238,31 +238,58 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout
 def run_write(name, steps, warmup):
     """The KV-cache write followed by attention in one call
     (attn_paged_fwd_write) on a workload's shape, with seeded new K/V rows
-    for every query token.  The line's value is the write kernel's rate:
-    every new K/V byte read once and written once."""
+    for every query token.  On the split-decode paths the write runs inside
+    the attention launch; the line also times the two-launch form (the write
+    kernel, then attention) on the same inputs.  value = the step's
+    algorithmic bytes (attention's, plus every new K/V byte read once and
+    written once) per second."""
     import paged_kv_gqa_fwd_amd as pa
     log("[bench] generating %s (with KV-cache write)" % name)
     case = workloads.WORKLOADS[name](device="cuda")
     k_new, v_new = workloads.new_kv_tokens(case, case.seed + 1000)
     out = torch.empty_like(case.q)
+    mq = max(case.max_q, 1)
 
     def step():
         pa.paged_attention_write(case.q, k_new, v_new, case.kv, case.block_table, case.seq_lens, case.cu_q,
-                                 max(case.max_q, 1), case.scale, case.causal, out=out)
+                                 mq, case.scale, case.causal, out=out)
+
+    def two_launch():
+        pa.kv_write(case.kv, k_new, v_new, case.block_table, case.seq_lens, case.cu_q, mq, q_like=case.q)
+        pa.paged_attention(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, mq, case.scale,
+                           case.causal, out=out)
 
     steps = _secondary_steps(_warm(step, warmup), steps)
     step_ms = _time_steps(step, steps)
     main_ms, comb_ms, write_ms = _kernel_times(step, steps)
+    _warm(two_launch, warmup, 0.1)
+    two_ms = _time_steps(two_launch, steps)
+    _, _, write_alone_ms = _kernel_times(two_launch, steps)
     written = sum(min(n, L) for n, L in zip(case.q_lens, case.kv_lens))
     wbytes = 2 * written * case.num_kv_heads * 2 * case.head_dim * 2
-    gbs = wbytes / (write_ms * 1e-3) / 1e9
-    return {"workload": name + "+kv_write", "value": round(gbs, 2),
-            "unit": "GB/s (write kernel)", "write_bytes": wbytes, "write_kernel_ms": round(write_ms, 4),
-            "ms_per_step": round(step_ms, 4), "steps": steps, "attention_ms": round(main_ms + comb_ms, 4),
-            "path": "kv_write + attention",
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "paged_kv_write_kernel",
-                         "kernel_ms": round(write_ms, 4)}}
+    abytes = algorithmic_bytes(case)
+    fused = write_ms == 0.0
+    res = {"workload": name + "+kv_write", "value": round((abytes + wbytes) / (step_ms * 1e-3) / 1e9, 2),
+           "unit": "GB/s (attention + write bytes)", "fused_write": fused, "write_bytes": wbytes,
+           "ms_per_step": round(step_ms, 4), "steps": steps, "two_launch_ms_per_step": round(two_ms, 4),
+           "gain_vs_two_launches": round(two_ms / step_ms - 1.0, 4),
+           "write_kernel_ms_two_launch": round(write_alone_ms, 4),
+           "write_kernel_GBps_two_launch": round(wbytes / (write_alone_ms * 1e-3) / 1e9, 2),
+           "attention_ms": round(main_ms + comb_ms, 4), "path": "kv_write fused into attention" if fused else
+           "kv_write kernel + attention"}
+    kern_ms = main_ms if fused else write_ms
+    if BOUND[name] == "hbm":
+        ach = (abytes + wbytes if fused else wbytes) / (kern_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "paged_decode_balanced_kernel (with the write)" if fused
+                           else "paged_kv_write_kernel", "kernel_ms": round(kern_ms, 4)}
+    else:
+        ach = wbytes / (write_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "paged_kv_write_kernel",
+                           "kernel_ms": round(write_ms, 4)}
+    return res
 
 
 def run_quant(steps, warmup, cpu_seconds=0.0):

@@ -417,8 +417,10 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
                           block_table: torch.Tensor, seq_lens: torch.Tensor, cu_q: torch.Tensor, max_q: int,
                           scale: float, causal: bool = True, out: Optional[torch.Tensor] = None,
                           stream: Optional[torch.cuda.Stream] = None, k_scale: float = 1.0,
-                          v_scale: float = 1.0) -> torch.Tensor:
-    """The cache write then attention in one call (``attn_paged_fwd_write_opt``)."""
+                          v_scale: float = 1.0, path: int = PATH_AUTO, pages_per_split: int = 0,
+                          sinks: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
+    """The cache write then attention in one call (``attn_paged_fwd_write_opt``;
+    on the split paths the write runs inside the attention launch)."""
     lib = load_library()
     _check_device_tensor("q", q, torch.bfloat16)
     kv_dtype = _pool_dtype(kv_pool)
@@ -426,8 +428,13 @@ def paged_attention_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
         out = torch.zeros_like(q)
     dims = make_dims(q, kv_pool, block_table, out)
     nd = _new_kv_dims(k_new, v_new)
-    plan = make_plan(dims, seq_lens.numel(), max_q, kv_dtype=kv_dtype)
-    opt = attn_paged_options(None, 0, 0, 0, kv_dtype, float(k_scale), float(v_scale))
+    plan = make_plan(dims, seq_lens.numel(), max_q, path, pages_per_split, window, kv_dtype)
+    sinks_ptr = None
+    if sinks is not None:
+        _check_device_tensor("sinks", sinks, torch.float32)
+        sinks_ptr = sinks.data_ptr()
+    opt = attn_paged_options(sinks_ptr, int(window), int(path), int(pages_per_split), kv_dtype, float(k_scale),
+                             float(v_scale))
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     ws_ptr, ws_bytes, cached = None, 0, None
     if plan.workspace_bytes:

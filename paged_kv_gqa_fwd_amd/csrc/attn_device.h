@@ -101,6 +101,12 @@ struct AttnArgs {
     float v_scale;              // V = v_scale * e4m3(code) (1 for a bf16 pool); k_scale is in scale_log2
     int32_t *seg_splits;        // balanced split path: [B] pieces per sequence (1 = written directly, 0 = no page)
     int32_t row_blocks;         // split paths: blocks of 16 packed rows per workgroup (1, 2 or 4)
+    // Fused KV-cache write (split paths; null k_new = none): the step's new
+    // K/V rows [T, Hkv, D] bf16, written into the pool by the workgroup that
+    // streams their page, which attends to them in place of the slots' old bits.
+    const uint16_t *k_new, *v_new;
+    int64_t kn_st, kn_sh, vn_st, vn_sh;
+    float k_inv, v_inv;         // fp8 cache: codes of x * (1 / scale)
 };
 
 struct CombineArgs {

@@ -23,6 +23,7 @@
 // online softmax state; the waves of a row block merge in LDS at the end.
 // Per wave the registers are those of one row block whatever RB is.
 #include "attn_device.h"
+#include "kv_quant.h"
 
 namespace pa {
 
@@ -104,10 +105,12 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint3
 // Write a staged page into the LDS K and V tiles.  Slots at or past `valid`
 // (the tail of a sequence's last page) stage as zeros: their memory may hold
 // anything, and a non-finite V would turn the zero softmax weight of a
-// masked key into NaN in P.V.
+// masked key into NaN in P.V.  Slots in [valid_old, valid) are skipped: they
+// are the step's new tokens under a fused KV-cache write, whose rows the
+// holders of the new rows write (valid_old = valid without one).
 template <int D, bool F8, bool MASK>
 __device__ __forceinline__ void store_page_impl(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
-                                                uint16_t *ks, uint16_t *vs, int tid, int valid) {
+                                                uint16_t *ks, uint16_t *vs, int tid, int valid, int valid_old) {
     using C = DecodeCfg<D, F8>;
 #pragma unroll
     for (int it = 0; it < C::CH_PER_THREAD; ++it) {
@@ -116,6 +119,7 @@ __device__ __forceinline__ void store_page_impl(const u32x4 (&stage)[(DecodeCfg<
         const int kv = (c / C::DC) & 1;
         const int key = c / (2 * C::DC);
         uint16_t *dst = kv ? (vs + key * C::VROW + dc * C::EPC) : (ks + key * C::KROW + dc * C::EPC);
+        if (MASK && key >= valid_old && key < valid) continue;
         const u32x4 v = (!MASK || key < valid) ? stage[it] : u32x4{0u, 0u, 0u, 0u};
         if constexpr (!F8) {
             *reinterpret_cast<u32x4 *>(dst) = v;
@@ -131,15 +135,87 @@ __device__ __forceinline__ void store_page_impl(const u32x4 (&stage)[(DecodeCfg<
     }
 }
 
-// `valid` is uniform across the workgroup: a full page takes the branch
-// without the per-chunk selects.
+// `valid` and `valid_old` are uniform across the workgroup: a full page
+// without new tokens takes the branch without the per-chunk selects.
 template <int D, bool F8>
 __device__ __forceinline__ void store_page(const u32x4 (&stage)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
-                                           uint16_t *ks, uint16_t *vs, int tid, int valid) {
-    if (valid >= kPage)
-        store_page_impl<D, F8, false>(stage, ks, vs, tid, valid);
+                                           uint16_t *ks, uint16_t *vs, int tid, int valid, int valid_old) {
+    if (valid >= kPage && valid_old >= kPage)
+        store_page_impl<D, F8, false>(stage, ks, vs, tid, valid, valid_old);
     else
-        store_page_impl<D, F8, true>(stage, ks, vs, tid, valid);
+        store_page_impl<D, F8, true>(stage, ks, vs, tid, valid, min(valid_old, valid));
+}
+
+// One thread's share of a fused KV-cache write for one (sequence, KV head):
+// chunk c = tid of its new rows, token i = c / (2 DC), K (kv = 0) or V
+// (kv = 1) row, elements [EPC e, EPC e + EPC).  The bf16 input is loaded
+// when the piece starts; when the page holding key position `pos` is staged
+// the holder writes the value attention must see into the LDS tile (the
+// bf16 row, or the decoded e4m3 codes over an fp8 cache), and after the
+// piece its pool slot (bf16 or codes).  The host fuses the write only when
+// every chunk has a holder (n 2 DC <= 256).
+template <int D, bool F8>
+struct NewKV {
+    u32x4 val[F8 ? 2 : 1];   // the new row's EPC elements (bf16)
+    char *pool;              // the chunk's pool address once its page is staged, else null
+    int pos;                 // key position, or -1: no chunk (or a token with no slot)
+    int kv, e;
+};
+
+template <int D, bool F8>
+__device__ __forceinline__ void load_new_kv(const AttnArgs &a, int q0, int n, int L, int g, int tid,
+                                            NewKV<D, F8> &nk) {
+    using C = DecodeCfg<D, F8>;
+    nk.pos = -1;
+    nk.pool = nullptr;
+    nk.kv = (tid / C::DC) & 1;
+    nk.e = tid % C::DC;
+    if (!a.k_new) return;   // uniform: no fused write
+    const int i = tid / (2 * C::DC);
+    const int pos = L - n + i;
+    if (i < n && pos >= 0) {
+        const int64_t t = q0 + i;
+        const uint16_t *src = (nk.kv ? a.v_new + t * a.vn_st + (int64_t)g * a.vn_sh
+                                     : a.k_new + t * a.kn_st + (int64_t)g * a.kn_sh) + C::EPC * nk.e;
+#pragma unroll
+        for (int w = 0; w < (F8 ? 2 : 1); ++w) nk.val[w] = *reinterpret_cast<const u32x4 *>(src + 8 * w);
+        nk.pos = pos;
+    }
+}
+
+// While page p (id pid) is staged: the holder of a new slot in it writes the
+// slot's LDS row and remembers its pool address.
+template <int D, bool F8>
+__device__ __forceinline__ void new_kv_stage(const AttnArgs &a, NewKV<D, F8> &nk, uint16_t *ks, uint16_t *vs,
+                                             const char *head_base, int p, int pid) {
+    using C = DecodeCfg<D, F8>;
+    const int key = nk.pos - p * kPage;
+    if (key < 0 || key >= kPage) return;
+    uint16_t *dst = nk.kv ? (vs + key * C::VROW + nk.e * C::EPC) : (ks + key * C::KROW + nk.e * C::EPC);
+    if constexpr (!F8) {
+        *reinterpret_cast<u32x4 *>(dst) = nk.val[0];
+    } else {
+        const u32x4 codes = bf16x16_to_e4m3(nk.val[0], nk.val[1], nk.kv ? a.v_inv : a.k_inv);
+        uint32_t o[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) e4m3x4_to_bf16x4(codes[q4], o[2 * q4], o[2 * q4 + 1]);
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+    nk.pool = const_cast<char *>(head_base) +
+              ((int64_t)pid * a.kv_sp + (int64_t)key * a.kv_ss + nk.kv * a.kv_skv) * C::EB + nk.e * 16;
+}
+
+// After the piece: the holder stores its slot into the pool (a 16-byte
+// store; outside the page ring, so the ring's load counts stay exact).
+template <int D, bool F8>
+__device__ __forceinline__ void new_kv_commit(const AttnArgs &a, NewKV<D, F8> &nk) {
+    if (!nk.pool) return;
+    if constexpr (!F8)
+        *reinterpret_cast<u32x4 *>(nk.pool) = nk.val[0];
+    else
+        *reinterpret_cast<u32x4 *>(nk.pool) = bf16x16_to_e4m3(nk.val[0], nk.val[1], nk.kv ? a.v_inv : a.k_inv);
+    nk.pool = nullptr;
 }
 
 // Per-page work of one wave: the RB blocks of 16 keys starting at key kw0 of
@@ -320,19 +396,30 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
 // page is read and zeroed in LDS), page ids come through the scalar cache,
 // read a compute phase ahead, and the ring has one exit.  Otherwise the
 // wait covers every load in flight and the ring drains at each page.
-template <int D, bool F8, int RB>
+template <int D, bool F8, int RB, bool W>
 __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t *ks, uint16_t *vs,
                                                     const char *head_base, const int32_t *bt_row, int p_begin,
                                                     int p_end, int L, const bf16x8 (&qreg)[D / 32],
                                                     f32x4 (&oacc)[D / 16], float &m_run, float &l_part, int vis,
                                                     int lo, int tid,
                                                     u32x4 (&st1)[(DecodeCfg<D, F8>::CH_PER_THREAD)],
-                                                    bool preloaded, int next_pid) {
+                                                    bool preloaded, int next_pid, NewKV<D, F8> &nk, int nv_lo) {
     using C = DecodeCfg<D, F8>;
     const int lane = tid & 63;
     const int kw0 = decode_key_offset<RB>(tid >> 6);
     auto compute_page = [&](int p) {
         decode_compute_page<D, F8, RB>(ks, vs, qreg, oacc, m_run, l_part, p, vis, lo, a.scale_log2, kw0, lane);
+    };
+    // Stage page p from a register stage; under a fused KV-cache write (W)
+    // the slots of new tokens (key positions [nv_lo, L)) come from their holders.
+    auto stage_page = [&](const u32x4 (&stg)[C::CH_PER_THREAD], int p) {
+        if constexpr (W) {
+            store_page<D, F8>(stg, ks, vs, tid, L - p * kPage, nv_lo - p * kPage);
+            if (nv_lo < L && (p + 1) * kPage > nv_lo)   // uniform: the page holds new tokens
+                new_kv_stage<D, F8>(a, nk, ks, vs, head_base, p, load_invariant_i32(bt_row + p));
+        } else {
+            store_page<D, F8>(stg, ks, vs, tid, L - p * kPage, L - p * kPage);
+        }
     };
     const int64_t sp = a.kv_sp;
     const int p_last = p_end - 1;
@@ -360,7 +447,7 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
                 const bool live = p < p_end;
                 if (live) {
                     __syncthreads();             // the previous page is fully consumed
-                    store_page<D, F8>(st[k], ks, vs, tid, L - p * kPage);
+                    stage_page(st[k], p);
                     __syncthreads();
                 }
                 refill(st[k], p + C::STAGES);
@@ -377,14 +464,14 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
         int pid_a = load_invariant_i32(bt_row + min(p_begin + 2, p_last));
         for (int p = p_begin; p < p_end; p += 2) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(stA, ks, vs, tid, L - p * kPage);
+            stage_page(stA, p);
             __syncthreads();
             load_id(stA, pid_a);
             const int pid_b = load_invariant_i32(bt_row + min(p + 3, p_last));
             compute_page(p);
             if (p + 1 >= p_end) break;       // uniform across the workgroup
             __syncthreads();
-            store_page<D, F8>(stB, ks, vs, tid, L - (p + 1) * kPage);
+            stage_page(stB, p + 1);
             __syncthreads();
             load_id(stB, pid_b);
             pid_a = load_invariant_i32(bt_row + min(p + 4, p_last));
@@ -404,7 +491,7 @@ __device__ __forceinline__ void decode_stream_pages(const AttnArgs &a, uint16_t 
         int pid = pid_after(p_begin + 1);
         for (int p = p_begin; p < p_end; ++p) {
             __syncthreads();                 // the previous page is fully consumed
-            store_page<D, F8>(st1, ks, vs, tid, L - p * kPage);
+            stage_page(st1, p);
             __syncthreads();
             load_id(st1, pid);
             pid = pid_after(p + 2);
@@ -438,7 +525,7 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs &a, int q0, int n, in
     }
 }
 
-template <int D, bool F8, int RB>
+template <int D, bool F8, int RB, bool W>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(decode_waves(D, F8, RB))))
 void paged_decode_split_kernel(const AttnArgs a) {
@@ -489,9 +576,12 @@ void paged_decode_split_kernel(const AttnArgs a) {
     float m_run = -INFINITY;   // running max (log2 units) of this wave's keys, per row
     float l_part = 0.f;        // this lane's share of the running sum
 
+    NewKV<D, F8> nk;
+    if constexpr (W) load_new_kv<D, F8>(a, q0, n, L, g, tid, nk);
     u32x4 st1[C::CH_PER_THREAD];
-    decode_stream_pages<D, F8, RB>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part, vis,
-                                   lo, tid, st1, false, -1);
+    decode_stream_pages<D, F8, RB, W>(a, ks, vs, head_base, bt_row, p_begin, p_end, L, qreg, oacc, m_run, l_part,
+                                      vis, lo, tid, st1, false, -1, nk, W ? L - n : L);
+    if constexpr (W) new_kv_commit<D, F8>(a, nk);
 
     // ---- merge the waves' (m, l, O) in LDS, write -------------------------
     const bool split = a.max_splits > 1;
@@ -567,7 +657,7 @@ void paged_decode_split_kernel(const AttnArgs a) {
 // LDS prefix sum over at most kBalMaxSeqs sequences), so nothing but the
 // launch orders the two kernels.  Workgroup (0, 0) publishes each
 // sequence's piece count for the combine kernel.
-template <int D, bool F8, int RB>
+template <int D, bool F8, int RB, bool W>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(decode_waves(D, F8, RB))))
 void paged_decode_balanced_kernel(const AttnArgs a) {
@@ -686,8 +776,12 @@ void paged_decode_balanced_kernel(const AttnArgs a) {
         for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m_run = -INFINITY;
         float l_part = 0.f;
-        decode_stream_pages<D, F8, RB>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p, p + cnt,
-                                       L, qreg, oacc, m_run, l_part, vis, lo, tid, st1, preloaded, next_pid);
+        NewKV<D, F8> nk;
+        if constexpr (W) load_new_kv<D, F8>(a, q0, n, L, g, tid, nk);
+        decode_stream_pages<D, F8, RB, W>(a, ks, vs, head_base, a.block_table + (int64_t)b * a.bt_stride, p,
+                                          p + cnt, L, qreg, oacc, m_run, l_part, vis, lo, tid, st1, preloaded,
+                                          next_pid, nk, W ? L - n : L);
+        if constexpr (W) new_kv_commit<D, F8>(a, nk);
         // The piece: the whole sequence (written out) or split slot
         // r - floor(F_b / C) of its ns pieces.
         const int ns = (F0 + np - 1) / Cr - F0 / Cr + 1;
@@ -768,37 +862,51 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
 
 // Row blocks of 16 packed rows: one for decode (<= 16 rows), two or four for
 // the short-sequence body (<= 32 / <= 64 rows).
-template <int D, bool F8>
+template <int D, bool F8, bool W>
 hipError_t launch_decode_split_rb(const AttnArgs &a, dim3 grid, hipStream_t stream) {
     if (a.row_blocks <= 1)
-        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 1>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 1, W>), grid, dim3(kThreads), 0, stream, a);
     else if (a.row_blocks == 2)
-        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 2>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 2, W>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 4>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_split_kernel<D, F8, 4, W>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, bool F8>
+template <int D, bool F8, bool W>
 hipError_t launch_decode_balanced_rb(const AttnArgs &a, dim3 grid, hipStream_t stream) {
     if (a.row_blocks <= 1)
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 1>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 1, W>), grid, dim3(kThreads), 0, stream, a);
     else if (a.row_blocks == 2)
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 2>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 2, W>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 4>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<D, F8, 4, W>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+// The kernels with the fused KV-cache write are separate instantiations, so
+// the plain decode kernels carry none of its state.
+template <int D, bool F8>
+hipError_t launch_decode_split_w(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    return a.k_new ? launch_decode_split_rb<D, F8, true>(a, grid, stream)
+                   : launch_decode_split_rb<D, F8, false>(a, grid, stream);
+}
+
+template <int D, bool F8>
+hipError_t launch_decode_balanced_w(const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    return a.k_new ? launch_decode_balanced_rb<D, F8, true>(a, grid, stream)
+                   : launch_decode_balanced_rb<D, F8, false>(a, grid, stream);
 }
 
 template <int D>
 hipError_t launch_decode_split(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    return a.kv_fp8 ? launch_decode_split_rb<D, true>(a, grid, stream) : launch_decode_split_rb<D, false>(a, grid, stream);
+    return a.kv_fp8 ? launch_decode_split_w<D, true>(a, grid, stream) : launch_decode_split_w<D, false>(a, grid, stream);
 }
 
 template <int D>
 hipError_t launch_decode_balanced(const AttnArgs &a, dim3 grid, hipStream_t stream) {
-    return a.kv_fp8 ? launch_decode_balanced_rb<D, true>(a, grid, stream)
-                    : launch_decode_balanced_rb<D, false>(a, grid, stream);
+    return a.kv_fp8 ? launch_decode_balanced_w<D, true>(a, grid, stream)
+                    : launch_decode_balanced_w<D, false>(a, grid, stream);
 }
 
 template <int D>

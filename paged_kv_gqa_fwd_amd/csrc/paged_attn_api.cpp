@@ -555,6 +555,29 @@ int quant_attend_impl(void *out, const attn_quant_dims *d, float scale, int32_t 
     return ATTN_OK;
 }
 
+// ---- KV-cache write fused into the split-decode launch ----------------------
+// The split kernels can take the step's new K/V rows themselves when every
+// 16-byte chunk of one (sequence, KV head)'s new rows has a holder thread:
+// n * 2 * (D / elements per chunk) <= 256 (decode, and short runs of up to
+// 8 tokens at D = 128, 4 at D = 256; twice that over an fp8 cache).
+bool write_fusable(const attn_paged_plan &plan, const attn_paged_dims *d, int32_t max_q, int32_t kv_dtype) {
+    const bool split = plan.path == ATTN_PATH_SPLIT_DECODE || plan.path == ATTN_PATH_SPLIT_FUSED ||
+                       plan.path == ATTN_PATH_SPLIT_BALANCED;
+    const int64_t epc = kv_dtype == ATTN_KV_FP8_E4M3 ? 16 : 8;
+    return split && (int64_t)std::max<int32_t>(max_q, 1) * 2 * (d->head_dim / epc) <= pa::kThreads;
+}
+
+void fuse_write(pa::AttnArgs &a, const pa::KvWriteArgs &w) {
+    a.k_new = w.k_new;
+    a.v_new = w.v_new;
+    a.kn_st = w.k_st;
+    a.kn_sh = w.k_sh;
+    a.vn_st = w.v_st;
+    a.vn_sh = w.v_sh;
+    a.k_inv = w.k_inv;
+    a.v_inv = w.v_inv;
+}
+
 // ---- allocation-free entry point ------------------------------------------
 // The split-KV partials of attn_paged_fwd_noalloc live in this library-owned
 // device array (one copy per GPU, resident from the code object's load on
@@ -718,6 +741,10 @@ int attn_paged_fwd_write(void *out, const void *q, const void *k_new, const void
                        workspace, workspace_bytes, ATTN_PATH_AUTO, 0, nullptr, 0, plan, a);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (write_fusable(plan, dims, max_q, ATTN_KV_BF16)) {
+        fuse_write(a, w);   // one launch: the split kernel writes the new rows it streams
+        return paged_launch(plan, a, dims->head_dim, st);
+    }
     rc = kv_write_launch(w, st);
     if (rc != ATTN_OK) return rc;
     return paged_launch(plan, a, dims->head_dim, st);
@@ -753,6 +780,10 @@ int attn_paged_fwd_write_opt(void *out, const void *q, const void *k_new, const 
                        plan, a, opt->kv_dtype, opt->k_scale, opt->v_scale);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (write_fusable(plan, dims, max_q, opt->kv_dtype)) {
+        fuse_write(a, w);
+        return paged_launch(plan, a, dims->head_dim, st);
+    }
     rc = kv_write_launch(w, st);
     if (rc != ATTN_OK) return rc;
     return paged_launch(plan, a, dims->head_dim, st);
