@@ -55,6 +55,13 @@
 
 namespace pa {
 
+#ifndef PA_PREFILL_PREFETCH
+#define PA_PREFILL_PREFETCH 2
+#endif
+#ifndef PA_PF_TILE_PAGES128
+#define PA_PF_TILE_PAGES128 2
+#endif
+
 template <int D>
 struct PfCfg {
     static constexpr int WAVES = D == 128 ? PA_PF_WAVES128 : PA_PF_WAVES256;
@@ -68,10 +75,17 @@ struct PfCfg {
     static constexpr int CH = D / 8;                // 16-byte chunks per K or V row
     static constexpr int TILE = kPage * D;          // bf16 elements of one K (or V) page
     static constexpr int LOADS = kPage * CH / THREADS;  // 16-byte loads per thread per K page
-    // Pages in flight beyond the next one, and the K / V ring depths that
-    // allow it with the step pipeline below (K of page t+1 and V of page t
+    // The K/V ring's unit: a tile of TP pages (64 TP keys, SPT = 2 TP
+    // 32-key steps), published by one workgroup barrier per tile.  At
+    // D = 128 two pages per tile halve the barriers per key (and their wave
+    // skew) at the LDS of the one-page ring with two pages of lead; at
+    // D = 256 a page already fills the LDS.
+    static constexpr int TP = D == 128 ? PA_PF_TILE_PAGES128 : 1;
+    static constexpr int SPT = 2 * TP;
+    // Tiles in flight beyond the next one, and the K / V ring depths that
+    // allow it with the step pipeline below (K of tile t+1 and V of tile t
     // are read in the same step).
-    static constexpr int LEAD = D == 128 ? 2 : 1;
+    static constexpr int LEAD = (D == 128 && TP == 1) ? 2 : 1;
     static constexpr int NK = LEAD + 1;
     static constexpr int NV = LEAD + 2;
     // D = 256 (one page of lead): a page's V rows are first read a page
@@ -83,9 +97,6 @@ struct PfCfg {
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
-#ifndef PA_PREFILL_PREFETCH
-#define PA_PREFILL_PREFETCH 2
-#endif
 
 constexpr float kRescaleThreshold = 8.f;   // log2 units: P stays <= 256
 
@@ -147,8 +158,8 @@ __device__ __forceinline__ void pf_load_v(uint16_t *lds_v, const uint16_t *vbase
 template <int D>
 __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(const AttnArgs a) {
     using C = PfCfg<D>;
-    __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TP * C::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TP * C::TILE];
 
     const int g = blockIdx.y;
     const int b = blockIdx.z;
@@ -189,10 +200,11 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     // every row's window; pages below the workgroup's first row's window
     // start are never loaded (0 and page 0 without a window)
     const int w_lo = window_start(L - n + min(R - 1, r0 + 32 * C::RB * (w + 1) - 1) / G, a.window);
-    const int t0 = window_start(L - n + r0 / G, a.window) / kPage;
-    const int j0 = 2 * t0;                     // first 32-key step
+    const int t0 = window_start(L - n + r0 / G, a.window) / (kPage * C::TP);
+    const int j0 = C::SPT * t0;                // first 32-key step
     const int nsteps = (kv_end + 31) / 32;     // 32-key softmax steps
-    const int ntiles = (nsteps + 1) / 2;       // 64-key pages
+    const int ntiles = (nsteps + C::SPT - 1) / C::SPT;   // ring tiles of TP pages
+    const int npages = (kv_end + kPage - 1) / kPage;      // pages with a key some row sees
 
     const uint16_t *head_base = a.kv + (int64_t)g * a.kv_sh;
     const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
@@ -235,15 +247,25 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         pl.kof0[i] = (uint32_t)(ck * 8) * 2u;
         pl.vof0[i] = (uint32_t)(cv * 8) * 2u;
     }
-    auto issue_page = [&](int t) {
-        const int pid = load_page_id(bt_row, t);
+    auto issue_page = [&](int t) {   // tile t: pages TP t .. TP t + TP - 1
         if constexpr (C::SPLITV) {   // all of K, then all of V
+            const int pid = load_page_id(bt_row, t);
             pf_load_k<D>(sk[t % C::NK], head_base + (int64_t)pid * a.kv_sp, pl, w, L - t * kPage);
             pf_load_v<D, C::LOADS>(sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w,
                                    L - t * kPage, 0);
         } else {
-            pf_load_page<D>(sk[t % C::NK], sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp, pl,
-                            a.kv_skv, w, L - t * kPage);
+#pragma unroll
+            for (int pp = 0; pp < C::TP; ++pp) {
+                // A page of the last tile past the workgroup's last visible
+                // key is not named by the table: its slots re-read key 0 of
+                // the tile's first page (finite, weight zero), so every tile
+                // issues the same loads.
+                const int page = C::TP * t + pp;
+                const bool real = page < npages;
+                const int pid = load_page_id(bt_row, real ? page : C::TP * t);
+                pf_load_page<D>(sk[t % C::NK] + pp * C::TILE, sv[t % C::NV] + pp * C::TILE,
+                                head_base + (int64_t)pid * a.kv_sp, pl, a.kv_skv, w, real ? L - page * kPage : 0);
+            }
         }
     };
     // SPLITV: the page whose V rows are being issued over the two steps
@@ -258,12 +280,12 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     // Wait until page t has landed in LDS: pages t+1 .. `issued` were
     // issued after it and may stay in flight (loads complete in issue order).
     int issued = -1;
-    auto wait_page = [&](int t) {
+    auto wait_page = [&](int t) {   // tile t; TP pages of K and V rows per tile
         const int younger = issued - t;
         if (C::LEAD == 2 && younger == 2)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * C::LOADS) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * C::TP * C::LOADS) : "memory");
         else if (younger >= 1)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::TP * C::LOADS) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
@@ -319,8 +341,13 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         const bf16x4 hi4 = lds_read_tr16(v1 + 8 * D);
         return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    auto kstage = [&](int j) { return sk[(j >> 1) % C::NK] + (32 * (j & 1)) * D + klane; };
-    auto vstage = [&](int j) { return sv[(j >> 1) % C::NV] + (32 * (j & 1)) * D + vlane; };
+    // (steps are never negative: unsigned division by the power-of-two SPT is a shift)
+    auto kstage = [&](int j) {
+        return sk[((unsigned)j / C::SPT) % C::NK] + (32 * ((unsigned)j % C::SPT)) * D + klane;
+    };
+    auto vstage = [&](int j) {
+        return sv[((unsigned)j / C::SPT) % C::NV] + (32 * ((unsigned)j % C::SPT)) * D + vlane;
+    };
 
     // S^T = K Q^T for the 32 keys of step j (raw scores, f32); no overlap
     // (pipeline prologue).  s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4
@@ -509,7 +536,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                     vp_valid = L - (t + 2) * kPage;
                 }
             }
-        } else if (!(j & 1) && t + 1 < ntiles) {
+        } else if ((unsigned)j % C::SPT == C::SPT - 2 && (int)((unsigned)j / C::SPT) + 1 < ntiles) {
+            // tile version of the same boundary: after B(SPT t + SPT - 2)
+            // publish tile t+1, refill K tile t / V tile t-1's slots
+            const int t = (unsigned)j / C::SPT;
             wait_page(t + 1);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
@@ -530,8 +560,12 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
         // Two steps per page; the S registers alternate roles between them.
         for (int t = t0; t < ntiles; ++t) {
-            step(2 * t, sA, sB);
-            if (2 * t + 1 < nsteps) step(2 * t + 1, sB, sA);
+            step(C::SPT * t, sA, sB);
+            if (C::SPT * t + 1 < nsteps) step(C::SPT * t + 1, sB, sA);
+            if constexpr (C::SPT == 4) {
+                if (C::SPT * t + 2 < nsteps) step(C::SPT * t + 2, sA, sB);
+                if (C::SPT * t + 3 < nsteps) step(C::SPT * t + 3, sB, sA);
+            }
         }
         pv(nsteps - 1, pb);
     }
