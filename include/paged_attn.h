@@ -227,9 +227,12 @@ typedef struct attn_paged_options {
  * (1 byte; dims' kv strides then count bytes and must be multiples of 16),
  * with one scale for all of K and one for all of V (the Mojo SM100MHA2Q docs
  * carry fp8 branches of the KV dtype; per-tensor scales are the reading taken
- * here).  Supported on the split-decode paths (packed rows G * max_q <= 64);
- * a call that would take the prefill path returns ATTN_ERR_UNSUPPORTED.
- * Scales must be finite.
+ * here).  Supported on every path.  The split-decode paths (packed rows
+ * G * max_q <= 64) read the codes directly; the prefill path first decodes
+ * the pages it reads (exactly: every e4m3 value is a bf16 value) into a
+ * bf16 staging pool in the workspace, so its plan's workspace_bytes is
+ * n_seqs * max_pages_per_seq * (P * Hkv * 2 * D * 2 + 4) bytes (each part
+ * 256-byte aligned).  Scales must be finite.
  */
 enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3 = 1 };
 

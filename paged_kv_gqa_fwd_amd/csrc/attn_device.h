@@ -107,6 +107,13 @@ struct AttnArgs {
     const uint16_t *k_new, *v_new;
     int64_t kn_st, kn_sh, vn_st, vn_sh;
     float k_inv, v_inv;         // fp8 cache: codes of x * (1 / scale)
+    // Prefill over an fp8 cache: the pages the call reads are first decoded
+    // (exactly) into a bf16 staging pool in the workspace, [n_seqs * MP]
+    // pages of [P, Hkv, 2, D], with its own table [n_seqs, MP] (page b*MP + j
+    // for page j of sequence b; -1 for pages not staged).  Null = none.
+    uint16_t *stage_kv;
+    int32_t *stage_bt;
+    int32_t mp;                 // block-table columns (the staging pool's pages per sequence)
 };
 
 struct CombineArgs {

@@ -94,13 +94,6 @@ __device__ __forceinline__ void load_page(u32x4 (&stage)[(DecodeCfg<D, F8>::CH_P
     }
 }
 
-// Four OCP e4m3 codes (one 32-bit word) to four bf16 (two words), exactly:
-// every e4m3 value is a bf16 value (one conversion instruction per pair,
-// with a unit scale).
-__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));  // bytes 0, 1
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));   // bytes 2, 3
-}
 
 // Write a staged page into the LDS K and V tiles.  Slots at or past `valid`
 // (the tail of a sequence's last page) stage as zeros: their memory may hold

@@ -1,6 +1,6 @@
-// Device helpers of the quantising KV-cache write (fp8 cache): bf16 rows to
-// OCP e4m3 codes of x * (1 / scale).  Shared by the write kernel and the
-// split-decode kernels' fused write.  Internal to the library.
+// Device helpers of the fp8 (OCP e4m3) KV cache: bf16 rows to codes of
+// x * (1 / scale) (the quantising write, also fused into the split-decode
+// kernels) and codes back to bf16, exactly.  Internal to the library.
 #pragma once
 
 #include "attn_device.h"
@@ -31,6 +31,14 @@ __device__ __forceinline__ u32x4 bf16x16_to_e4m3(const u32x4 a, const u32x4 b, f
         r[w] = (uint32_t)word;
     }
     return r;
+}
+
+// Four OCP e4m3 codes (one 32-bit word) to four bf16 (two words), exactly:
+// every e4m3 value is a bf16 value (one conversion instruction per pair,
+// with a unit scale).
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));  // bytes 0, 1
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));   // bytes 2, 3
 }
 
 }  // namespace pa

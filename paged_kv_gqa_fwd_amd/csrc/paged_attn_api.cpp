@@ -23,6 +23,7 @@ hipError_t launch_decode_balanced_any(int D, const AttnArgs &a, dim3 grid, hipSt
 hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
 hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream);
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
+hipError_t launch_fp8_stage_any(int D, const AttnArgs &a, hipStream_t stream);
 hipError_t launch_quant_prep(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_quant_attn(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
@@ -124,7 +125,6 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     const bool split_path = path == ATTN_PATH_SPLIT_DECODE || path == ATTN_PATH_SPLIT_FUSED || balanced;
     if (split_path && mq * G > kMaxDecodeRows) return ATTN_ERR_UNSUPPORTED;
     if (balanced && !balanced_fits(d, n_seqs, mq, window)) return ATTN_ERR_UNSUPPORTED;
-    if (!split_path && kv_dtype != ATTN_KV_BF16) return ATTN_ERR_UNSUPPORTED;   // prefill reads bf16 only
     *plan = attn_paged_plan{};
     plan->path = path;
     plan->block_threads = pa::kThreads;
@@ -184,8 +184,17 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
     } else {
         // The prefill kernel addresses a page's K/V rows with 32-bit byte
         // offsets from the page's base (one VGPR per direct-to-LDS load):
-        // 63 slot strides plus one row must stay below 4 GiB.
-        if ((63 * d->kv_stride_slot + d->head_dim) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+        // 63 slot strides plus one row must stay below 4 GiB.  Over an fp8
+        // cache it reads the bf16 staging pool ([P, Hkv, 2, D] pages).
+        const bool f8 = kv_dtype == ATTN_KV_FP8_E4M3;
+        const int64_t ss = f8 ? (int64_t)d->num_kv_heads * 2 * d->head_dim : d->kv_stride_slot;
+        if ((63 * ss + d->head_dim) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+        if (f8) {
+            // [staging pool: n_seqs * MP pages of P * Hkv * 2 * D bf16 | staging table: n_seqs * MP i32]
+            const size_t pages = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)d->max_pages_per_seq;
+            plan->workspace_bytes = align_up(pages * (size_t)pa::kPage * (size_t)ss * 2, kWsAlign) +
+                                    align_up(pages * 4, kWsAlign);
+        }
         const int64_t bm = pa::prefill_rows(d->head_dim);
         const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -280,13 +289,23 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     // The prefill kernel takes the maximum of raw scores and applies the
     // scale afterwards, which needs a positive scale: a negative one is
     // applied by negating Q (exact), and zero as the smallest normal float
-    // (every weight is then exactly 1 unless |q.k| exceeds about 1e30).
-    a.scale_log2_pos = std::max((float)(std::fabs((double)scale) * 1.4426950408889634), FLT_MIN);
-    a.q_negate = scale < 0.f ? 1 : 0;
+    // (every weight is then exactly 1 unless |q.k| exceeds about 1e30).  An
+    // fp8 cache's k_scale joins the score scale (1 for bf16).
+    const double eff_scale = (double)scale * (double)k_scale;
+    a.scale_log2_pos = std::max((float)(std::fabs(eff_scale) * 1.4426950408889634), FLT_MIN);
+    a.q_negate = eff_scale < 0.0 ? 1 : 0;
     a.sinks = sinks;
     a.window = effective_window(dims, window);
     a.row_blocks = pa::decode_row_blocks((int64_t)std::max<int32_t>(max_q, 1) * G);
-    if (plan.workspace_bytes > 0) {
+    a.mp = dims->max_pages_per_seq;
+    if (plan.path == ATTN_PATH_PREFILL && plan.workspace_bytes > 0) {
+        // prefill over an fp8 cache: [staging pool | staging table]
+        const size_t pages = (size_t)n_seqs * (size_t)dims->max_pages_per_seq;
+        const size_t pool_bytes = pages * (size_t)pa::kPage * (size_t)dims->num_kv_heads * 2 * (size_t)D * 2;
+        char *ws = static_cast<char *>(workspace);
+        a.stage_kv = reinterpret_cast<uint16_t *>(ws);
+        a.stage_bt = reinterpret_cast<int32_t *>(ws + align_up(pool_bytes, kWsAlign));
+    } else if (plan.workspace_bytes > 0) {
         // [merge counters or pieces per sequence | partial O | partial (m, l)],
         // each 256-byte aligned
         const size_t rows = (size_t)n_seqs * (size_t)max_q * (size_t)dims->num_q_heads * (size_t)plan.max_splits;
@@ -310,10 +329,35 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
     const dim3 grid(plan.grid_x, plan.grid_y, plan.grid_z);
     const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
-    if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
-    hipError_t e = plan.path == ATTN_PATH_PREFILL            ? pa::launch_prefill_any(D, a, grid, st)
-                   : plan.path == ATTN_PATH_SPLIT_BALANCED ? pa::launch_decode_balanced_any(D, a, grid, st)
-                                                           : pa::launch_decode_split_any(D, a, grid, st);
+    hipError_t e;
+    if (plan.path == ATTN_PATH_PREFILL && a.stage_kv) {
+        // Over an fp8 cache: decode the pages the prefill reads into the bf16
+        // staging pool (timed as preparation), then prefill from it.
+        TimedLaunch t_stage{};
+        if (timing && record_event(&t_stage.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+        if (pa::launch_fp8_stage_any(D, a, st) != hipSuccess) return ATTN_ERR_HIP;
+        if (timing) {
+            if (record_event(&t_stage.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+            t_stage.kind = kTimedPrep;
+            timing_push(t_stage);
+        }
+        pa::AttnArgs b = a;
+        b.kv = a.stage_kv;
+        b.kv_ss = (int64_t)a.hkv * 2 * D;
+        b.kv_sp = (int64_t)pa::kPage * b.kv_ss;
+        b.kv_sh = 2 * D;
+        b.kv_skv = D;
+        b.block_table = a.stage_bt;
+        b.bt_stride = a.mp;
+        b.kv_fp8 = 0;
+        if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+        e = pa::launch_prefill_any(D, b, grid, st);
+    } else {
+        if (timing && record_event(&t_main.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+        e = plan.path == ATTN_PATH_PREFILL            ? pa::launch_prefill_any(D, a, grid, st)
+            : plan.path == ATTN_PATH_SPLIT_BALANCED ? pa::launch_decode_balanced_any(D, a, grid, st)
+                                                    : pa::launch_decode_split_any(D, a, grid, st);
+    }
     if (e != hipSuccess) return ATTN_ERR_HIP;
     if (timing && record_event(&t_main.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
     const bool need_combine = (plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1) ||

@@ -51,6 +51,7 @@
 //  * Keys past the causal frontier of the workgroup's last row are never
 //    loaded; steps below the frontier of a wave's first row skip the mask.
 #include "attn_device.h"
+#include "kv_quant.h"
 #include "lds_stream.h"
 
 namespace pa {
@@ -581,7 +582,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const float sink2 = a.sinks[h_[rb]] * kLog2e;
             if (sink2 != -INFINITY) l_row += exp2_fast(sink2 - m_ref[rb]);
         }
-        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+        // v_scale: V = v_scale * e4m3(code) over an fp8 cache (1 for bf16)
+        const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
         uint16_t *op = a.out + (int64_t)(q0 + qi_[rb]) * a.o_st + (int64_t)h_[rb] * a.o_sh;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -596,6 +598,61 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             }
         }
     }
+}
+
+// ---- prefill over an fp8 cache: stage the pages as bf16 ---------------------
+// Workgroup (j, b) decodes page j of sequence b, all KV heads, K and V, from
+// e4m3 codes into bf16 (exactly: every e4m3 value is a bf16 value; the
+// scales stay out, k_scale in the score scale and v_scale in the output) at
+// staging page b * MP + j, and writes that index into the staging table.
+// Pages the prefill kernel cannot read are not staged and keep -1: those of
+// sequences with no query, those past the sequence's keys, and those below
+// the window start of the sequence's first query (rounded down to a
+// two-page ring tile).  The kernel then reads the staging pool exactly as
+// a bf16 pool.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fp8_stage_pages_kernel(const AttnArgs a) {
+    const int j = blockIdx.x;
+    const int b = blockIdx.y;
+    const int L = a.seq_lens[b];
+    const int q0 = a.cu_q[b];
+    int n = a.cu_q[b + 1] - q0;
+    if (n > a.max_q) n = a.max_q;
+    const int npages = (L + kPage - 1) / kPage;
+    const int p_lo = split_first_page(L, n, a.window) & ~1;
+    const bool staged = n > 0 && j >= p_lo && j < npages;
+    const int64_t si = (int64_t)b * a.mp + j;
+    if (threadIdx.x == 0) a.stage_bt[si] = staged ? (int32_t)si : -1;
+    if (!staged) return;
+    const int pid = a.block_table[(int64_t)b * a.bt_stride + j];
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(a.kv) + (int64_t)pid * a.kv_sp;   // byte strides
+    constexpr int d = D;
+    constexpr int dc = D / 16;                           // 16-code chunks per row
+    const int per_slot = a.hkv * 2 * dc;
+    uint16_t *dst = a.stage_kv + si * ((int64_t)kPage * a.hkv * 2 * d);
+    for (int c = threadIdx.x; c < kPage * per_slot; c += kThreads) {
+        const int slot = c / per_slot;
+        const int r = c - slot * per_slot;
+        const int h = r / (2 * dc);
+        const int kv = (r / dc) & 1;
+        const int ch = r % dc;
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(src + (int64_t)slot * a.kv_ss + (int64_t)h * a.kv_sh +
+                                                        kv * a.kv_skv + 16 * ch);
+        uint32_t o[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) e4m3x4_to_bf16x4(w[q4], o[2 * q4], o[2 * q4 + 1]);
+        uint16_t *op = dst + ((int64_t)(slot * a.hkv + h) * 2 + kv) * d + 16 * ch;
+        *reinterpret_cast<u32x4 *>(op) = u32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4 *>(op + 8) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+}
+
+hipError_t launch_fp8_stage_any(int D, const AttnArgs &a, hipStream_t stream) {
+    if (D == 128)
+        hipLaunchKernelGGL(fp8_stage_pages_kernel<128>, dim3(a.mp, a.n_seqs), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(fp8_stage_pages_kernel<256>, dim3(a.mp, a.n_seqs), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int D>

@@ -345,9 +345,16 @@ def test_fp8_cache_options_validate(pa):
                                              kw.get("vs", 1.0))
     assert mp(f8()) == OK and plan.path == mod.PATH_SPLIT_BALANCED
     assert mp(f8(dtype=2)) == E_UNSUP
-    assert mp(f8(path=2)) == E_UNSUP                        # the prefill kernel reads bf16 only
     assert mp(f8(), max_q=16) == OK                         # 64 packed rows: the short-sequence body
-    assert mp(f8(), max_q=17) == E_UNSUP                    # 68 packed rows: prefill would be needed
+    # more rows take the prefill kernel, which reads the pages through a bf16
+    # staging pool in the workspace: 64 seqs x 128 pages x 64 slots x 8 heads
+    # x 2 x D 128 bf16, plus one i32 table entry per page
+    for kw in (dict(path=2), dict()):
+        assert mp(f8(**kw), max_q=17) == OK and plan.path == mod.PATH_PREFILL
+        pages = 64 * 128
+        assert plan.workspace_bytes == pages * 64 * 8 * 2 * 128 * 2 + pages * 4
+    bf = mod.attn_paged_options(None, 0, 2, 0, 0, 1.0, 1.0)
+    assert mp(bf) == OK and plan.workspace_bytes == 0       # a bf16 prefill needs no workspace
     assert mp(f8(), dd=dims(max_pages_per_seq=128, bt_stride=128, kv_stride_kv=136)) == E_STRIDE
     assert fo(f8(ks=float("inf"))) == E_SHAPE
     assert fo(f8(vs=float("nan"))) == E_SHAPE

@@ -1,5 +1,6 @@
-"""GPU parity of decode over an fp8 (OCP e4m3) paged KV cache against the
-fp64 oracle (same codes, same per-tensor scales), through the C ABI.
+"""GPU parity of attention over an fp8 (OCP e4m3) paged KV cache against the
+fp64 oracle (same codes, same per-tensor scales), through the C ABI: the
+split-decode paths and the prefill path (through its bf16 staging pool).
 
 Tolerance: the bf16 bar (max-abs 2e-2, rel-RMS 5e-3).  The dequantisation
 is exact (every e4m3 value is a bf16 value; the scales enter the scores and
@@ -110,13 +111,54 @@ def test_every_code_decodes_exactly():
             assert torch.equal(out[b, h].cpu().float(), expect[b].float()), (b, h)
 
 
-def test_fp8_prefill_is_unsupported():
+# ---------------------------------------------- prefill over an fp8 cache
+# The prefill kernel reads an fp8 cache through a bf16 staging pool: the
+# pages it reads are decoded (exactly) into the workspace first, k_scale joins
+# the score scale and v_scale the output.
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_fp8_prefill_chunks(oracle_mod, d):
+    """Chunked-prefill shapes (prior context + new tokens, causal, poisoned
+    slots) at both head dims, against the oracle on the same codes."""
+    case = workloads.make_case("f8-pf-%d" % d, 826 + d, [150, 37, 300], [700, 40, 300], 24 if d == 256 else 32,
+                               4 if d == 256 else 8, d, causal=True, extra_pages=2, poison=True)
+    _check(oracle_mod, workloads.fp8_pool_case(case), 0.5, 0.5, "fp8 prefill D=%d" % d)
+
+
+def test_fp8_prefill_noncausal_window_sinks(oracle_mod):
+    case = workloads.make_case("f8-pf-w", 828, [90, 200], [333, 200], 12, 3, 128, causal=False, extra_pages=1,
+                               poison=True)
+    g = torch.Generator().manual_seed(4)
+    sinks = (torch.randn(12, generator=g) * 2).float()
+    sinks[2] = -math.inf
+    case8 = workloads.fp8_pool_case(case, mult=4.0)
+    _check(oracle_mod, case8, 0.25, 0.5, "fp8 prefill non-causal", path=PATH_PREFILL)
+    _check(oracle_mod, case8, 0.25, 0.5, "fp8 prefill window 77 + sinks", path=PATH_PREFILL, window=77, sinks=sinks)
+    _check(oracle_mod, case8, -0.25, 0.5, "fp8 prefill negative k_scale", path=PATH_PREFILL)
+
+
+def test_fp8_prefill_manifest_pool(oracle_mod):
+    """The manifest's two-layer pool (layer 1), 32-token chunks at G 6: the
+    automatic plan takes the prefill kernel through the staging pool."""
+    _check(oracle_mod, workloads.fp8_pool_case(workloads.tiny_mixed(seed=829)), 0.5, 1.0, "fp8 tiny mixed")
+
+
+def test_fp8_prefill_equals_bf16_prefill_bitwise():
+    """With unit scales the staged pages are exactly the bf16 pool of the
+    decoded codes, so the prefill output must be the bf16 prefill's bits."""
+    import dataclasses
     import paged_kv_gqa_fwd_amd as pa
-    case8 = workloads.fp8_pool_case(workloads.chunked_prefill(n_seqs=2, q_lo=100, q_hi=200, ctx_hi=300,
-                                                              seed=826)).to("cuda")
-    with pytest.raises(pa.AttnError):
-        pa.paged_attention(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, case8.max_q,
+    case8 = workloads.fp8_pool_case(workloads.chunked_prefill(n_seqs=3, q_lo=100, q_hi=260, ctx_hi=500,
+                                                              seed=830)).to("cuda")
+    vals = case8.pool_storage.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    kvb = vals.as_strided(case8.kv.shape, case8.kv.stride(), case8.kv.storage_offset())
+    caseb = dataclasses.replace(case8, pool_storage=vals, kv=kvb)
+    a = pa.paged_attention(case8.q, case8.kv, case8.block_table, case8.seq_lens, case8.cu_q, case8.max_q,
                            case8.scale, True, k_scale=1.0, v_scale=1.0)
+    b = pa.paged_attention(caseb.q, caseb.kv, caseb.block_table, caseb.seq_lens, caseb.cu_q, caseb.max_q,
+                           caseb.scale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 @pytest.mark.parametrize("big", [False, True])
