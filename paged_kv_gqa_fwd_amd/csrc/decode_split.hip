@@ -63,9 +63,9 @@ struct DecodeCfg {
 // KW rb .. KW rb + KW - 1 (KW = 4 / RB) share row block rb and take
 // consecutive slices of 16 RB keys of every page.
 template <int RB>
-__device__ __forceinline__ int decode_row_block(int w) { return w / (4 / RB); }
+__device__ __forceinline__ int decode_row_block(int w) { return RB == 1 ? 0 : w / (4 / RB); }
 template <int RB>
-__device__ __forceinline__ int decode_key_offset(int w) { return (w % (4 / RB)) * 16 * RB; }
+__device__ __forceinline__ int decode_key_offset(int w) { return RB == 1 ? 16 * w : (w % (4 / RB)) * 16 * RB; }
 
 // Issue the 16-byte loads of one page (K and V rows of one KV head) into
 // registers.  Chunk c -> key = c / (2 DC), kv = (c / DC) % 2, dc = c % DC:
@@ -301,7 +301,7 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int row = lane & 15;
-    const int w0 = w - w % KW;   // first wave of this wave's row block
+    const int w0 = KW == 4 ? 0 : w - w % KW;   // first wave of this wave's row block
     const int G = a.group;
     float l_row = l_part + shfl_xor_f32(l_part, 16);
     l_row += shfl_xor_f32(l_row, 32);
@@ -333,7 +333,7 @@ __device__ __forceinline__ void decode_merge_write(const AttnArgs &a, uint16_t *
     constexpr int RSTEP = kThreads / D;   // 1 (D=256) or 2 (D=128)
     const int d = tid % D;
     for (int r = tid / D; r < rows; r += RSTEP) {
-        const int rw0 = (r / 16) * KW, rr = r % 16;
+        const int rw0 = KW == 4 ? 0 : (r / 16) * KW, rr = KW == 4 ? r : r % 16;
         float Mr = -INFINITY;
 #pragma unroll
         for (int k = 0; k < KW; ++k) Mr = fmaxf(Mr, red_m[rw0 + k][rr]);
