@@ -7,10 +7,10 @@ synthetic, seeded input already resident in HBM.
 Default workload: the decode batch (64 sequences x 1 query token, 32 q / 8 KV
 heads, head_dim 128, page 64, KV lengths uniform in [1024, 8192], causal),
 reported as achieved HBM GB/s of algorithmic bytes (K and V read once per KV
-head, plus Q and the output).  Secondary lines (the tiny mixed call's latency,
-long-context decode on both pool layouts, chunked prefill, DiT non-causal,
-the quantised DiT path, and variants) are timed first, each after a
-time-bounded warmup, then the primary line (W warmup steps, K timed steps).
+head, plus Q and the output): W warmup steps, then K timed steps.  Secondary
+lines (the tiny mixed call's latency, long-context decode on both pool
+layouts, chunked prefill, DiT non-causal, the quantised DiT path, and
+variants) follow, each after a time-bounded warmup.
 Prefill lines are in TFLOP/s of algorithmic FLOPs (4 * D per visible
 (query, q head, key) triple).  Every line carries its roofline block; the
 primary line and the tiny, long-decode, chunked-prefill, DiT and quantised
@@ -688,20 +688,11 @@ def main():
         return
     torch.manual_seed(0)
     cpu_on = not args.no_cpu_baseline
-    # The primary line's inputs are generated first and stay resident; the
-    # secondary lines run next, so the GPU is under load, at its steady
-    # clocks, when the primary line's W warmup and K timed steps follow
-    # without a generation gap.
-    log("[bench] generating %s (primary line)" % args.workload)
-    prim_case = workloads.WORKLOADS[args.workload](device="cuda")
-    secondary = []
-    for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
-        ss = run_secondary(name, args, cpu_on)
-        log("[bench] %s" % json.dumps(ss))
-        secondary.append(ss)
-        torch.cuda.empty_cache()
-    prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path, secondary=False,
-                        case=prim_case)
+    # The primary line first (W warmup and K timed steps right after its
+    # inputs are generated, before the secondary lines have heated the chip:
+    # the decode kernel, mostly HBM-bound, measured 1-3% slower at the end of
+    # the run than at its start), then the secondary lines.
+    prim = run_workload(args.workload, args.steps, args.warmup, args.pages_per_split, args.path, secondary=False)
     s = summarize(prim)
     log("[bench] %s" % json.dumps(s))
     bound = BOUND[args.workload]
@@ -712,11 +703,18 @@ def main():
     ceiling = None
     if bound == "hbm":
         # the practical denominator beside the 8 TB/s peak: a plain read
-        # stream over as many bytes as one step moves
+        # stream over as many bytes as one step moves, right after the
+        # primary line (the same state of the chip)
         ceiling = stream_read_ceiling(prim["bytes"])
         ceiling["kernel_frac"] = round(s["main_kernel_GBps"] / ceiling["GBps"], 4)
         ceiling["step_frac"] = round(s["value"] / ceiling["GBps"], 4)
         log("[bench] read ceiling %s" % json.dumps(ceiling))
+    secondary = []
+    for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        ss = run_secondary(name, args, cpu_on)
+        log("[bench] %s" % json.dumps(ss))
+        secondary.append(ss)
+        torch.cuda.empty_cache()
     cpu = None
     if cpu_on:
         log("[bench] timing the CPU oracle on a sample")
