@@ -709,18 +709,18 @@ def main():
         ceiling["kernel_frac"] = round(s["main_kernel_GBps"] / ceiling["GBps"], 4)
         ceiling["step_frac"] = round(s["value"] / ceiling["GBps"], 4)
         log("[bench] read ceiling %s" % json.dumps(ceiling))
-    secondary = []
-    for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
-        ss = run_secondary(name, args, cpu_on)
-        log("[bench] %s" % json.dumps(ss))
-        secondary.append(ss)
-        torch.cuda.empty_cache()
     cpu = None
     if cpu_on:
         log("[bench] timing the CPU oracle on a sample")
         cpu = cpu_baseline(prim)
         log("[bench] cpu baseline %s" % json.dumps(cpu))
     case = prim["case"]
+    secondary = []
+    for name in [x for x in args.secondary.split(",") if x and x != args.workload]:
+        ss = run_secondary(name, args, cpu_on)
+        log("[bench] %s" % json.dumps(ss))
+        secondary.append(ss)
+        torch.cuda.empty_cache()
     line = {
         "metric": METRIC, "value": s["value"], "unit": s["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(prim["ms_per_step"], 4),
