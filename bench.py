@@ -321,13 +321,21 @@ def run_quant(steps, warmup, cpu_seconds=0.0):
            "frac_of_int8_fp8_peak": round(tops / Q8_PEAK_TOPS, 4),
            "path": "quant (int8 QK, fp8 PV)", "step_ms_dist": dist,
            "roofline": {"bound": "mfma", "achieved": round(loop_tops, 2), "peak": Q8_PEAK_TOPS, "unit": "TOPS",
-                        "frac": round(loop_tops / Q8_PEAK_TOPS, 4), "traffic": None,
+                        "frac": round(loop_tops / Q8_PEAK_TOPS, 4),
+                        "traffic": measured_traffic(QUANT_SOURCES, "quant_attn_kernel__dit_quant.traffic.json"),
                         "kernel": "quant_attn_kernel", "kernel_ms": round(main_ms, 4)}}
     if cpu_seconds > 0:
         log("[bench] timing the quantised CPU oracle on a sample")
         res["cpu_baseline"] = cpu_quant_baseline(case, cpu_seconds)
         log("[bench] cpu baseline %s" % json.dumps(res["cpu_baseline"]))
     return res
+
+
+# the sources each kernel is built from: a counter summary taken on other
+# sources no longer describes the kernel
+DECODE_SOURCES = ["decode_split.hip", "attn_device.h", "kv_quant.h"]
+PREFILL_SOURCES = ["prefill.hip", "attn_device.h", "kv_quant.h", "lds_stream.h"]
+QUANT_SOURCES = ["quant.hip", "attn_device.h", "quant_device.h", "lds_stream.h"]
 
 
 def measured_traffic(kernel_files, profile_name):
@@ -366,7 +374,7 @@ def _roofline(res, bound):
     ach = res["flops"] / (res["main_kernel_ms"] * 1e-3) / 1e12
     traffic = None
     if name == "chunked_prefill" or name == "dit_self_attn":
-        traffic = measured_traffic(["prefill.hip", "attn_device.h", "lds_stream.h"],
+        traffic = measured_traffic(PREFILL_SOURCES,
                                    "paged_prefill_kernel__%s.traffic.json" % name)
     return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kern,
@@ -698,7 +706,7 @@ def main():
     bound = BOUND[args.workload]
     roof = s["roofline"]
     if bound == "hbm" and args.workload == "decode_batch" and "split" in prim["path"]:
-        roof["traffic"] = measured_traffic(["decode_split.hip", "attn_device.h"],
+        roof["traffic"] = measured_traffic(DECODE_SOURCES,
                                            "%s__decode_batch.traffic.json" % roof["kernel"])
     ceiling = None
     if bound == "hbm":
