@@ -36,9 +36,11 @@
 //    page's first step, so no block opens on an LDS round trip; the first
 //    Q.K MFMA of a step goes out before the row-max reduction and rescale
 //    that separate the two blocks.  At D = 256
-//    (one page of lead) the barrier waits for the next page's K rows only:
-//    its V rows, first read a page later, are issued after them, spread over
-//    the steps between two barriers.
+//    (one page of lead) the barrier waits for the next page's K rows only,
+//    and no loads go out there: the following page's K rows are issued one
+//    load per four MFMAs over the next step and its V rows likewise over the
+//    step after (a burst of a page's loads stalls the issuing waves until
+//    the CU's vector-memory path has taken them).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with keys on M: each lane owns
 //    one query row per block, so row max / row sum are in-lane plus one
 //    permlane32 swap.  The S^T C layout is directly the B operand of
@@ -58,6 +60,9 @@ namespace pa {
 
 #ifndef PA_PREFILL_PREFETCH
 #define PA_PREFILL_PREFETCH 2
+#endif
+#ifndef PA_PF_SPREAD   // 0: D = 256 issues a page's K rows at the barrier (the former refill)
+#define PA_PF_SPREAD 1
 #endif
 #ifndef PA_PF_TILE_PAGES128
 #define PA_PF_TILE_PAGES128 2
@@ -95,6 +100,18 @@ struct PfCfg {
     // barrier then waits for K only.
     static constexpr bool SPLITV = D == 256;
     static constexpr int VPH = LOADS / 4;
+    // SPREAD (D = 256): no load burst at the barrier: page t+2's K rows go
+    // out one load per SP MFMAs over step 2t+1, its V rows the same way over
+    // step 2t+2, so the vector-memory path never queues more than one load
+    // per wave and the issuing wave's wait hides under its running MFMA.
+    static constexpr bool SPREAD = SPLITV && PA_PF_SPREAD;
+    // Load i of K sits at MFMA slot SP i of step 2t+1, load i of V at slot
+    // SP i of step 2t+2 (slot p of the pair: p < 32 in 2t+1, p - 32 in 2t+2).
+    // (K loads packed into the first half of step 2t+1, or K and V over
+    // three-fifths / two-fifths of the pair, measured the same.)
+    static constexpr int SP = 2 * (D / 16) / LOADS;   // 32 MFMA slots per step / 8 loads
+    static constexpr int k_at(int p) { return p < 32 && p % SP == 0 ? p / SP : -1; }
+    static constexpr int v_at(int p) { return p >= 32 && p % SP == 0 ? (p - 32) / SP : -1; }
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
@@ -275,8 +292,29 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     uint16_t *vp_slot = sv[0];
     int vp_valid = 0;
     bool vp_on = false;
+    uint16_t *kp_slot = sk[0];
     auto issue_v_part = [&](int q) {
-        if (C::SPLITV && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, vp_valid, q * C::VPH);
+        if (C::SPLITV && !C::SPREAD && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, vp_valid, q * C::VPH);
+    };
+    // SPREAD: MFMA slot s (0 .. 31) of step j; K load s / SP of the page in
+    // odd steps, V load s / SP in even steps.  The loads always issue (a
+    // branch around each would split the step's basic blocks, and the
+    // compiler then moves the exponentials away from the MFMAs they overlap):
+    // with no page to load they re-read key 0 of the last page into the free
+    // ring slots, and a vmcnt(0) before the epilogue drains them.
+    auto spread_load = [&](int j, int s) {
+        if constexpr (C::SPREAD) {
+            const int p = (j & 1) ? s : 32 + s;
+            const int ik = C::k_at(p), iv = C::v_at(p);
+            if (ik >= 0) {
+                const int slot = (ik * C::THREADS + w * 64) * 8;
+                dma16(lds_address(kp_slot + slot), vp_base - a.kv_skv, pl.key[ik] < vp_valid ? pl.kof[ik] : pl.kof0[ik]);
+            }
+            if (iv >= 0) {
+                const int slot = (iv * C::THREADS + w * 64) * 8;
+                dma16(lds_address(vp_slot + slot), vp_base, pl.key[iv] < vp_valid ? pl.vof[iv] : pl.vof0[iv]);
+            }
+        }
     };
     // Wait until page t has landed in LDS: pages t+1 .. `issued` were
     // issued after it and may stay in flight (loads complete in issue order).
@@ -421,6 +459,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 for (int rb = 0; rb < C::RB; ++rb) {
                     oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         vop[k % (PF + 1)], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+                    spread_load(j, k);
                     constexpr int EH = EA / C::RB;
 #pragma unroll
                     for (int e = (k * C::RB + rb) * EH; e < (k * C::RB + rb + 1) * EH; ++e)
@@ -480,6 +519,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 for (int rb = 0; rb < C::RB; ++rb) {
                     if (ks > 0)
                         snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks % (PF + 1)], qreg[rb][ks], snext[rb], 0, 0, 0);
+                    spread_load(j, NPV + ks);
                     constexpr int EH = EB / C::RB;
 #pragma unroll
                     for (int e = (ks * C::RB + rb) * EH; e < (ks * C::RB + rb + 1) * EH; ++e) {
@@ -517,9 +557,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         if constexpr (C::SPLITV) {
             // K page t+1 has landed (only V page t+1, issued after it, may
             // be in flight; its first reader is A(2t+3), after the next
-            // barrier); the refill issues K page t+2 now and its V over the
-            // next two steps.  After the last page's first step every load
-            // is waited for (its V rows are read next).
+            // barrier); the refill of page t+2 issues its K rows over step
+            // 2t+1 and its V rows over step 2t+2 (SPREAD; else K now and V
+            // over the next two steps).  After the last page's first step
+            // every load is waited for (its V rows are read next).
             if (!(j & 1)) {
                 if (t + 1 < ntiles)
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
@@ -528,10 +569,17 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 vp_on = t + 2 < ntiles;
+                if constexpr (C::SPREAD) {
+                    // the slots page t+2 takes are free whether or not it exists
+                    kp_slot = sk[(t + 2) % C::NK];
+                    vp_slot = sv[(t + 2) % C::NV];
+                    vp_valid = 0;
+                }
                 if (vp_on) {
                     const int pid = load_page_id(bt_row, t + 2);
                     const uint16_t *pb2 = head_base + (int64_t)pid * a.kv_sp;
-                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
+                    if constexpr (!C::SPREAD)
+                        pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
                     vp_base = pb2 + a.kv_skv;
                     vp_slot = sv[(t + 2) % C::NV];
                     vp_valid = L - (t + 2) * kPage;
@@ -556,6 +604,14 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         wait_page(t0);
         __builtin_amdgcn_s_barrier();
         qk(j0, sA);
+        if constexpr (C::SPREAD) {
+            // step j0 (even) issues its V loads before the first refill is
+            // set up: into the slot page t0+2 will take, from page t0
+            kp_slot = sk[(t0 + 2) % C::NK];
+            vp_slot = sv[(t0 + 2) % C::NV];
+            vp_base = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp + a.kv_skv;
+            vp_valid = 0;
+        }
         if constexpr (!C::SPLITV)
 #pragma unroll
             for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
@@ -569,6 +625,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             }
         }
         pv(nsteps - 1, pb);
+        if constexpr (C::SPREAD) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS load outlives the workgroup
     }
 
     // Epilogue: out = O / l, rounded to bf16.  oacc[rb][db][i] holds
