@@ -64,6 +64,9 @@ namespace pa {
 #ifndef PA_PF_SPREAD   // 0: D = 256 issues a page's K rows at the barrier (the former refill)
 #define PA_PF_SPREAD 1
 #endif
+#ifndef PA_PF_SPREAD128   // 1: D = 128 spreads its tile refills the same way
+#define PA_PF_SPREAD128 0
+#endif
 #ifndef PA_PF_TILE_PAGES128
 #define PA_PF_TILE_PAGES128 2
 #endif
@@ -100,18 +103,16 @@ struct PfCfg {
     // barrier then waits for K only.
     static constexpr bool SPLITV = D == 256;
     static constexpr int VPH = LOADS / 4;
-    // SPREAD (D = 256): no load burst at the barrier: page t+2's K rows go
-    // out one load per SP MFMAs over step 2t+1, its V rows the same way over
-    // step 2t+2, so the vector-memory path never queues more than one load
-    // per wave and the issuing wave's wait hides under its running MFMA.
-    static constexpr bool SPREAD = SPLITV && PA_PF_SPREAD;
-    // Load i of K sits at MFMA slot SP i of step 2t+1, load i of V at slot
-    // SP i of step 2t+2 (slot p of the pair: p < 32 in 2t+1, p - 32 in 2t+2).
-    // (K loads packed into the first half of step 2t+1, or K and V over
-    // three-fifths / two-fifths of the pair, measured the same.)
-    static constexpr int SP = 2 * (D / 16) / LOADS;   // 32 MFMA slots per step / 8 loads
-    static constexpr int k_at(int p) { return p < 32 && p % SP == 0 ? p / SP : -1; }
-    static constexpr int v_at(int p) { return p >= 32 && p % SP == 0 ? (p - 32) / SP : -1; }
+    // SPREAD: no load burst at the barrier.  The tile that the barrier
+    // after step SPT t + SPT - 2 frees slots for (tile t+2) has its K rows
+    // issued one load per SP MFMAs over the next step (SPT t + SPT - 1) and
+    // its V rows the same way over the step after (SPT t + SPT), so the
+    // vector-memory path never queues more than one load per wave and the
+    // issuing wave's wait hides under its running MFMA.  (At D = 256, K loads
+    // packed into the first half of the step, or K and V over three-fifths /
+    // two-fifths of the two steps, measured the same.)
+    static constexpr bool SPREAD = PA_PF_SPREAD && (SPLITV || PA_PF_SPREAD128);
+    static constexpr int SP = (2 * (D / 32) + D / 16) / (TP * LOADS);   // MFMA slots per step / loads per step
 };
 static_assert(PfCfg<128>::BM == prefill_rows(128) && PfCfg<256>::BM == prefill_rows(256), "row tile");
 
@@ -292,27 +293,46 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     uint16_t *vp_slot = sv[0];
     int vp_valid = 0;
     bool vp_on = false;
-    uint16_t *kp_slot = sk[0];
     auto issue_v_part = [&](int q) {
         if (C::SPLITV && !C::SPREAD && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, vp_valid, q * C::VPH);
     };
-    // SPREAD: MFMA slot s (0 .. 31) of step j; K load s / SP of the page in
-    // odd steps, V load s / SP in even steps.  The loads always issue (a
-    // branch around each would split the step's basic blocks, and the
-    // compiler then moves the exponentials away from the MFMAs they overlap):
-    // with no page to load they re-read key 0 of the last page into the free
-    // ring slots, and a vmcnt(0) before the epilogue drains them.
+    // SPREAD: the tile being refilled (page bases, valid keys per page) and
+    // its ring slots.  Its loads always issue (a branch around each would
+    // split the step's basic blocks, and the compiler then moves the
+    // exponentials away from the MFMAs they overlap): with no tile to load
+    // they re-read key 0 of an existing page into free ring slots, and a
+    // vmcnt(0) before the epilogue drains them.
+    const uint16_t *rp_base[C::TP];
+    int rp_valid[C::TP];
+    uint16_t *kp_slot = sk[0];
+    // tile tn's pages (tile tv, which exists, lends a page id if tn does not)
+    auto set_refill = [&](int tn, int tv) {
+        kp_slot = sk[tn % C::NK];
+        vp_slot = sv[tn % C::NV];
+#pragma unroll
+        for (int pp = 0; pp < C::TP; ++pp) {
+            const int page = C::TP * tn + pp;
+            const bool real = tn < ntiles && page < npages;
+            const int pid = load_page_id(bt_row, real ? page : C::TP * (tn < ntiles ? tn : tv));
+            rp_base[pp] = head_base + (int64_t)pid * a.kv_sp;
+            rp_valid[pp] = real ? L - page * kPage : 0;
+        }
+    };
+    // MFMA slot s of step j: K load s / SP of the refill tile in steps
+    // SPT t + SPT - 1, V load s / SP in steps SPT t.
     auto spread_load = [&](int j, int s) {
         if constexpr (C::SPREAD) {
-            const int p = (j & 1) ? s : 32 + s;
-            const int ik = C::k_at(p), iv = C::v_at(p);
-            if (ik >= 0) {
-                const int slot = (ik * C::THREADS + w * 64) * 8;
-                dma16(lds_address(kp_slot + slot), vp_base - a.kv_skv, pl.key[ik] < vp_valid ? pl.kof[ik] : pl.kof0[ik]);
-            }
-            if (iv >= 0) {
-                const int slot = (iv * C::THREADS + w * 64) * 8;
-                dma16(lds_address(vp_slot + slot), vp_base, pl.key[iv] < vp_valid ? pl.vof[iv] : pl.vof0[iv]);
+            const bool kstep = (unsigned)j % C::SPT == C::SPT - 1;
+            const bool vstep = (unsigned)j % C::SPT == 0;
+            if (s % C::SP == 0 && (kstep || vstep)) {
+                const int q = s / C::SP;
+                const int pp = q / C::LOADS, i = q % C::LOADS;
+                const int slot = pp * C::TILE + (i * C::THREADS + w * 64) * 8;
+                const bool ok = pl.key[i] < rp_valid[pp];
+                if (kstep)
+                    dma16(lds_address(kp_slot + slot), rp_base[pp], ok ? pl.kof[i] : pl.kof0[i]);
+                else
+                    dma16(lds_address(vp_slot + slot), rp_base[pp] + a.kv_skv, ok ? pl.vof[i] : pl.vof0[i]);
             }
         }
     };
@@ -341,13 +361,19 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[rb][i] = f32x16{};
-    float m_ref[C::RB], l_part[C::RB];
+    const float sl2 = a.scale_log2_pos;   // > 0
+    const float inv_sl2 = 1.f / sl2;
+    // m_ref: the row's reference max (log2 units), m_use the value P is taken
+    // against (0 while no key of the row has been seen), thr the raw score
+    // above which the reference moves: (m_ref + threshold) / sl2.
+    float m_ref[C::RB], m_use[C::RB], thr[C::RB], l_part[C::RB];
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
         m_ref[rb] = -INFINITY;
+        m_use[rb] = 0.f;
+        thr[rb] = -INFINITY;
         l_part[rb] = 0.f;
     }
-    const float sl2 = a.scale_log2_pos;   // > 0
 
     // Per-lane LDS element offsets.  K operand of a 32-key step: key
     // lane & 31, logical chunk 2 ks + hi, physical chunk (2 ks + hi) ^ (lane & 15).
@@ -474,25 +500,26 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         for (int rb = 0; rb < C::RB; ++rb)
             snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcar[0], qreg[rb][0], f32x16{}, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        float alpha[C::RB], m_use[C::RB];
-        bool any_upd = false;
+        // ---- reference max and rescale.  Each lane first compares its
+        // half-row max with the raw threshold; only when some lane of the
+        // wave passes it (rare: a row's max rose by more than 2^8) are the
+        // half-rows combined, the references moved and O, l rescaled.
+        bool past = false;
 #pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) {
-            const float mt = max_xor32(mx[rb]) * sl2;   // -inf stays -inf (sl2 > 0)
-            const bool upd = mt > m_ref[rb] + kRescaleThreshold;
-            const float m_new = upd ? mt : m_ref[rb];
-            alpha[rb] = upd ? exp2_fast(m_ref[rb] - m_new) : 1.f;
-            any_upd |= upd;
-            m_ref[rb] = m_new;
-            m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
-        }
-        // ---- rescale (rare: only when a row's max rose by more than 2^8)
-        if (__any(any_upd)) {
+        for (int rb = 0; rb < C::RB; ++rb) past |= mx[rb] > thr[rb];
+        if (__any(past)) {
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb) {
-                l_part[rb] *= alpha[rb];
+                const float mt = max_xor32(mx[rb]) * sl2;   // -inf stays -inf (sl2 > 0)
+                const bool upd = mt > m_ref[rb] + kRescaleThreshold;
+                const float m_new = upd ? mt : m_ref[rb];
+                const float alpha = upd ? exp2_fast(m_ref[rb] - m_new) : 1.f;
+                m_ref[rb] = m_new;
+                m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
+                thr[rb] = (m_new + kRescaleThreshold) * inv_sl2;
+                l_part[rb] *= alpha;
 #pragma unroll
-                for (int i = 0; i < D / 32; ++i) oacc[rb][i] *= alpha[rb];
+                for (int i = 0; i < D / 32; ++i) oacc[rb][i] *= alpha;
             }
         }
         // ---- B(j): S_{j+1} = K_{j+1} Q^T on the MFMA pipe, two K operands
@@ -570,16 +597,11 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 __builtin_amdgcn_s_barrier();
                 vp_on = t + 2 < ntiles;
                 if constexpr (C::SPREAD) {
-                    // the slots page t+2 takes are free whether or not it exists
-                    kp_slot = sk[(t + 2) % C::NK];
-                    vp_slot = sv[(t + 2) % C::NV];
-                    vp_valid = 0;
-                }
-                if (vp_on) {
+                    set_refill(t + 2, t);   // the slots page t+2 takes are free whether or not it exists
+                } else if (vp_on) {
                     const int pid = load_page_id(bt_row, t + 2);
                     const uint16_t *pb2 = head_base + (int64_t)pid * a.kv_sp;
-                    if constexpr (!C::SPREAD)
-                        pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
+                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
                     vp_base = pb2 + a.kv_skv;
                     vp_slot = sv[(t + 2) % C::NV];
                     vp_valid = L - (t + 2) * kPage;
@@ -589,12 +611,20 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             // tile version of the same boundary: after B(SPT t + SPT - 2)
             // publish tile t+1, refill K tile t / V tile t-1's slots
             const int t = (unsigned)j / C::SPT;
-            wait_page(t + 1);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            if (t + 1 + C::LEAD < ntiles) {
-                issue_page(t + 1 + C::LEAD);
-                issued = t + 1 + C::LEAD;
+            if constexpr (C::SPREAD) {
+                // tile t+1's loads were the last issued (steps SPT t - 1, SPT t)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                set_refill(t + 1 + C::LEAD, t);
+            } else {
+                wait_page(t + 1);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                if (t + 1 + C::LEAD < ntiles) {
+                    issue_page(t + 1 + C::LEAD);
+                    issued = t + 1 + C::LEAD;
+                }
             }
         }
     };
@@ -605,12 +635,17 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         __builtin_amdgcn_s_barrier();
         qk(j0, sA);
         if constexpr (C::SPREAD) {
-            // step j0 (even) issues its V loads before the first refill is
-            // set up: into the slot page t0+2 will take, from page t0
-            kp_slot = sk[(t0 + 2) % C::NK];
+            // step j0 issues V loads before the first refill is set up: into
+            // the free V slot tile t0+2 will take, from tile t0's first page;
+            // K loads of a step before the first barrier (a single tile, no
+            // barrier) go to the free slot of tile t0+1
+            kp_slot = sk[(t0 + 1) % C::NK];
             vp_slot = sv[(t0 + 2) % C::NV];
-            vp_base = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp + a.kv_skv;
-            vp_valid = 0;
+#pragma unroll
+            for (int pp = 0; pp < C::TP; ++pp) {
+                rp_base[pp] = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp;
+                rp_valid[pp] = 0;
+            }
         }
         if constexpr (!C::SPLITV)
 #pragma unroll
