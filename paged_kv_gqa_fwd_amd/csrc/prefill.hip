@@ -84,6 +84,8 @@ struct PfCfg {
     static constexpr int CH = D / 8;                // 16-byte chunks per K or V row
     static constexpr int TILE = kPage * D;          // bf16 elements of one K (or V) page
     static constexpr int LOADS = kPage * CH / THREADS;  // 16-byte loads per thread per K page
+    static constexpr int KPL = THREADS / CH;            // keys per load
+    static_assert(THREADS % CH == 0, "load layout");
     // The K/V ring's unit: a tile of TP pages (64 TP keys, SPT = 2 TP
     // 32-key steps), published by one workgroup barrier per tile.  At
     // D = 128 two pages per tile halve the barriers per key (and their wave
@@ -126,51 +128,62 @@ constexpr float kRescaleThreshold = 8.f;   // log2 units: P stays <= 256
 // of key k is stored at c ^ (k & 15) (sixteen keys per b128 read cycle), V
 // chunk c at c ^ 4(k & 3) (four keys x four chunks per transposing read
 // cycle).
-// kof / vof hold this thread's byte offsets within a page, kof0 / vof0 the
-// same chunks of key 0.  Keys at or past `valid` re-read key 0 (always valid
-// when a page is loaded): their weight is exactly zero, but a poisoned
-// (non-finite) V row there would turn 0 * V into NaN.
+// kof / vof hold this thread's byte offsets within a page; load i carries
+// key KPL i + kq (KPL = THREADS / CH).  Every slot of a page is read, also
+// those past the sequence's last key: they lie inside the page, their scores
+// are masked (a select, so any K there is harmless), and their V rows are
+// zeroed in LDS once the page has landed (pf_zero_v_tail), since a
+// non-finite V there would turn the zero weight into NaN.
 template <int D>
 struct PageLoad {
     uint32_t kof[PfCfg<D>::LOADS], vof[PfCfg<D>::LOADS];
-    uint32_t kof0[PfCfg<D>::LOADS], vof0[PfCfg<D>::LOADS];
-    int key[PfCfg<D>::LOADS];
+    int kq;
 };
 
 template <int D>
 __device__ __forceinline__ void pf_load_page(uint16_t *lds_k, uint16_t *lds_v, const uint16_t *page_base,
-                                             const PageLoad<D> &pl, int64_t kv_skv, int w, int valid) {
+                                             const PageLoad<D> &pl, int64_t kv_skv, int w) {
     using C = PfCfg<D>;
     const uint16_t *vbase = page_base + kv_skv;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-        const bool ok = pl.key[i] < valid;
         const int slot = (i * C::THREADS + w * 64) * 8;   // wave-uniform LDS element offset
-        dma16(lds_address(lds_k + slot), page_base, ok ? pl.kof[i] : pl.kof0[i]);
-        dma16(lds_address(lds_v + slot), vbase, ok ? pl.vof[i] : pl.vof0[i]);
+        dma16(lds_address(lds_k + slot), page_base, pl.kof[i]);
+        dma16(lds_address(lds_v + slot), vbase, pl.vof[i]);
     }
+}
+
+// Zero this thread's 16-byte chunks of the V rows at or past `valid` in a
+// page that has landed in LDS (the chunks its own loads wrote).
+template <int D>
+__device__ __forceinline__ void pf_zero_v_tail(uint16_t *lds_v, const PageLoad<D> &pl, int tid, int valid) {
+    using C = PfCfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+        if (C::KPL * i + pl.kq >= valid)
+            *reinterpret_cast<u32x4 *>(lds_v + (i * C::THREADS + tid) * 8) = u32x4{0u, 0u, 0u, 0u};
 }
 
 template <int D>
 __device__ __forceinline__ void pf_load_k(uint16_t *lds_k, const uint16_t *page_base, const PageLoad<D> &pl,
-                                          int w, int valid) {
+                                          int w) {
     using C = PfCfg<D>;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int slot = (i * C::THREADS + w * 64) * 8;
-        dma16(lds_address(lds_k + slot), page_base, pl.key[i] < valid ? pl.kof[i] : pl.kof0[i]);
+        dma16(lds_address(lds_k + slot), page_base, pl.kof[i]);
     }
 }
 
 // V loads i0 .. i0+N-1 of a page (vbase = the page's V rows).
 template <int D, int N>
 __device__ __forceinline__ void pf_load_v(uint16_t *lds_v, const uint16_t *vbase, const PageLoad<D> &pl, int w,
-                                          int valid, int i0) {
+                                          int i0) {
     using C = PfCfg<D>;
 #pragma unroll
     for (int i = i0; i < i0 + N; ++i) {
         const int slot = (i * C::THREADS + w * 64) * 8;
-        dma16(lds_address(lds_v + slot), vbase, pl.key[i] < valid ? pl.vof[i] : pl.vof0[i]);
+        dma16(lds_address(lds_v + slot), vbase, pl.vof[i]);
     }
 }
 
@@ -254,36 +267,42 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
 
     // This thread's page-relative load offsets (fixed for every page).
     PageLoad<D> pl;
+    pl.kq = tid / C::CH;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
         const int p = i * C::THREADS + tid;
-        const int key = p / C::CH;
+        const int key = p / C::CH;   // = KPL i + kq
         const int ck = (p % C::CH) ^ (key & 15);
         const int cv = (p % C::CH) ^ (4 * (key & 3));
-        pl.key[i] = key;
         pl.kof[i] = (uint32_t)(key * a.kv_ss + ck * 8) * 2u;
         pl.vof[i] = (uint32_t)(key * a.kv_ss + cv * 8) * 2u;
-        pl.kof0[i] = (uint32_t)(ck * 8) * 2u;
-        pl.vof0[i] = (uint32_t)(cv * 8) * 2u;
     }
+    // V rows past the last key of tile t (its last page, or a page of the
+    // last tile that no row reaches) zeroed once the tile has landed
+    auto zero_tile_tail = [&](int t) {
+#pragma unroll
+        for (int pp = 0; pp < C::TP; ++pp) {
+            const int page = C::TP * t + pp;
+            const int valid = page < npages ? L - page * kPage : 0;
+            if (valid < kPage) pf_zero_v_tail<D>(sv[t % C::NV] + pp * C::TILE, pl, tid, valid);
+        }
+    };
     auto issue_page = [&](int t) {   // tile t: pages TP t .. TP t + TP - 1
         if constexpr (C::SPLITV) {   // all of K, then all of V
             const int pid = load_page_id(bt_row, t);
-            pf_load_k<D>(sk[t % C::NK], head_base + (int64_t)pid * a.kv_sp, pl, w, L - t * kPage);
-            pf_load_v<D, C::LOADS>(sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w,
-                                   L - t * kPage, 0);
+            pf_load_k<D>(sk[t % C::NK], head_base + (int64_t)pid * a.kv_sp, pl, w);
+            pf_load_v<D, C::LOADS>(sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w, 0);
         } else {
 #pragma unroll
             for (int pp = 0; pp < C::TP; ++pp) {
                 // A page of the last tile past the workgroup's last visible
-                // key is not named by the table: its slots re-read key 0 of
-                // the tile's first page (finite, weight zero), so every tile
-                // issues the same loads.
+                // key is not named by the table: it re-reads the tile's first
+                // page (its V rows are then zeroed), so every tile issues the
+                // same loads.
                 const int page = C::TP * t + pp;
-                const bool real = page < npages;
-                const int pid = load_page_id(bt_row, real ? page : C::TP * t);
+                const int pid = load_page_id(bt_row, page < npages ? page : C::TP * t);
                 pf_load_page<D>(sk[t % C::NK] + pp * C::TILE, sv[t % C::NV] + pp * C::TILE,
-                                head_base + (int64_t)pid * a.kv_sp, pl, a.kv_skv, w, real ? L - page * kPage : 0);
+                                head_base + (int64_t)pid * a.kv_sp, pl, a.kv_skv, w);
             }
         }
     };
@@ -291,19 +310,16 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     // after its K rows (part q of 4 during phase q of those steps).
     const uint16_t *vp_base = head_base;
     uint16_t *vp_slot = sv[0];
-    int vp_valid = 0;
     bool vp_on = false;
     auto issue_v_part = [&](int q) {
-        if (C::SPLITV && !C::SPREAD && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, vp_valid, q * C::VPH);
+        if (C::SPLITV && !C::SPREAD && vp_on) pf_load_v<D, C::VPH>(vp_slot, vp_base, pl, w, q * C::VPH);
     };
-    // SPREAD: the tile being refilled (page bases, valid keys per page) and
-    // its ring slots.  Its loads always issue (a branch around each would
-    // split the step's basic blocks, and the compiler then moves the
-    // exponentials away from the MFMAs they overlap): with no tile to load
-    // they re-read key 0 of an existing page into free ring slots, and a
-    // vmcnt(0) before the epilogue drains them.
+    // SPREAD: the tile being refilled (page bases) and its ring slots.  Its
+    // loads always issue (a branch around each would split the step's basic
+    // blocks, and the compiler then moves the exponentials away from the
+    // MFMAs they overlap): with no tile to load they re-read an existing page
+    // into free ring slots, and a vmcnt(0) before the epilogue drains them.
     const uint16_t *rp_base[C::TP];
-    int rp_valid[C::TP];
     uint16_t *kp_slot = sk[0];
     // tile tn's pages (tile tv, which exists, lends a page id if tn does not)
     auto set_refill = [&](int tn, int tv) {
@@ -315,7 +331,6 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const bool real = tn < ntiles && page < npages;
             const int pid = load_page_id(bt_row, real ? page : C::TP * (tn < ntiles ? tn : tv));
             rp_base[pp] = head_base + (int64_t)pid * a.kv_sp;
-            rp_valid[pp] = real ? L - page * kPage : 0;
         }
     };
     // MFMA slot s of step j: K load s / SP of the refill tile in steps
@@ -328,11 +343,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 const int q = s / C::SP;
                 const int pp = q / C::LOADS, i = q % C::LOADS;
                 const int slot = pp * C::TILE + (i * C::THREADS + w * 64) * 8;
-                const bool ok = pl.key[i] < rp_valid[pp];
                 if (kstep)
-                    dma16(lds_address(kp_slot + slot), rp_base[pp], ok ? pl.kof[i] : pl.kof0[i]);
+                    dma16(lds_address(kp_slot + slot), rp_base[pp], pl.kof[i]);
                 else
-                    dma16(lds_address(vp_slot + slot), rp_base[pp] + a.kv_skv, ok ? pl.vof[i] : pl.vof0[i]);
+                    dma16(lds_address(vp_slot + slot), rp_base[pp] + a.kv_skv, pl.vof[i]);
             }
         }
     };
@@ -593,6 +607,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                // V page t (issued before K page t+1) has landed; it is first
+                // read by A(2t+1)
+                if (t == ntiles - 1) zero_tile_tail(t);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 vp_on = t + 2 < ntiles;
@@ -601,10 +618,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 } else if (vp_on) {
                     const int pid = load_page_id(bt_row, t + 2);
                     const uint16_t *pb2 = head_base + (int64_t)pid * a.kv_sp;
-                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w, L - (t + 2) * kPage);
+                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w);
                     vp_base = pb2 + a.kv_skv;
                     vp_slot = sv[(t + 2) % C::NV];
-                    vp_valid = L - (t + 2) * kPage;
                 }
             }
         } else if ((unsigned)j % C::SPT == C::SPT - 2 && (int)((unsigned)j / C::SPT) + 1 < ntiles) {
@@ -614,11 +630,13 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             if constexpr (C::SPREAD) {
                 // tile t+1's loads were the last issued (steps SPT t - 1, SPT t)
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (t + 1 == ntiles - 1) zero_tile_tail(t + 1);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 set_refill(t + 1 + C::LEAD, t);
             } else {
                 wait_page(t + 1);
+                if (t + 1 == ntiles - 1) zero_tile_tail(t + 1);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 if (t + 1 + C::LEAD < ntiles) {
@@ -632,6 +650,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     f32x16 sA[C::RB], sB[C::RB];
     if (j0 < nsteps) {
         wait_page(t0);
+        // A(j0) reads tile t0's V (with zero weights) before any other barrier
+        if (t0 == ntiles - 1) zero_tile_tail(t0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         qk(j0, sA);
         if constexpr (C::SPREAD) {
@@ -642,10 +663,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             kp_slot = sk[(t0 + 1) % C::NK];
             vp_slot = sv[(t0 + 2) % C::NV];
 #pragma unroll
-            for (int pp = 0; pp < C::TP; ++pp) {
+            for (int pp = 0; pp < C::TP; ++pp)
                 rp_base[pp] = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp;
-                rp_valid[pp] = 0;
-            }
         }
         if constexpr (!C::SPLITV)
 #pragma unroll
