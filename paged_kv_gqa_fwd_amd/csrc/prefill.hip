@@ -67,6 +67,9 @@ namespace pa {
 #ifndef PA_PF_SPREAD128   // 1: D = 128 spreads its tile refills the same way
 #define PA_PF_SPREAD128 0
 #endif
+#ifndef PA_PF_Q_AGPR
+#define PA_PF_Q_AGPR 1
+#endif
 #ifndef PA_PF_TILE_PAGES128
 #define PA_PF_TILE_PAGES128 2
 #endif
@@ -104,6 +107,7 @@ struct PfCfg {
     // spreads V over the next two steps (VPH loads per MFMA phase); the
     // barrier then waits for K only.
     static constexpr bool SPLITV = D == 256;
+    static constexpr bool Q_AGPR = PA_PF_Q_AGPR && D == 256;
     static constexpr int VPH = LOADS / 4;
     // SPREAD: no load burst at the barrier.  The tile that the barrier
     // after step SPT t + SPT - 2 frees slots for (tile t+2) has its K rows
@@ -237,6 +241,11 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     const int nsteps = (kv_end + 31) / 32;     // 32-key softmax steps
     const int ntiles = (nsteps + C::SPT - 1) / C::SPT;   // ring tiles of TP pages
     const int npages = (kv_end + kPage - 1) / kPage;      // pages with a key some row sees
+    // Ring slots count from the first tile, so that with the loop unrolled
+    // by NK tiles the K slot of every step is a compile-time constant (its
+    // LDS offset folds into the read instructions).
+    auto kslot = [&](int t) { return (unsigned)(t - t0) % C::NK; };
+    auto vslot = [&](int t) { return (unsigned)(t - t0) % C::NV; };
 
     const uint16_t *head_base = a.kv + (int64_t)g * a.kv_sh;
     const int32_t *bt_row = a.block_table + (int64_t)b * a.bt_stride;
@@ -263,6 +272,16 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int ks = 0; ks < D / 16; ++ks)
                 qreg[rb][ks] = __builtin_bit_cast(bf16x8, (qraw[rb][ks] ^ qflip) & keep);
         }
+        // Q is only ever an MFMA operand, which may sit in accumulation
+        // registers: at D = 256 (one wave per SIMD, vector registers full)
+        // placing it there leaves the vector registers to the softmax.
+        // (At D = 128 two waves share a SIMD's registers and it spilled.)
+        if constexpr (C::Q_AGPR) {
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qreg[rb][ks]));
+        }
     }
 
     // This thread's page-relative load offsets (fixed for every page).
@@ -284,14 +303,14 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         for (int pp = 0; pp < C::TP; ++pp) {
             const int page = C::TP * t + pp;
             const int valid = page < npages ? L - page * kPage : 0;
-            if (valid < kPage) pf_zero_v_tail<D>(sv[t % C::NV] + pp * C::TILE, pl, tid, valid);
+            if (valid < kPage) pf_zero_v_tail<D>(sv[vslot(t)] + pp * C::TILE, pl, tid, valid);
         }
     };
     auto issue_page = [&](int t) {   // tile t: pages TP t .. TP t + TP - 1
         if constexpr (C::SPLITV) {   // all of K, then all of V
             const int pid = load_page_id(bt_row, t);
-            pf_load_k<D>(sk[t % C::NK], head_base + (int64_t)pid * a.kv_sp, pl, w);
-            pf_load_v<D, C::LOADS>(sv[t % C::NV], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w, 0);
+            pf_load_k<D>(sk[kslot(t)], head_base + (int64_t)pid * a.kv_sp, pl, w);
+            pf_load_v<D, C::LOADS>(sv[vslot(t)], head_base + (int64_t)pid * a.kv_sp + a.kv_skv, pl, w, 0);
         } else {
 #pragma unroll
             for (int pp = 0; pp < C::TP; ++pp) {
@@ -301,7 +320,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 // same loads.
                 const int page = C::TP * t + pp;
                 const int pid = load_page_id(bt_row, page < npages ? page : C::TP * t);
-                pf_load_page<D>(sk[t % C::NK] + pp * C::TILE, sv[t % C::NV] + pp * C::TILE,
+                pf_load_page<D>(sk[kslot(t)] + pp * C::TILE, sv[vslot(t)] + pp * C::TILE,
                                 head_base + (int64_t)pid * a.kv_sp, pl, a.kv_skv, w);
             }
         }
@@ -323,8 +342,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     uint16_t *kp_slot = sk[0];
     // tile tn's pages (tile tv, which exists, lends a page id if tn does not)
     auto set_refill = [&](int tn, int tv) {
-        kp_slot = sk[tn % C::NK];
-        vp_slot = sv[tn % C::NV];
+        kp_slot = sk[kslot(tn)];
+        vp_slot = sv[vslot(tn)];
 #pragma unroll
         for (int pp = 0; pp < C::TP; ++pp) {
             const int page = C::TP * tn + pp;
@@ -422,10 +441,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     };
     // (steps are never negative: unsigned division by the power-of-two SPT is a shift)
     auto kstage = [&](int j) {
-        return sk[((unsigned)j / C::SPT) % C::NK] + (32 * ((unsigned)j % C::SPT)) * D + klane;
+        return sk[((unsigned)(j - j0) / C::SPT) % C::NK] + (32 * ((unsigned)j % C::SPT)) * D + klane;
     };
     auto vstage = [&](int j) {
-        return sv[((unsigned)j / C::SPT) % C::NV] + (32 * ((unsigned)j % C::SPT)) * D + vlane;
+        return sv[((unsigned)(j - j0) / C::SPT) % C::NV] + (32 * ((unsigned)j % C::SPT)) * D + vlane;
     };
 
     // S^T = K Q^T for the 32 keys of step j (raw scores, f32); no overlap
@@ -618,9 +637,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 } else if (vp_on) {
                     const int pid = load_page_id(bt_row, t + 2);
                     const uint16_t *pb2 = head_base + (int64_t)pid * a.kv_sp;
-                    pf_load_k<D>(sk[(t + 2) % C::NK], pb2, pl, w);
+                    pf_load_k<D>(sk[kslot(t + 2)], pb2, pl, w);
                     vp_base = pb2 + a.kv_skv;
-                    vp_slot = sv[(t + 2) % C::NV];
+                    vp_slot = sv[vslot(t + 2)];
                 }
             }
         } else if ((unsigned)j % C::SPT == C::SPT - 2 && (int)((unsigned)j / C::SPT) + 1 < ntiles) {
@@ -660,8 +679,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             // the free V slot tile t0+2 will take, from tile t0's first page;
             // K loads of a step before the first barrier (a single tile, no
             // barrier) go to the free slot of tile t0+1
-            kp_slot = sk[(t0 + 1) % C::NK];
-            vp_slot = sv[(t0 + 2) % C::NV];
+            kp_slot = sk[kslot(t0 + 1)];
+            vp_slot = sv[vslot(t0 + 2)];
 #pragma unroll
             for (int pp = 0; pp < C::TP; ++pp)
                 rp_base[pp] = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp;
@@ -669,13 +688,14 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         if constexpr (!C::SPLITV)
 #pragma unroll
             for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
-        // Two steps per page; the S registers alternate roles between them.
-        for (int t = t0; t < ntiles; ++t) {
-            step(C::SPT * t, sA, sB);
-            if (C::SPT * t + 1 < nsteps) step(C::SPT * t + 1, sB, sA);
-            if constexpr (C::SPT == 4) {
-                if (C::SPT * t + 2 < nsteps) step(C::SPT * t + 2, sA, sB);
-                if (C::SPT * t + 3 < nsteps) step(C::SPT * t + 3, sB, sA);
+        // SPT steps per tile, NK tiles per iteration; the S registers
+        // alternate roles between steps.
+        for (int u = 0; t0 + C::NK * u < ntiles; ++u) {
+#pragma unroll
+            for (int c = 0; c < C::NK * C::SPT; c += 2) {
+                const int j = j0 + C::NK * C::SPT * u + c;
+                if (c == 0 || j < nsteps) step(j, sA, sB);
+                if (j + 1 < nsteps) step(j + 1, sB, sA);
             }
         }
         pv(nsteps - 1, pb);
