@@ -31,16 +31,23 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _flags():
+# Per-source flags.  The prefill kernel's MFMAs accumulate in vector
+# registers: at head_dim 256 (one wave per SIMD) the default form put the
+# score and output accumulators in the accumulation registers, and every
+# softmax read of a score then cost an extra register move.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def _flags(src: str | None = None):
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument"]
+            "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument"] + FILE_FLAGS.get(src, [])
 
 
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + _flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + _flags(src) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "is not a recognized feature for this target" not in l)
