@@ -505,7 +505,9 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const uint16_t *vt = vstage(j > j0 ? j - 1 : j0);
             bf16x8 vop[PF + 1];
 #pragma unroll
-            for (int k = 0; k < PF; ++k) vop[k] = C::SPLITV ? vread(vt, k) : vcar[k];
+            // (at D = 256 the V page A(2t+1) reads is published by the
+            // barrier just before it: no look-ahead into it)
+            for (int k = 0; k < PF; ++k) vop[k] = (C::SPLITV && (j & 1)) ? vread(vt, k) : vcar[k];
 #pragma unroll
             for (int k = 0; k < NPV; ++k) {
                 if (k == NPV / 2) issue_v_part(2 * (1 - (j & 1)));   // A(2t+1): part 0, A(2t+2): part 2
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 if (ks == NKS / 2) issue_v_part(2 * (1 - (j & 1)) + 1);   // B(2t+1): part 1, B(2t+2): part 3
                 if (ks + PF < NKS)
                     kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
-                else if constexpr (!C::SPLITV)
+                else if (!C::SPLITV || (j & 1))
                     vcar[ks + PF - NKS] = vread(vstage(j), ks + PF - NKS);   // A(j+1)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
@@ -685,9 +687,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int pp = 0; pp < C::TP; ++pp)
                 rp_base[pp] = head_base + (int64_t)load_page_id(bt_row, C::TP * t0) * a.kv_sp;
         }
-        if constexpr (!C::SPLITV)
 #pragma unroll
-            for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
+        for (int k = 0; k < PF; ++k) vcar[k] = vread(vstage(j0), k);
         // SPT steps per tile, NK tiles per iteration; the S registers
         // alternate roles between steps.
         for (int u = 0; t0 + C::NK * u < ntiles; ++u) {
