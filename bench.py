@@ -333,7 +333,7 @@ def run_quant(steps, warmup, cpu_seconds=0.0):
 
 # the sources each kernel is built from: a counter summary taken on other
 # sources no longer describes the kernel
-DECODE_SOURCES = ["decode_split.hip", "attn_device.h", "kv_quant.h"]
+DECODE_SOURCES = ["decode_kernels.h", "decode_split.hip", "attn_device.h", "kv_quant.h"]
 PREFILL_SOURCES = ["prefill.hip", "attn_device.h", "kv_quant.h", "lds_stream.h"]
 QUANT_SOURCES = ["quant.hip", "attn_device.h", "quant_device.h", "lds_stream.h"]
 

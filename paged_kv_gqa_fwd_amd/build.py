@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["paged_attn_api.cpp", "decode_split.hip", "prefill.hip", "quant.hip", "kv_write.hip", "stream_read.hip"]
+SOURCES = ["paged_attn_api.cpp", "decode_split.hip", "decode_f8_256.hip", "prefill.hip", "quant.hip", "kv_write.hip",
+           "stream_read.hip"]
 
 
 def _hipcc() -> str:
@@ -31,11 +32,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-# Per-source flags.  The prefill kernel's MFMAs accumulate in vector
-# registers: at head_dim 256 (one wave per SIMD) the default form put the
-# score and output accumulators in the accumulation registers, and every
-# softmax read of a score then cost an extra register move.
-FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags.  The prefill and decode kernels' MFMAs accumulate in
+# vector registers.  Prefill at head_dim 256 (one wave per SIMD): the default
+# form put the score and output accumulators in the accumulation registers,
+# and every softmax read of a score then cost an extra register move.
+# Decode over an fp8 cache at head_dim 256 (its own source): the vector form
+# fits the kernel in 256 registers, so two workgroups share a CU.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "decode_f8_256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _flags(src: str | None = None):

@@ -49,19 +49,24 @@ constexpr int prefill_threads(int d) { return d == 128 ? 64 * PA_PF_WAVES128 : 6
 constexpr int decode_stages(int d) { return d == 128 ? PA_DECODE_STAGES_128 : PA_DECODE_STAGES_256; }
 // Pages in flight per workgroup over an fp8 cache.  With non-temporal page
 // loads fewer bytes in flight per workgroup read faster on MI355X (as for a
-// plain read stream): one page at D = 128 (two workgroups per CU), two at
-// D = 256 (one workgroup per CU).
+// plain read stream): one page, with two workgroups per CU at both head
+// dims.  (At D = 256 one page and two workgroups per CU, which needs the
+// vector-register MFMA form to fit 256 registers, ran long fp8 decode 13%
+// faster than two pages and one workgroup per CU.)
 #ifndef PA_DECODE_F8_STAGES_128
 #define PA_DECODE_F8_STAGES_128 1
 #endif
 #ifndef PA_DECODE_F8_STAGES_256
-#define PA_DECODE_F8_STAGES_256 2
+#define PA_DECODE_F8_STAGES_256 1
 #endif
 constexpr int decode_stages_f8(int d) { return d == 128 ? PA_DECODE_F8_STAGES_128 : PA_DECODE_F8_STAGES_256; }
 #ifndef PA_DECODE_F8_WAVES_128
 #define PA_DECODE_F8_WAVES_128 2
 #endif
-constexpr int decode_waves_per_simd_f8(int d) { return d == 128 ? PA_DECODE_F8_WAVES_128 : PA_DECODE_WAVES_256; }
+#ifndef PA_DECODE_F8_WAVES_256
+#define PA_DECODE_F8_WAVES_256 2
+#endif
+constexpr int decode_waves_per_simd_f8(int d) { return d == 128 ? PA_DECODE_F8_WAVES_128 : PA_DECODE_F8_WAVES_256; }
 constexpr int decode_waves_per_simd(int d) { return d == 128 ? PA_DECODE_WAVES_128 : PA_DECODE_WAVES_256; }
 // Resident waves per SIMD of the split-decode kernels (with rb blocks of 16
 // packed rows a wave still holds one block's Q^T and O^T: the same count).
