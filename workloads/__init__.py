@@ -109,7 +109,8 @@ def make_case(name: str, seed: int, q_lens, kv_lens, num_q_heads: int, num_kv_he
     table_fill: "neg1" puts -1 in unused block-table columns, "valid" fills
     the whole table from the page permutation (the manifest's full table).
     poison: fill unused pool pages and the slots past L_b in each sequence's
-    last page with NaN / +-inf (a correct kernel never reads them).
+    last page with NaN / +-inf (a correct kernel never lets them reach the
+    output: it skips them, masks their scores or zeroes their V rows).
     layout: "slot_major" stores [page, layer, slot, kv_head, {K,V}, D] (the
     decode.json manifest's order); "head_major" stores [page, kv_head, {K,V},
     slot, D], so each (page, KV head) is one contiguous K block followed by
