@@ -167,7 +167,14 @@ int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int3
  *   workspace    device buffer of >= attn_paged_workspace_bytes bytes,
  *                256-byte aligned (may be NULL when that size is 0); holds
  *                the split-KV partials and, on the fused split path, the
- *                merge counters in its first plan.counter_bytes bytes.  Those
+ *                merge counters in its first plan.counter_bytes bytes.  On
+ *                the prefill path it holds the launch order when the grid
+ *                has two or more sequences and 512 or more workgroups (one
+ *                int32 per workgroup, written by the call before the
+ *                prefill kernel reads it: the grid's items sorted by the KV
+ *                pages each streams, most first, so that a ragged batch's
+ *                longest items do not start last), after the fp8 staging
+ *                pool and table over an fp8 cache.  Those
  *                counter bytes must be zero when the call starts; every call
  *                that runs to completion leaves them zero again.  A buffer
  *                from a zeroing allocator, or one cleared once with
@@ -231,7 +238,8 @@ typedef struct attn_paged_options {
  * G * max_q <= 64) read the codes directly; the prefill path first decodes
  * the pages it reads (exactly: every e4m3 value is a bf16 value) into a
  * bf16 staging pool in the workspace, so its plan's workspace_bytes is
- * n_seqs * max_pages_per_seq * (P * Hkv * 2 * D * 2 + 4) bytes (each part
+ * n_seqs * max_pages_per_seq * (P * Hkv * 2 * D * 2 + 4) bytes, plus the
+ * launch order's 4 bytes per workgroup where the grid takes one (each part
  * 256-byte aligned).  Scales must be finite.
  */
 enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3 = 1 };
@@ -262,7 +270,9 @@ int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int3
  *   q, out and the cache.
  * The plan is the automatic one except that the balanced split path budgets
  * its partials to half the array, so results can differ from
- * attn_paged_fwd_opt's by accumulation order (within the same tolerance).
+ * attn_paged_fwd_opt's by accumulation order (within the same tolerance),
+ * and that a prefill launch order that would not fit beside the fp8 staging
+ * pool in the array is left out (grid order; same bits).
  * A plan whose partials still exceed the array returns ATTN_ERR_WORKSPACE
  * before anything is launched.  Merge counters are cleared by a kernel
  * before each call that needs them (no memset node).  Every call on one GPU

@@ -119,6 +119,10 @@ struct AttnArgs {
     uint16_t *stage_kv;
     int32_t *stage_bt;
     int32_t mp;                 // block-table columns (the staging pool's pages per sequence)
+    // Prefill launch order (null = grid order, latest tiles first): entry i
+    // is the (tile, KV head, sequence) index, in grid order, that workgroup i
+    // computes; a permutation of the grid written by prefill_order_kernel.
+    int32_t *pf_order;
 };
 
 struct CombineArgs {

@@ -24,6 +24,7 @@ hipError_t launch_combine_any(int D, const CombineArgs &a, hipStream_t stream);
 hipError_t launch_workspace_clear(uint32_t *p, size_t words, hipStream_t stream);
 hipError_t launch_prefill_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_fp8_stage_any(int D, const AttnArgs &a, hipStream_t stream);
+hipError_t launch_prefill_order_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream);
 hipError_t launch_quant_prep(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_quant_attn(const QuantArgs &a, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t stream);
@@ -92,9 +93,33 @@ bool balanced_fits(const attn_paged_dims *d, int32_t n_seqs, int64_t mq, int32_t
 
 size_t bal_lead_bytes(int32_t n_seqs) { return align_up((size_t)std::max<int32_t>(n_seqs, 1) * 4, kWsAlign); }
 
+// Prefill workspace: [fp8 staging pool | staging table] over an fp8 cache,
+// then the launch-order table (one i32 per workgroup) when the grid holds
+// several sequences and enough workgroups for their order to matter (fewer:
+// the sort's launch costs more than a ragged tail); only if it fits ws_cap.
+constexpr int64_t kPfOrderMinItems = 512;
+constexpr int64_t kPfOrderMaxItems = int64_t(1) << 22;
+struct PrefillWs {
+    size_t stage_pool = 0, stage_table = 0, order = 0;
+    size_t total() const { return stage_pool + stage_table + order; }
+};
+PrefillWs prefill_ws(const attn_paged_dims *d, int32_t n_seqs, int64_t ss, bool f8, int64_t items, size_t ws_cap) {
+    PrefillWs w;
+    if (f8) {
+        const size_t pages = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)d->max_pages_per_seq;
+        w.stage_pool = align_up(pages * (size_t)pa::kPage * (size_t)ss * 2, kWsAlign);
+        w.stage_table = align_up(pages * 4, kWsAlign);
+    }
+    if (n_seqs >= 2 && items >= kPfOrderMinItems && items <= kPfOrderMaxItems) {
+        const size_t ob = align_up((size_t)items * 4, kWsAlign);
+        if (w.total() + ob <= ws_cap) w.order = ob;
+    }
+    return w;
+}
+
 int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t path_hint,
               int32_t pps, int32_t window, attn_paged_plan *plan, int32_t kv_dtype = ATTN_KV_BF16,
-              size_t bal_budget = kBalPartialBudget) {
+              size_t bal_budget = kBalPartialBudget, size_t ws_cap = SIZE_MAX) {
     int rc = validate_dims(d, n_seqs, max_q);
     if (rc != ATTN_OK) return rc;
     if (kv_dtype != ATTN_KV_BF16 && kv_dtype != ATTN_KV_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
@@ -189,12 +214,6 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         const bool f8 = kv_dtype == ATTN_KV_FP8_E4M3;
         const int64_t ss = f8 ? (int64_t)d->num_kv_heads * 2 * d->head_dim : d->kv_stride_slot;
         if ((63 * ss + d->head_dim) * 2 > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
-        if (f8) {
-            // [staging pool: n_seqs * MP pages of P * Hkv * 2 * D bf16 | staging table: n_seqs * MP i32]
-            const size_t pages = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)d->max_pages_per_seq;
-            plan->workspace_bytes = align_up(pages * (size_t)pa::kPage * (size_t)ss * 2, kWsAlign) +
-                                    align_up(pages * 4, kWsAlign);
-        }
         const int64_t bm = pa::prefill_rows(d->head_dim);
         const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -204,6 +223,9 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         plan->grid_x = (int32_t)tiles;
         plan->grid_y = d->num_kv_heads;
         plan->grid_z = n_seqs;
+        // [staging pool: n_seqs * MP pages of P * Hkv * 2 * D bf16 | staging
+        // table: n_seqs * MP i32] over an fp8 cache, then the launch order
+        plan->workspace_bytes = prefill_ws(d, n_seqs, ss, f8, tiles * d->num_kv_heads * n_seqs, ws_cap).total();
     }
     return ATTN_OK;
 }
@@ -240,8 +262,9 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
                   float scale, int32_t causal, const attn_paged_dims *dims, void *workspace,
                   size_t workspace_bytes, int32_t path_hint, int32_t pps, const float *sinks,
                   int32_t window, attn_paged_plan &plan, pa::AttnArgs &a, int32_t kv_dtype = ATTN_KV_BF16,
-                  float k_scale = 1.f, float v_scale = 1.f, size_t bal_budget = kBalPartialBudget) {
-    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan, kv_dtype, bal_budget);
+                  float k_scale = 1.f, float v_scale = 1.f, size_t bal_budget = kBalPartialBudget,
+                  size_t ws_cap = SIZE_MAX) {
+    int rc = make_plan(dims, n_seqs, max_q, path_hint, pps, window, &plan, kv_dtype, bal_budget, ws_cap);
     if (rc != ATTN_OK) return rc;
     if (!std::isfinite(scale)) return ATTN_ERR_SHAPE;
     if (kv_dtype == ATTN_KV_BF16) k_scale = v_scale = 1.f;   // the scales belong to an fp8 cache only
@@ -298,13 +321,17 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     a.window = effective_window(dims, window);
     a.row_blocks = pa::decode_row_blocks((int64_t)std::max<int32_t>(max_q, 1) * G);
     a.mp = dims->max_pages_per_seq;
-    if (plan.path == ATTN_PATH_PREFILL && plan.workspace_bytes > 0) {
-        // prefill over an fp8 cache: [staging pool | staging table]
-        const size_t pages = (size_t)n_seqs * (size_t)dims->max_pages_per_seq;
-        const size_t pool_bytes = pages * (size_t)pa::kPage * (size_t)dims->num_kv_heads * 2 * (size_t)D * 2;
+    if (plan.path == ATTN_PATH_PREFILL) {
+        // [staging pool | staging table] over an fp8 cache, then the launch order
+        const int64_t ss = (int64_t)dims->num_kv_heads * 2 * D;
+        const PrefillWs w = prefill_ws(dims, n_seqs, ss, a.kv_fp8 != 0,
+                                       (int64_t)plan.grid_x * plan.grid_y * plan.grid_z, ws_cap);
         char *ws = static_cast<char *>(workspace);
-        a.stage_kv = reinterpret_cast<uint16_t *>(ws);
-        a.stage_bt = reinterpret_cast<int32_t *>(ws + align_up(pool_bytes, kWsAlign));
+        if (w.stage_pool > 0) {
+            a.stage_kv = reinterpret_cast<uint16_t *>(ws);
+            a.stage_bt = reinterpret_cast<int32_t *>(ws + w.stage_pool);
+        }
+        if (w.order > 0) a.pf_order = reinterpret_cast<int32_t *>(ws + w.stage_pool + w.stage_table);
     } else if (plan.workspace_bytes > 0) {
         // [merge counters or pieces per sequence | partial O | partial (m, l)],
         // each 256-byte aligned
@@ -330,6 +357,17 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
     const bool timing = timing_enabled();
     TimedLaunch t_main{}, t_comb{};
     hipError_t e;
+    if (plan.path == ATTN_PATH_PREFILL && a.pf_order) {
+        // Sort the grid's items by work (timed as preparation).
+        TimedLaunch t_ord{};
+        if (timing && record_event(&t_ord.start, st) != ATTN_OK) return ATTN_ERR_HIP;
+        if (pa::launch_prefill_order_any(D, a, grid, st) != hipSuccess) return ATTN_ERR_HIP;
+        if (timing) {
+            if (record_event(&t_ord.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
+            t_ord.kind = kTimedPrep;
+            timing_push(t_ord);
+        }
+    }
     if (plan.path == ATTN_PATH_PREFILL && a.stage_kv) {
         // Over an fp8 cache: decode the pages the prefill reads into the bf16
         // staging pool (timed as preparation), then prefill from it.
@@ -733,12 +771,12 @@ int attn_paged_fwd_noalloc(void *out, const void *q, const void *kv_pool, const 
     pa::AttnArgs a;
     void *const stand_in = reinterpret_cast<void *>(uintptr_t(kWsAlign));
     int rc = make_plan(dims, n_seqs, max_q, o.path_hint, o.pages_per_split, o.window, &plan, o.kv_dtype,
-                       kScratchBalBudget);
+                       kScratchBalBudget, kScratchBytes);
     if (rc != ATTN_OK) return rc;
     if (plan.workspace_bytes > kScratchBytes) return ATTN_ERR_WORKSPACE;
     rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims,
                        stand_in, kScratchBytes, o.path_hint, o.pages_per_split, o.sinks, o.window, plan, a,
-                       o.kv_dtype, o.k_scale, o.v_scale, kScratchBalBudget);
+                       o.kv_dtype, o.k_scale, o.v_scale, kScratchBalBudget, kScratchBytes);
     if (rc != ATTN_OK || n_seqs == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     void *ws = nullptr;
@@ -747,7 +785,7 @@ int attn_paged_fwd_noalloc(void *out, const void *q, const void *kv_pool, const 
         if (rc != ATTN_OK) return rc;
         rc = paged_prepare(out, q, kv_pool, block_table, seq_lens, cu_q, n_seqs, max_q, scale, causal, dims, ws,
                            kScratchBytes, o.path_hint, o.pages_per_split, o.sinks, o.window, plan, a, o.kv_dtype,
-                           o.k_scale, o.v_scale, kScratchBalBudget);
+                           o.k_scale, o.v_scale, kScratchBalBudget, kScratchBytes);
         if (rc != ATTN_OK) return rc;
         // The single-launch merge needs its counters at zero; earlier calls
         // on this GPU may have left partials in those bytes.  A kernel, not a

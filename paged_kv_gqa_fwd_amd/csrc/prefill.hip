@@ -197,10 +197,21 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TP * C::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TP * C::TILE];
 
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
-    // Later query tiles see more keys under a causal mask: launch them first.
-    const int tile = gridDim.x - 1 - blockIdx.x;
+    int g, b, tile;
+    if (a.pf_order) {
+        // Launch order by decreasing work: workgroup i takes the i-th entry
+        // of the order table, a (tile, KV head, sequence) index in grid order.
+        const int item = a.pf_order[blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)];
+        tile = item % (int)gridDim.x;
+        const int hb = item / (int)gridDim.x;
+        g = hb % (int)gridDim.y;
+        b = hb / (int)gridDim.y;
+    } else {
+        g = blockIdx.y;
+        b = blockIdx.z;
+        // Later query tiles see more keys under a causal mask: launch them first.
+        tile = gridDim.x - 1 - blockIdx.x;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -784,6 +795,112 @@ hipError_t launch_fp8_stage_any(int D, const AttnArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(fp8_stage_pages_kernel<128>, dim3(a.mp, a.n_seqs), dim3(kThreads), 0, stream, a);
     else
         hipLaunchKernelGGL(fp8_stage_pages_kernel<256>, dim3(a.mp, a.n_seqs), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---- prefill launch order ----------------------------------------------------
+// One workgroup sorts the prefill grid's (tile, KV head, sequence) items by
+// the pages each streams, most first, and writes the permutation to
+// a.pf_order: a counting sort on the page count (plus one for the start-up,
+// clamped to kOrderBuckets - 1; items with no rows count 0).  Under a causal
+// mask the last tiles of the longest sequences stream the most pages;
+// launched first, they leave the short items to fill the tail of the grid
+// (longest-processing-time-first list scheduling).  Every KV head of a
+// (tile, sequence) pair has the same work, so pairs are sorted and their
+// heads take adjacent places: the hardware deals workgroups to the eight
+// XCDs in turn, so when Hkv divides 8 each XCD then works on fixed KV heads
+// and its L2 holds only their pages (in grid order every XCD sees every
+// head).  Pairs with equal counts land in any order: each item writes only
+// its own output rows, so the order changes no bit of the result.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 2048;
+constexpr int kOrderRegs = 8;       // pairs per thread whose bucket stays in registers
+
+template <int D>
+__device__ __forceinline__ int prefill_pair_bucket(const AttnArgs &a, int tile, int b) {
+    using C = PfCfg<D>;
+    const int L = a.seq_lens[b];
+    const int q0 = a.cu_q[b];
+    const int n = min(a.cu_q[b + 1] - q0, a.max_q);
+    const int R = n * a.group;
+    const int r0 = tile * C::BM;
+    int work = 0;
+    if (r0 < R) {
+        // the pages the kernel streams for this tile: from its first ring
+        // tile (window start of its first row) to the last visible key
+        const int r_last = min(R, r0 + C::BM) - 1;
+        const int kv_end = visible_keys(L, n, r_last / a.group, a.causal);
+        const int first = window_start(L - n + r0 / a.group, a.window) / (kPage * C::TP) * C::TP;
+        work = 1 + max(0, (int)(((int64_t)kv_end + kPage - 1) / kPage) - first);
+    }
+    return kOrderBuckets - 1 - min(work, kOrderBuckets - 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(kOrderThreads) void prefill_order_kernel(const AttnArgs a, int tiles) {
+    constexpr int PER = kOrderBuckets / kOrderThreads;
+    static_assert(kOrderBuckets % kOrderThreads == 0, "buckets per thread");
+    __shared__ int hist[kOrderBuckets];
+    __shared__ int wsum[kOrderThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int hkv = a.hkv;
+    const int pairs = tiles * a.n_seqs;
+    auto bucket = [&](int p) { return prefill_pair_bucket<D>(a, p % tiles, p / tiles); };
+    // hkv places per pair, the pair's heads side by side
+    auto place = [&](int p, int pos) {
+        const int tile = p % tiles;
+        const int base = tile + tiles * hkv * (p / tiles);
+        for (int g = 0; g < hkv; ++g) a.pf_order[pos + g] = base + tiles * g;
+    };
+    for (int i = tid; i < kOrderBuckets; i += kOrderThreads) hist[i] = 0;
+    __syncthreads();
+    int bk[kOrderRegs];
+#pragma unroll
+    for (int k = 0; k < kOrderRegs; ++k) {
+        const int p = tid + k * kOrderThreads;
+        bk[k] = p < pairs ? bucket(p) : -1;
+        if (bk[k] >= 0) atomicAdd(&hist[bk[k]], hkv);
+    }
+    for (int p = tid + kOrderRegs * kOrderThreads; p < pairs; p += kOrderThreads) atomicAdd(&hist[bucket(p)], hkv);
+    __syncthreads();
+    // exclusive scan of the counts (bucket 0 = most pages): thread t owns
+    // buckets [PER t, PER t + PER)
+    int cnt[PER], own = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        cnt[k] = hist[PER * tid + k];
+        own += cnt[k];
+    }
+    int incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int base = incl - own;
+    for (int w = 0; w < wv; ++w) base += wsum[w];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        hist[PER * tid + k] = base;   // each thread rewrites only the buckets it read
+        base += cnt[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kOrderRegs; ++k)
+        if (bk[k] >= 0) place(tid + k * kOrderThreads, atomicAdd(&hist[bk[k]], hkv));
+    for (int p = tid + kOrderRegs * kOrderThreads; p < pairs; p += kOrderThreads)
+        place(p, atomicAdd(&hist[bucket(p)], hkv));
+}
+
+hipError_t launch_prefill_order_any(int D, const AttnArgs &a, dim3 grid, hipStream_t stream) {
+    if (D == 128)
+        hipLaunchKernelGGL(prefill_order_kernel<128>, dim3(1), dim3(kOrderThreads), 0, stream, a, (int)grid.x);
+    else
+        hipLaunchKernelGGL(prefill_order_kernel<256>, dim3(1), dim3(kOrderThreads), 0, stream, a, (int)grid.x);
     return hipGetLastError();
 }
 

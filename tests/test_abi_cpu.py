@@ -165,8 +165,16 @@ def test_plan_paths_and_sizes(pa):
               kv_stride_page=64 * 4 * 2 * 256, kv_stride_slot=4 * 2 * 256, kv_stride_head=512,
               kv_stride_kv=256, max_pages_per_seq=192, bt_stride=192)
     p2 = mod.make_plan(d2, 8, 4096)
-    assert p2.path == mod.PATH_PREFILL and p2.workspace_bytes == 0
+    assert p2.path == mod.PATH_PREFILL
     assert p2.grid_x == -(-4096 * 6 // 128) and p2.grid_y == 4 and p2.grid_z == 8
+    # ... except the launch-order table of a ragged batch: one i32 per
+    # workgroup, 256-byte aligned, from 512 workgroups and two sequences up
+    assert p2.workspace_bytes == -(-p2.grid_x * 4 * 8 * 4 // 256) * 256
+    assert mod.make_plan(d2, 1, 4096).workspace_bytes == 0          # one sequence: grid order
+    p5 = mod.make_plan(d2, 2, 63 * 128 // 6)                       # 63 tiles x 4 x 2 = 504 ...
+    assert p5.grid_x == 63 and p5.workspace_bytes == 0
+    p5 = mod.make_plan(d2, 2, 63 * 128 // 6 + 1)                   # ... 64 tiles: 512 workgroups
+    assert p5.grid_x == 64 and p5.workspace_bytes == 2048
     # forced split sizes are clamped to [1, MP]
     p3 = mod.make_plan(d, 64, 1, mod.PATH_SPLIT_DECODE, 1000)
     assert p3.pages_per_split == 128 and p3.max_splits == 1 and p3.workspace_bytes == 0
@@ -348,13 +356,16 @@ def test_fp8_cache_options_validate(pa):
     assert mp(f8(), max_q=16) == OK                         # 64 packed rows: the short-sequence body
     # more rows take the prefill kernel, which reads the pages through a bf16
     # staging pool in the workspace: 64 seqs x 128 pages x 64 slots x 8 heads
-    # x 2 x D 128 bf16, plus one i32 table entry per page
+    # x 2 x D 128 bf16, plus one i32 table entry per page, then the launch
+    # order of the 1 x 8 x 64 workgroups
     for kw in (dict(path=2), dict()):
         assert mp(f8(**kw), max_q=17) == OK and plan.path == mod.PATH_PREFILL
         pages = 64 * 128
-        assert plan.workspace_bytes == pages * 64 * 8 * 2 * 128 * 2 + pages * 4
+        assert plan.workspace_bytes == pages * 64 * 8 * 2 * 128 * 2 + pages * 4 + 512 * 4
     bf = mod.attn_paged_options(None, 0, 2, 0, 0, 1.0, 1.0)
-    assert mp(bf) == OK and plan.workspace_bytes == 0       # a bf16 prefill needs no workspace
+    assert mp(bf) == OK and plan.workspace_bytes == 512 * 4  # a bf16 prefill: only the launch order
+    assert mp(bf, dd=dims(max_pages_per_seq=128, bt_stride=128, num_kv_heads=4)) == OK
+    assert plan.workspace_bytes == 0                        # 256 workgroups: grid order, no workspace
     assert mp(f8(), dd=dims(max_pages_per_seq=128, bt_stride=128, kv_stride_kv=136)) == E_STRIDE
     assert fo(f8(ks=float("inf"))) == E_SHAPE
     assert fo(f8(vs=float("nan"))) == E_SHAPE
