@@ -191,6 +191,24 @@ __device__ __forceinline__ void pf_load_v(uint16_t *lds_v, const uint16_t *vbase
     }
 }
 
+// At D = 256 (one wave per SIMD) O is accumulated in accumulation
+// registers, which leaves the vector registers room to hold every K read
+// address for the whole loop (below).  The library builds its MFMAs in
+// vector-register form, so this P.V MFMA is written as asm, and the
+// compiler's hazard tracking does not see it: vector code that reads or
+// writes O first passes pf_o_fence (its P and V operands are written well
+// before, and LDS returns are waited for as for any asm operand).
+__device__ __forceinline__ void pf_mfma_pv_agpr(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 20 wait states (an 8-pass MFMA's result may be read by vector
+// instructions 11 after it) between the last asm MFMA into O and vector
+// reads or writes of O, and between those and the next MFMA.
+__device__ __forceinline__ void pf_o_fence(f32x16 (&o)[8]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+}
+
 template <int D>
 __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(const AttnArgs a) {
     using C = PfCfg<D>;
@@ -405,6 +423,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[rb][i] = f32x16{};
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) pf_o_fence(oacc[rb]);
+    }
     const float sl2 = a.scale_log2_pos;   // > 0
     const float inv_sl2 = 1.f / sl2;
     // m_ref: the row's reference max (log2 units), m_use the value P is taken
@@ -454,6 +476,28 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     auto kstage = [&](int j) {
         return sk[((unsigned)(j - j0) / C::SPT) % C::NK] + (32 * ((unsigned)j % C::SPT)) * D + klane;
     };
+    // D = 256: the LDS byte address of every K chunk this lane reads, in ring
+    // slot 0 at the first step of a tile, held in registers for the whole
+    // loop (an empty asm hides their origin, so the compiler cannot re-derive
+    // them inside it); a read adds its slot and step as the instruction's
+    // offset.  cp: the step's position in the loop unrolled by NK tiles (j0
+    // is a multiple of SPT), a compile-time constant.
+    constexpr uint32_t SLOT_B = C::TP * C::TILE * 2;
+    uint32_t kaddr[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        kaddr[ks] = lds_address(sk[0]) + 2u * (klane + ((2 * ks + hi) ^ kswz) * 8);
+        if constexpr (D == 256) asm volatile("" : "+v"(kaddr[ks]));
+    }
+    auto kread_at = [&](int j, int cp, int ks) -> bf16x8 {
+        if constexpr (D == 256) {
+            const uint32_t imm = (uint32_t)((cp / C::SPT) % C::NK) * SLOT_B + 64u * (uint32_t)(cp % C::SPT) * D;
+            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
+                (uintptr_t)(kaddr[ks] + imm));
+        } else {
+            return kread(kstage(j), ks);
+        }
+    };
     auto vstage = [&](int j) {
         return sv[((unsigned)(j - j0) / C::SPT) % C::NV] + (32 * ((unsigned)j % C::SPT)) * D + vlane;
     };
@@ -461,13 +505,12 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     // S^T = K Q^T for the 32 keys of step j (raw scores, f32); no overlap
     // (pipeline prologue).  s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4
     // for this lane's row of block rb.
-    auto qk = [&](int j, f32x16 (&s)[C::RB]) {
-        const uint16_t *kp = kstage(j);
+    auto qk = [&](int j, int cp, f32x16 (&s)[C::RB]) {
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) s[rb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const bf16x8 kop = kread(kp, ks);
+            const bf16x8 kop = kread_at(j, cp, ks);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
                 s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rb][ks], s[rb], 0, 0, 0);
@@ -483,8 +526,11 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             const bf16x8 vop = vread(vt, k);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
-                oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    vop, p[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+                if constexpr (D == 256)
+                    pf_mfma_pv_agpr(oacc[rb][k % (D / 32)], vop, p[rb][k / (D / 32)]);
+                else
+                    oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vop, p[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
         }
     };
 
@@ -495,7 +541,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) pb[rb][0] = pb[rb][1] = bf16x8{};
     // One pipelined step: scur holds S_j on entry; snext receives S_{j+1}.
-    auto step = [&](int j, f32x16 (&scur)[C::RB], f32x16 (&snext)[C::RB]) {
+    auto step = [&](int j, int cp, f32x16 (&scur)[C::RB], f32x16 (&snext)[C::RB]) {
         // ---- mask (diagonal, tail and window-edge steps only)
         if (32 * j + 32 > w_full || 32 * j < w_lo) {
 #pragma unroll
@@ -525,12 +571,15 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 if (k + PF < NPV)
                     vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
                 else
-                    kcar[k + PF - NPV] = kread(kstage(j + 1), k + PF - NPV);   // B(j)'s first operands
+                    kcar[k + PF - NPV] = kread_at(j + 1, cp + 1, k + PF - NPV);   // B(j)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
-                    oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        vop[k % (PF + 1)], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
+                    if constexpr (D == 256)
+                        pf_mfma_pv_agpr(oacc[rb][k % (D / 32)], vop[k % (PF + 1)], pb[rb][k / (D / 32)]);
+                    else
+                        oacc[rb][k % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            vop[k % (PF + 1)], pb[rb][k / (D / 32)], oacc[rb][k % (D / 32)], 0, 0, 0);
                     spread_load(j, k);
                     constexpr int EH = EA / C::RB;
 #pragma unroll
@@ -564,15 +613,16 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
                 thr[rb] = (m_new + kRescaleThreshold) * inv_sl2;
                 l_part[rb] *= alpha;
+                if constexpr (D == 256) pf_o_fence(oacc[rb]);
 #pragma unroll
                 for (int i = 0; i < D / 32; ++i) oacc[rb][i] *= alpha;
+                if constexpr (D == 256) pf_o_fence(oacc[rb]);
             }
         }
         // ---- B(j): S_{j+1} = K_{j+1} Q^T on the MFMA pipe, two K operands
         // ahead, with P_j = exp2(S_j scale - m) on the VALU.  After the last
         // step the product reads a stale stage (in bounds) and is discarded.
         {
-            const uint16_t *kp = kstage(j + 1);
             bf16x8 kop[PF + 1];
 #pragma unroll
             for (int k = 0; k < PF; ++k) kop[k] = kcar[k];
@@ -584,7 +634,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int ks = 0; ks < NKS; ++ks) {
                 if (ks == NKS / 2) issue_v_part(2 * (1 - (j & 1)) + 1);   // B(2t+1): part 1, B(2t+2): part 3
                 if (ks + PF < NKS)
-                    kop[(ks + PF) % (PF + 1)] = kread(kp, ks + PF);
+                    kop[(ks + PF) % (PF + 1)] = kread_at(j + 1, cp + 1, ks + PF);
                 else if (!C::SPLITV || (j & 1))
                     vcar[ks + PF - NKS] = vread(vstage(j), ks + PF - NKS);   // A(j+1)'s first operands
                 // one MFMA, then its share of the VALU work
@@ -686,7 +736,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         if (t0 == ntiles - 1) zero_tile_tail(t0);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        qk(j0, sA);
+        qk(j0, 0, sA);
         if constexpr (C::SPREAD) {
             // step j0 issues V loads before the first refill is set up: into
             // the free V slot tile t0+2 will take, from tile t0's first page;
@@ -706,8 +756,8 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
 #pragma unroll
             for (int c = 0; c < C::NK * C::SPT; c += 2) {
                 const int j = j0 + C::NK * C::SPT * u + c;
-                if (c == 0 || j < nsteps) step(j, sA, sB);
-                if (j + 1 < nsteps) step(j + 1, sB, sA);
+                if (c == 0 || j < nsteps) step(j, c, sA, sB);
+                if (j + 1 < nsteps) step(j + 1, c + 1, sB, sA);
             }
         }
         pv(nsteps - 1, pb);
@@ -716,6 +766,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
 
     // Epilogue: out = O / l, rounded to bf16.  oacc[rb][db][i] holds
     // d = 32db + 8(i/4) + 4hi + i%4 of this lane's row in block rb.
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) pf_o_fence(oacc[rb]);
+    }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
         float l_row = sum_xor32(l_part[rb]);
