@@ -10,7 +10,8 @@ batch output equals, bit for bit, the same sequences called one at a time
 bar (max-abs 2e-2, rel-RMS 5e-3) on every row of the short sequences and a
 seeded quarter of the long ones.  Cases cover both head dims, causal,
 unmasked and windowed masks (Mojo SM100MHA2Q docs, MaskType), an empty
-query run, poisoned tails, and an fp8 cache read through the staging pool.
+query run, an odd number of KV heads (the heads of a pair then straddle the
+XCD deal), poisoned tails, and an fp8 cache read through the staging pool.
 """
 import numpy as np
 import pytest
@@ -29,6 +30,8 @@ CASES = [
     (128, 4, 8, [2048, 300, 5], [3000, 300, 4000], True, 0),                 # 32 tiles x 8 x 3
     (128, 2, 8, [3000, 1400, 128], [3000, 2000, 128], False, 300),           # 24 tiles x 8 x 3
     (256, 3, 8, [1400, 90], [5000, 120], True, 700),                         # 33 tiles x 8 x 2
+    (256, 2, 3, [1400, 30, 500, 1, 0, 900, 64, 200],
+     [2000, 30, 600, 1000, 100, 900, 4000, 250], True, 0),                   # 22 tiles x 3 x 8 (Hkv odd)
 ]
 
 
@@ -98,14 +101,17 @@ def test_ordered_batch_equals_single_calls(oracle_mod, i, fp8):
     compare(out, ref, rows=np.nonzero(mask)[0], what="%s fp8=%s window=%d" % (case.name, fp8, window))
 
 
-def test_order_table_is_a_permutation_most_pages_first():
+@pytest.mark.parametrize("ci", [0, 4])
+def test_order_table_is_a_permutation_most_pages_first(ci):
     """The order table in the caller's workspace (its first bytes on a bf16
     cache): a permutation of the grid's items whose streamed pages
     (1 + ceil(last visible key / 64) for an item with rows, 0 without; no
-    window) never increase along the launch order."""
+    window) never increase along the launch order, with the KV heads of each
+    (tile, sequence) pair in adjacent places."""
     import paged_kv_gqa_fwd_amd as pa
-    d, G, hkv, q_lens, kv_lens, causal, window = CASES[0]
-    case = workloads.make_case("pforder-table", 2350, q_lens, kv_lens, G * hkv, hkv, d, causal=causal,
+    d, G, hkv, q_lens, kv_lens, causal, window = CASES[ci]
+    assert window == 0
+    case = workloads.make_case("pforder-table%d" % ci, 2350 + ci, q_lens, kv_lens, G * hkv, hkv, d, causal=causal,
                                table_cols=max(kv_lens) // 64 + 2)
     plan = pa.make_plan(pa.make_dims(case.q, case.kv, case.block_table), case.n_seqs, case.max_q, PATH_PREFILL)
     items = plan.grid_x * plan.grid_y * plan.grid_z
@@ -134,3 +140,8 @@ def test_order_table_is_a_permutation_most_pages_first():
     work = np.array([pages(int(i)) for i in order])
     assert (np.diff(work) <= 0).all(), "launch order is not most pages first"
     assert work[-1] == 0 and work[0] > 1     # items without rows last
+    # heads side by side: places hkv k .. hkv k + hkv - 1 hold one (tile, sequence) pair, heads 0 .. hkv-1
+    pairs = order.reshape(-1, hkv)
+    tile, rest = pairs % plan.grid_x, pairs // plan.grid_x
+    assert (tile == tile[:, :1]).all() and (rest // hkv == rest[:, :1] // hkv).all()
+    assert (rest % hkv == np.arange(hkv)[None, :]).all()
