@@ -87,9 +87,11 @@ typedef struct attn_paged_dims {
 typedef struct attn_paged_plan {
     int32_t path;              /* ATTN_PATH_SPLIT_DECODE or ATTN_PATH_PREFILL */
     int32_t pages_per_split;   /* KV pages one workgroup streams (split path); balanced
-                                  path: the least pages of one range */
+                                  path: the least pages of one range; split-key
+                                  prefill: the pages of one key run */
     int32_t max_splits;        /* ceil(MP / pages_per_split); balanced path: the most
-                                  pieces one sequence can be cut into */
+                                  pieces one sequence can be cut into; prefill: key
+                                  runs per item (1 = one pass) */
     int32_t grid_x, grid_y, grid_z;
     int32_t block_threads;
     size_t workspace_bytes;    /* bytes of workspace the call needs (0 if none) */
@@ -103,7 +105,12 @@ enum {
                                    blocks of 16 (more than 16 rows: the short-sequence body of
                                    the Mojo SM100MHA2Q docs' struct summary, short query runs
                                    routed to a cheaper body than the prefill tile) */
-    ATTN_PATH_PREFILL = 2,      /* q-tile kernel with causal tile skipping, one pass */
+    ATTN_PATH_PREFILL = 2,      /* q-tile kernel with causal tile skipping; a grid of at
+                                   most 128 (tile, KV head, sequence) items has each
+                                   item's keys split into runs of the split-decode
+                                   layout (page runs from row 0's window start),
+                                   merged by the combine kernel, so that about one
+                                   workgroup per CU runs */
     ATTN_PATH_SPLIT_FUSED = 3,  /* split-KV kernel whose last split per (sequence, KV head)
                                    merges the partials: one launch (decode.json's single
                                    launch with an i32 counter scratch, ops.decode.impl).
@@ -127,9 +134,10 @@ enum {
 /*
  * attn_paged_make_plan -- choose path, split size and grid for a call with
  * these sizes.  path_hint: ATTN_PATH_AUTO or a forced path; pages_per_split:
- * 0 = automatic, otherwise forced (split paths only; with ATTN_PATH_AUTO a
- * forced value selects ATTN_PATH_SPLIT_DECODE, and on the balanced path it
- * is the least range size).  Pure host logic: it
+ * 0 = automatic, otherwise forced (with ATTN_PATH_AUTO a forced value
+ * selects ATTN_PATH_SPLIT_DECODE; on the balanced path it is the least range
+ * size; with ATTN_PATH_PREFILL it splits every item's keys into runs of that
+ * many pages, and a value of at least max_pages_per_seq keeps one pass).  Pure host logic: it
  * reads no device memory and may be called without a GPU.
  * Split-KV partial outputs and (max, sum) statistics per split follow the
  * decode.json manifest's scratch buffers partial / stats (ops.decode.impl
@@ -173,8 +181,9 @@ int attn_paged_workspace_bytes(const attn_paged_dims *dims, int32_t n_seqs, int3
  *                int32 per workgroup, written by the call before the
  *                prefill kernel reads it: the grid's items sorted by the KV
  *                pages each streams, most first, so that a ragged batch's
- *                longest items do not start last), after the fp8 staging
- *                pool and table over an fp8 cache.  Those
+ *                longest items do not start last), or, for a split-key
+ *                prefill, the split partials, after the fp8 staging pool
+ *                and table over an fp8 cache.  Those
  *                counter bytes must be zero when the call starts; every call
  *                that runs to completion leaves them zero again.  A buffer
  *                from a zeroing allocator, or one cleared once with
@@ -239,8 +248,8 @@ typedef struct attn_paged_options {
  * the pages it reads (exactly: every e4m3 value is a bf16 value) into a
  * bf16 staging pool in the workspace, so its plan's workspace_bytes is
  * n_seqs * max_pages_per_seq * (P * Hkv * 2 * D * 2 + 4) bytes, plus the
- * launch order's 4 bytes per workgroup where the grid takes one (each part
- * 256-byte aligned).  Scales must be finite.
+ * launch order's 4 bytes per workgroup where the grid takes one or a split-key
+ * prefill's partials (each part 256-byte aligned).  Scales must be finite.
  */
 enum { ATTN_KV_BF16 = 0, ATTN_KV_FP8_E4M3 = 1 };
 
@@ -271,8 +280,10 @@ int attn_paged_fwd_opt(void *out, const void *q, const void *kv_pool, const int3
  * The plan is the automatic one except that the balanced split path budgets
  * its partials to half the array, so results can differ from
  * attn_paged_fwd_opt's by accumulation order (within the same tolerance),
- * and that a prefill launch order that would not fit beside the fp8 staging
- * pool in the array is left out (grid order; same bits).
+ * that a prefill launch order that would not fit beside the fp8 staging
+ * pool in the array is left out (grid order; same bits), and that a small
+ * prefill grid whose split partials would not fit keeps one pass (within
+ * the same tolerance).
  * A plan whose partials still exceed the array returns ATTN_ERR_WORKSPACE
  * before anything is launched.  Merge counters are cleared by a kernel
  * before each call that needs them (no memset node).  Every call on one GPU

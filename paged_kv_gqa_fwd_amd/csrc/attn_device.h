@@ -123,6 +123,10 @@ struct AttnArgs {
     // is the (tile, KV head, sequence) index, in grid order, that workgroup i
     // computes; a permutation of the grid written by prefill_order_kernel.
     int32_t *pf_order;
+    // Split-key prefill (> 1: small grids): splits per (sequence, KV head),
+    // the page ranges and partial layout of the split-decode path
+    // (pages_per_split, max_splits, part_o, part_ml); merged by the combine.
+    int32_t pf_splits;
 };
 
 struct CombineArgs {

@@ -99,18 +99,32 @@ size_t bal_lead_bytes(int32_t n_seqs) { return align_up((size_t)std::max<int32_t
 // the sort's launch costs more than a ragged tail); only if it fits ws_cap.
 constexpr int64_t kPfOrderMinItems = 512;
 constexpr int64_t kPfOrderMaxItems = int64_t(1) << 22;
+// Split-key prefill: a grid of at most half as many items as CUs has its
+// keys split into floor(kPfSplitTarget / items) runs, one round of
+// workgroups (measured on MI355X: a 128-item grid over 8k-16k keys 18-32%
+// faster with two splits, slower with three or four; a 16-item one 2.7x
+// faster over 8k keys).
+constexpr int64_t kPfSplitMaxItems = 128;
+constexpr int64_t kPfSplitTarget = 256;
 struct PrefillWs {
-    size_t stage_pool = 0, stage_table = 0, order = 0;
-    size_t total() const { return stage_pool + stage_table + order; }
+    size_t stage_pool = 0, stage_table = 0, order = 0, part_o = 0, part_ml = 0;
+    size_t total() const { return stage_pool + stage_table + order + part_o + part_ml; }
 };
-PrefillWs prefill_ws(const attn_paged_dims *d, int32_t n_seqs, int64_t ss, bool f8, int64_t items, size_t ws_cap) {
+// splits > 1: the split partials [rows * splits * D f32 | rows * splits * 2 f32]
+// (rows = n_seqs * max_q * Hq) take the order table's place.
+PrefillWs prefill_ws(const attn_paged_dims *d, int32_t n_seqs, int64_t mq, int64_t ss, bool f8, int64_t items,
+                     int64_t splits, size_t ws_cap) {
     PrefillWs w;
     if (f8) {
         const size_t pages = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)d->max_pages_per_seq;
         w.stage_pool = align_up(pages * (size_t)pa::kPage * (size_t)ss * 2, kWsAlign);
         w.stage_table = align_up(pages * 4, kWsAlign);
     }
-    if (n_seqs >= 2 && items >= kPfOrderMinItems && items <= kPfOrderMaxItems) {
+    if (splits > 1) {
+        const size_t rows = (size_t)std::max<int32_t>(n_seqs, 1) * (size_t)mq * (size_t)d->num_q_heads * (size_t)splits;
+        w.part_o = align_up(rows * (size_t)d->head_dim * 4, kWsAlign);
+        w.part_ml = align_up(rows * 8, kWsAlign);
+    } else if (n_seqs >= 2 && items >= kPfOrderMinItems && items <= kPfOrderMaxItems) {
         const size_t ob = align_up((size_t)items * 4, kWsAlign);
         if (w.total() + ob <= ws_cap) w.order = ob;
     }
@@ -217,15 +231,39 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
         const int64_t bm = pa::prefill_rows(d->head_dim);
         const int64_t tiles = (mq * G + bm - 1) / bm;
         if (tiles > INT32_MAX) return ATTN_ERR_SHAPE;
+        const int64_t items = tiles * d->num_kv_heads * n_seqs;
+        // Split-key prefill: forced by pages_per_split on the prefill path,
+        // else for grids too small to fill the GPU.  Splits follow the
+        // split-decode layout: runs of pps pages from row 0's window start,
+        // at most the pages a row can see (the window's reach, else MP).
+        int64_t MPw = MP;
+        if (window > 0) MPw = std::min<int64_t>(MP, (window + mq + 62) / pa::kPage + 1);
+        int64_t pp = MPw, S = 1;
+        if (path_hint == ATTN_PATH_PREFILL && pps > 0) {
+            pp = std::min<int64_t>(pps, MPw);
+        } else if (items > 0 && items <= kPfSplitMaxItems && MPw >= 2) {
+            const int64_t tp = d->head_dim == 128 ? 2 : 1;   // pages per ring tile
+            const int64_t want = std::min<int64_t>(kPfSplitTarget / items, MPw);
+            pp = ((MPw + want - 1) / want + tp - 1) / tp * tp;
+        }
+        S = (MPw + pp - 1) / pp;
+        if (S > 1 && tiles * S > INT32_MAX) return ATTN_ERR_SHAPE;
+        PrefillWs w = prefill_ws(d, n_seqs, mq, ss, f8, items, S, ws_cap);
+        if (S > 1 && w.total() > ws_cap) {
+            S = 1;   // the partials do not fit the caller's bound: one pass
+            pp = MPw;
+            w = prefill_ws(d, n_seqs, mq, ss, f8, items, S, ws_cap);
+        }
         plan->block_threads = pa::prefill_threads(d->head_dim);
-        plan->pages_per_split = (int32_t)MP;
-        plan->max_splits = 1;
-        plan->grid_x = (int32_t)tiles;
+        plan->pages_per_split = (int32_t)(S > 1 ? pp : MP);
+        plan->max_splits = (int32_t)S;
+        plan->grid_x = (int32_t)(tiles * S);
         plan->grid_y = d->num_kv_heads;
         plan->grid_z = n_seqs;
         // [staging pool: n_seqs * MP pages of P * Hkv * 2 * D bf16 | staging
-        // table: n_seqs * MP i32] over an fp8 cache, then the launch order
-        plan->workspace_bytes = prefill_ws(d, n_seqs, ss, f8, tiles * d->num_kv_heads * n_seqs, ws_cap).total();
+        // table: n_seqs * MP i32] over an fp8 cache, then the launch order or
+        // the split partials
+        plan->workspace_bytes = w.total();
     }
     return ATTN_OK;
 }
@@ -324,14 +362,20 @@ int paged_prepare(void *out, const void *q, const void *kv_pool, const int32_t *
     if (plan.path == ATTN_PATH_PREFILL) {
         // [staging pool | staging table] over an fp8 cache, then the launch order
         const int64_t ss = (int64_t)dims->num_kv_heads * 2 * D;
-        const PrefillWs w = prefill_ws(dims, n_seqs, ss, a.kv_fp8 != 0,
-                                       (int64_t)plan.grid_x * plan.grid_y * plan.grid_z, ws_cap);
+        const int64_t S = plan.max_splits;
+        const PrefillWs w = prefill_ws(dims, n_seqs, std::max<int32_t>(max_q, 1), ss, a.kv_fp8 != 0,
+                                       (int64_t)plan.grid_x / S * plan.grid_y * plan.grid_z, S, ws_cap);
         char *ws = static_cast<char *>(workspace);
         if (w.stage_pool > 0) {
             a.stage_kv = reinterpret_cast<uint16_t *>(ws);
             a.stage_bt = reinterpret_cast<int32_t *>(ws + w.stage_pool);
         }
         if (w.order > 0) a.pf_order = reinterpret_cast<int32_t *>(ws + w.stage_pool + w.stage_table);
+        a.pf_splits = (int32_t)S;
+        if (S > 1) {
+            a.part_o = reinterpret_cast<float *>(ws + w.stage_pool + w.stage_table);
+            a.part_ml = reinterpret_cast<float *>(ws + w.stage_pool + w.stage_table + w.part_o);
+        }
     } else if (plan.workspace_bytes > 0) {
         // [merge counters or pieces per sequence | partial O | partial (m, l)],
         // each 256-byte aligned
@@ -398,7 +442,8 @@ int paged_launch(const attn_paged_plan &plan, const pa::AttnArgs &a, int D, hipS
     }
     if (e != hipSuccess) return ATTN_ERR_HIP;
     if (timing && record_event(&t_main.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
-    const bool need_combine = (plan.path == ATTN_PATH_SPLIT_DECODE && plan.max_splits > 1) ||
+    const bool need_combine = ((plan.path == ATTN_PATH_SPLIT_DECODE || plan.path == ATTN_PATH_PREFILL) &&
+                               plan.max_splits > 1) ||
                               plan.path == ATTN_PATH_SPLIT_BALANCED;
     if (need_combine) {
         pa::CombineArgs c{};

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     __shared__ __attribute__((aligned(1024))) uint16_t sk[C::NK][C::TP * C::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sv[C::NV][C::TP * C::TILE];
 
-    int g, b, tile;
+    int g, b, tile, split = 0;
     if (a.pf_order) {
         // Launch order by decreasing work: workgroup i takes the i-th entry
         // of the order table, a (tile, KV head, sequence) index in grid order.
@@ -227,8 +227,11 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     } else {
         g = blockIdx.y;
         b = blockIdx.z;
-        // Later query tiles see more keys under a causal mask: launch them first.
-        tile = gridDim.x - 1 - blockIdx.x;
+        // Later query tiles see more keys under a causal mask: launch them
+        // first.  Split-key launch: x = split * tiles + (reversed) tile.
+        const int tiles = (int)gridDim.x / (a.pf_splits > 1 ? a.pf_splits : 1);
+        split = (int)blockIdx.x / tiles;
+        tile = tiles - 1 - ((int)blockIdx.x - split * tiles);
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -243,6 +246,19 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     const int R = n * G;
     const int r0 = tile * C::BM;
     if (r0 >= R) return;
+    // Split-key launch (pf_splits > 1, small grids): this workgroup takes
+    // the sequence's pages [ps, pe) of the split-decode layout (pages_per_split
+    // pages from row 0's window start) and writes (O, m, l) partials that the
+    // combine kernel merges.  A split past the last page writes nothing (the
+    // combine never reads it); split 0 always runs, so that a row with no key
+    // still gets its zero output.
+    int ps = 0, pe = INT_MAX / kPage;
+    if (a.pf_splits > 1) {
+        const int np = (L + kPage - 1) / kPage;
+        ps = split_first_page(L, n, a.window) + split * a.pages_per_split;
+        if (split > 0 && ps >= np) return;
+        pe = min(np, ps + a.pages_per_split);
+    }
 
     // This lane's rows: one per 32-row block.  Row keys are [lo, vis).
     int vis[C::RB], lo[C::RB];
@@ -254,18 +270,20 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         row_ok[rb] = r < R;
         qi_[rb] = r / G;
         h_[rb] = g * G + (r - qi_[rb] * G);
-        vis[rb] = row_ok[rb] ? visible_keys(L, n, qi_[rb], a.causal) : 0;
-        lo[rb] = row_ok[rb] ? window_start(L - n + qi_[rb], a.window) : 0;
+        vis[rb] = row_ok[rb] ? min(visible_keys(L, n, qi_[rb], a.causal), kPage * pe) : 0;
+        lo[rb] = row_ok[rb] ? max(window_start(L - n + qi_[rb], a.window), kPage * ps) : 0;
     }
     const int r_last = min(R, r0 + C::BM) - 1;
-    const int kv_end = visible_keys(L, n, r_last / G, a.causal);   // max over the workgroup's rows
+    // max over the workgroup's rows (and the split's last key)
+    const int kv_end = min(visible_keys(L, n, r_last / G, a.causal), kPage * pe);
     // keys below this wave's first row's frontier are visible to all its rows
-    const int w_full = visible_keys(L, n, min(R - 1, r0 + 32 * C::RB * w) / G, a.causal);
-    // keys at or above the window start of this wave's last row are inside
-    // every row's window; pages below the workgroup's first row's window
-    // start are never loaded (0 and page 0 without a window)
-    const int w_lo = window_start(L - n + min(R - 1, r0 + 32 * C::RB * (w + 1) - 1) / G, a.window);
-    const int t0 = window_start(L - n + r0 / G, a.window) / (kPage * C::TP);
+    const int w_full = min(visible_keys(L, n, min(R - 1, r0 + 32 * C::RB * w) / G, a.causal), kPage * pe);
+    // keys at or above the window start of this wave's last row (and the
+    // split's first key) are inside every row's window; pages below the
+    // workgroup's first row's window start are never loaded (0 and page 0
+    // without a window)
+    const int w_lo = max(window_start(L - n + min(R - 1, r0 + 32 * C::RB * (w + 1) - 1) / G, a.window), kPage * ps);
+    const int t0 = max(window_start(L - n + r0 / G, a.window) / kPage, ps) / C::TP;
     const int j0 = C::SPT * t0;                // first 32-key step
     const int nsteps = (kv_end + 31) / 32;     // 32-key softmax steps
     const int ntiles = (nsteps + C::SPT - 1) / C::SPT;   // ring tiles of TP pages
@@ -769,6 +787,30 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     if constexpr (D == 256) {
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) pf_o_fence(oacc[rb]);
+    }
+    if (a.pf_splits > 1) {
+        // split partials: O (f32, v_scale applied) and l against the
+        // reference m (log2 units; -inf for a row that saw no key), the
+        // split-decode kernels' layout; the sink joins in the combine
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) {
+            const float l_row = sum_xor32(l_part[rb]);
+            if (!row_ok[rb]) continue;
+            const int64_t prow = (((int64_t)b * a.max_q + qi_[rb]) * a.hq + h_[rb]) * a.max_splits + split;
+            float *po = a.part_o + prow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    *reinterpret_cast<f32x4 *>(po + 32 * db + 8 * c4 + 4 * hi) =
+                        f32x4{oacc[rb][db][4 * c4 + 0] * a.v_scale, oacc[rb][db][4 * c4 + 1] * a.v_scale,
+                              oacc[rb][db][4 * c4 + 2] * a.v_scale, oacc[rb][db][4 * c4 + 3] * a.v_scale};
+            if (hi == 0) {
+                a.part_ml[prow * 2] = m_ref[rb];
+                a.part_ml[prow * 2 + 1] = l_row;
+            }
+        }
+        return;
     }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {

@@ -505,3 +505,37 @@ def test_noalloc_validates_before_any_hip_call(pa):
     opt = mod.attn_paged_options(None, 0, mod.PATH_SPLIT_DECODE, 1, 0, 1.0, 1.0)
     assert mod.make_plan(big, 1024, 1, mod.PATH_SPLIT_DECODE, 1).workspace_bytes > mod.NOALLOC_SCRATCH_BYTES
     assert noalloc(big, n_seqs=1024, opt=opt) == E_WS
+
+
+def test_prefill_split_plan(pa):
+    """Split-key prefill plans (host logic): a grid of at most 128 items has
+    its keys split into floor(256 / items) runs of the split-decode layout,
+    page runs rounded to a ring tile (two pages at head_dim 128), with the
+    partials in the workspace; a forced pages_per_split on the prefill path
+    splits any grid; a window bounds the pages a split layout covers."""
+    import paged_kv_gqa_fwd_amd as mod
+    # 2 seqs x 32 tokens, 24 / 4 heads, D 256: 2 tiles x 4 x 2 = 16 items, MP 11
+    d = dims(num_q_heads=24, num_kv_heads=4, head_dim=256, q_stride_token=24 * 256, q_stride_head=256,
+             o_stride_token=24 * 256, o_stride_head=256, num_tokens=64, kv_stride_page=64 * 4 * 2 * 256,
+             kv_stride_slot=4 * 2 * 256, kv_stride_head=512, kv_stride_kv=256, max_pages_per_seq=11, bt_stride=11)
+    p = mod.make_plan(d, 2, 32)
+    assert p.path == mod.PATH_PREFILL and p.max_splits == 11 and p.pages_per_split == 1
+    assert (p.grid_x, p.grid_y, p.grid_z) == (2 * 11, 4, 2)
+    rows = 2 * 32 * 24 * 11
+    assert p.workspace_bytes == -(-rows * 256 * 4 // 256) * 256 + -(-rows * 8 // 256) * 256
+    # forced: 3 pages per split -> ceil(11 / 3) = 4 splits; one split past every page -> one pass
+    p3 = mod.make_plan(d, 2, 32, mod.PATH_PREFILL, 3)
+    assert (p3.max_splits, p3.pages_per_split, p3.grid_x) == (4, 3, 8)
+    p1 = mod.make_plan(d, 2, 32, mod.PATH_PREFILL, 1 << 30)
+    assert (p1.max_splits, p1.grid_x, p1.workspace_bytes) == (1, 2, 0)
+    # a window of 64 keys: rows reach (64 + 32 + 62) // 64 + 1 = 3 pages -> 3 splits of one page
+    pw = mod.make_plan(d, 2, 32, mod.PATH_AUTO, 0, 64)
+    assert pw.max_splits == 3 and pw.pages_per_split == 1
+    # head_dim 128 (tiles of 2 pages): 16 seqs x 17 tokens x G 4 = 68 rows = 1 tile x 8 heads x 16 seqs
+    # = 128 items, MP 31: 2 splits of 16 pages (15.5 rounded up to a tile)
+    d2 = dims(max_pages_per_seq=31, bt_stride=31, num_tokens=16 * 17)
+    p2 = mod.make_plan(d2, 16, 17)
+    assert p2.path == mod.PATH_PREFILL and p2.max_splits == 2 and p2.pages_per_split == 16 and p2.grid_x == 2
+    # 129 items and more: one pass
+    p4 = mod.make_plan(dims(max_pages_per_seq=31, bt_stride=31, num_tokens=17 * 17), 17, 17)
+    assert p4.path == mod.PATH_PREFILL and p4.max_splits == 1 and p4.grid_x == 1

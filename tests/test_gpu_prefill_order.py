@@ -6,7 +6,7 @@ items by the pages each one streams, and the prefill workgroups then take
 their items in that order, most pages first.  Every item writes only its
 own output rows, so the order changes no bit of the result: each case's
 batch output equals, bit for bit, the same sequences called one at a time
-(one sequence keeps the grid order), and matches the fp64 oracle to the bf16
+(one sequence keeps the grid order; its keys in one pass), and matches the fp64 oracle to the bf16
 bar (max-abs 2e-2, rel-RMS 5e-3) on every row of the short sequences and a
 seeded quarter of the long ones.  Cases cover both head dims, causal,
 unmasked and windowed masks (Mojo SM100MHA2Q docs, MaskType), an empty
@@ -48,11 +48,14 @@ def _gpu_ready():
     pa.load_library()
 
 
-def _call(case, window, kw):
+def _call(case, window, kw, one_pass=False):
     import paged_kv_gqa_fwd_amd as pa
     g = case.to("cuda")
+    # one_pass: a split size past every page keeps a small grid's keys in one
+    # pass (no split-key partials), the arithmetic of the batch's workgroups
     out = pa.paged_attention(g.q, g.kv, g.block_table, g.seq_lens, g.cu_q, max(case.max_q, 1), case.scale,
-                             case.causal, path=PATH_PREFILL, window=window, **kw)
+                             case.causal, path=PATH_PREFILL, window=window,
+                             pages_per_split=(1 << 30) if one_pass else 0, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -82,7 +85,7 @@ def test_ordered_batch_equals_single_calls(oracle_mod, i, fp8):
         if cu[b + 1] == cu[b]:
             continue
         sub, rows = sub_case_rows(case, [b])
-        one = _call(sub, window, kw)
+        one = _call(sub, window, kw, one_pass=True)
         got = out[cu[b]:cu[b + 1]]
         assert torch.equal(got.view(torch.int16), one[:len(rows)].view(torch.int16)), \
             "%s: sequence %d differs from its own call" % (case.name, b)

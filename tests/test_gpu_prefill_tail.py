@@ -10,7 +10,9 @@ cases put the last key at page edges and inside pages, make the number of
 visible pages odd and even, and poison the slots past L and the unused
 pages with NaN / inf, on the bf16 pool and through the fp8 staging pool,
 causal, unmasked and windowed (Mojo SM100MHA2Q docs, MaskType; kern-kernels
-examples/decode.json, buffers.kv: pages of 64 slots).
+examples/decode.json, buffers.kv: pages of 64 slots).  The grids are small,
+so each case runs both with its keys split (the automatic plan: every split's
+last page is a last tile) and in one pass.
 
 Tolerance: the bf16 bar (max-abs 2e-2, rel-RMS 5e-3 over every written row).
 """
@@ -55,7 +57,8 @@ def _case(i, d, G, hkv, q_lens, kv_lens, causal):
 
 @pytest.mark.parametrize("i", range(len(CASES)))
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_prefill_last_tile(oracle_mod, i, fp8):
+@pytest.mark.parametrize("one_pass", [False, True], ids=["auto", "one_pass"])
+def test_prefill_last_tile(oracle_mod, i, fp8, one_pass):
     import paged_kv_gqa_fwd_amd as pa
     d, G, hkv, q_lens, kv_lens, causal, window = CASES[i]
     case = _case(i, d, G, hkv, q_lens, kv_lens, causal)
@@ -66,9 +69,11 @@ def test_prefill_last_tile(oracle_mod, i, fp8):
     ref = oracle_mod.paged_attn(case.q, case.kv, case.block_table, case.seq_lens, case.cu_q, case.scale, causal,
                                 window=window, **kw)
     g = case.to("cuda")
-    log("  gpu prefill call: %s fp8=%s window=%d" % (case.name, fp8, window))
+    # these grids are small, so the automatic plan splits their keys; a
+    # split size past every page keeps them in one pass
+    log("  gpu prefill call: %s fp8=%s window=%d one_pass=%s" % (case.name, fp8, window, one_pass))
     out = pa.paged_attention(g.q, g.kv, g.block_table, g.seq_lens, g.cu_q, max(case.max_q, 1), case.scale, causal,
-                             path=PATH_PREFILL, window=window, **kw)
+                             path=PATH_PREFILL, window=window, pages_per_split=(1 << 30) if one_pass else 0, **kw)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    compare(out, ref, what="%s fp8=%s window=%d" % (case.name, fp8, window))
+    compare(out, ref, what="%s fp8=%s window=%d one_pass=%s" % (case.name, fp8, window, one_pass))

@@ -98,19 +98,19 @@ def test_noalloc_single_launch_merge_counters_start_at_zero(oracle_mod):
 
 
 def test_noalloc_prefill(oracle_mod):
-    """Prefill-shaped calls need no partials; a ragged batch of 512 or more
-    workgroups keeps its launch-order table in the scratch (over the
-    partials an earlier call left there), a small one needs none.  Same plan
-    on both entry points: bitwise equal."""
+    """Prefill-shaped calls in the scratch (over the partials an earlier call
+    left there): a ragged batch of 512 or more workgroups keeps its
+    launch-order table there, a grid of at most 128 items its split-key
+    partials.  Same plan on both entry points: bitwise equal."""
     import paged_kv_gqa_fwd_amd as pa
     fill = workloads.decode_batch(device="cuda", n_seqs=32, seed=620)
     _noalloc(fill, torch.empty_like(fill.q))
     big = workloads.chunked_prefill(device="cuda", n_seqs=4, q_lo=900, q_hi=1500, ctx_hi=1500, seed=619)
     small = workloads.chunked_prefill(device="cuda", n_seqs=2, q_lo=100, q_hi=300, ctx_hi=500, seed=617)
-    for case, ordered in ((big, True), (small, False)):
+    for case, split in ((big, False), (small, True)):
         plan = pa.make_plan(pa.make_dims(case.q, case.kv, case.block_table), case.n_seqs, case.max_q)
-        assert (plan.workspace_bytes > 0) == ordered
-        _check(case, bitwise=True, oracle_mod=oracle_mod if not ordered else None)
+        assert plan.workspace_bytes > 0 and (plan.max_splits > 1) == split
+        _check(case, bitwise=True, oracle_mod=oracle_mod if split else None)
 
 
 def test_noalloc_rejects_plans_past_the_scratch():
