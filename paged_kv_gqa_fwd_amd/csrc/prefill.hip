@@ -485,7 +485,10 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     };
     auto vread = [&](const uint16_t *vt, int k) {
         const int jj = k / (D / 32), db = k % (D / 32);
-        const uint16_t *v1 = vt + (16 * jj) * D + ((4 * db + vcol_chunk) ^ vswz) * 8;
+        // the swizzle only moves chunks within each group of 16 (bits 2-3 of
+        // the chunk index), so column blocks db and db + 4 share a lane's
+        // address up to a constant 16 chunks: one address per block pair
+        const uint16_t *v1 = vt + (16 * jj) * D + ((4 * (db & 3) + vcol_chunk) ^ vswz) * 8 + (db >> 2) * 128;
         const bf16x4 lo4 = lds_read_tr16(v1);
         const bf16x4 hi4 = lds_read_tr16(v1 + 8 * D);
         return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
