@@ -480,9 +480,6 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     static_assert(EB % C::RB == 0 && EA % C::RB == 0, "even split per MFMA");
     constexpr int PF = PA_PREFILL_PREFETCH;   // LDS operand reads in flight ahead of their MFMA
 
-    auto kread = [&](const uint16_t *kp, int ks) {
-        return *reinterpret_cast<const bf16x8 *>(kp + ((2 * ks + hi) ^ kswz) * 8);
-    };
     auto vread = [&](const uint16_t *vt, int k) {
         const int jj = k / (D / 32), db = k % (D / 32);
         // the swizzle only moves chunks within each group of 16 (bits 2-3 of
@@ -493,31 +490,24 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         const bf16x4 hi4 = lds_read_tr16(v1 + 8 * D);
         return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    // (steps are never negative: unsigned division by the power-of-two SPT is a shift)
-    auto kstage = [&](int j) {
-        return sk[((unsigned)(j - j0) / C::SPT) % C::NK] + (32 * ((unsigned)j % C::SPT)) * D + klane;
-    };
-    // D = 256: the LDS byte address of every K chunk this lane reads, in ring
-    // slot 0 at the first step of a tile, held in registers for the whole
-    // loop (an empty asm hides their origin, so the compiler cannot re-derive
-    // them inside it); a read adds its slot and step as the instruction's
-    // offset.  cp: the step's position in the loop unrolled by NK tiles (j0
-    // is a multiple of SPT), a compile-time constant.
+    // The LDS byte address of every K chunk this lane reads, in ring slot 0
+    // at the first step of a tile, held in registers for the whole loop (an
+    // empty asm hides their origin, so the compiler cannot re-derive them
+    // inside it); a read adds its slot and step as the instruction's offset.
+    // cp: the step's position in the loop unrolled by NK tiles (j0 is a
+    // multiple of SPT), a compile-time constant.  (At D = 128, where the
+    // compiler kept no such registers, a change elsewhere in the kernel once
+    // moved it to re-adding addresses in the loop: DiT -2.4%.)
     constexpr uint32_t SLOT_B = C::TP * C::TILE * 2;
     uint32_t kaddr[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         kaddr[ks] = lds_address(sk[0]) + 2u * (klane + ((2 * ks + hi) ^ kswz) * 8);
-        if constexpr (D == 256) asm volatile("" : "+v"(kaddr[ks]));
+        asm volatile("" : "+v"(kaddr[ks]));
     }
-    auto kread_at = [&](int j, int cp, int ks) -> bf16x8 {
-        if constexpr (D == 256) {
-            const uint32_t imm = (uint32_t)((cp / C::SPT) % C::NK) * SLOT_B + 64u * (uint32_t)(cp % C::SPT) * D;
-            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(
-                (uintptr_t)(kaddr[ks] + imm));
-        } else {
-            return kread(kstage(j), ks);
-        }
+    auto kread_at = [&](int cp, int ks) -> bf16x8 {
+        const uint32_t imm = (uint32_t)((cp / C::SPT) % C::NK) * SLOT_B + 64u * (uint32_t)(cp % C::SPT) * D;
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>((uintptr_t)(kaddr[ks] + imm));
     };
     auto vstage = [&](int j) {
         return sv[((unsigned)(j - j0) / C::SPT) % C::NV] + (32 * ((unsigned)j % C::SPT)) * D + vlane;
@@ -526,12 +516,12 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
     // S^T = K Q^T for the 32 keys of step j (raw scores, f32); no overlap
     // (pipeline prologue).  s[rb][i] = score of key 32j + 8(i/4) + 4hi + i%4
     // for this lane's row of block rb.
-    auto qk = [&](int j, int cp, f32x16 (&s)[C::RB]) {
+    auto qk = [&](int cp, f32x16 (&s)[C::RB]) {
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) s[rb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const bf16x8 kop = kread_at(j, cp, ks);
+            const bf16x8 kop = kread_at(cp, ks);
 #pragma unroll
             for (int rb = 0; rb < C::RB; ++rb)
                 s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[rb][ks], s[rb], 0, 0, 0);
@@ -592,7 +582,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
                 if (k + PF < NPV)
                     vop[(k + PF) % (PF + 1)] = vread(vt, k + PF);
                 else
-                    kcar[k + PF - NPV] = kread_at(j + 1, cp + 1, k + PF - NPV);   // B(j)'s first operands
+                    kcar[k + PF - NPV] = kread_at(cp + 1, k + PF - NPV);   // B(j)'s first operands
                 // one MFMA, then its share of the VALU work
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
@@ -655,7 +645,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
             for (int ks = 0; ks < NKS; ++ks) {
                 if (ks == NKS / 2) issue_v_part(2 * (1 - (j & 1)) + 1);   // B(2t+1): part 1, B(2t+2): part 3
                 if (ks + PF < NKS)
-                    kop[(ks + PF) % (PF + 1)] = kread_at(j + 1, cp + 1, ks + PF);
+                    kop[(ks + PF) % (PF + 1)] = kread_at(cp + 1, ks + PF);
                 else if (!C::SPLITV || (j & 1))
                     vcar[ks + PF - NKS] = vread(vstage(j), ks + PF - NKS);   // A(j+1)'s first operands
                 // one MFMA, then its share of the VALU work
@@ -757,7 +747,7 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         if (t0 == ntiles - 1) zero_tile_tail(t0);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        qk(j0, 0, sA);
+        qk(0, sA);
         if constexpr (C::SPREAD) {
             // step j0 issues V loads before the first refill is set up: into
             // the free V slot tile t0+2 will take, from tile t0's first page;
