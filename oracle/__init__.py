@@ -9,8 +9,10 @@ next to this file is compiled by ``gcc`` on its own.
 (see the header of ``paged_attn_oracle.c`` for the formula and the pages it
 follows); ``kv_write`` is the cache write that precedes it, a plain scatter.  ``quant_prep`` / ``quant_attn`` emulate the int8 Q.K / fp8 P.V
 quantised variant step by step (``quant_oracle.c``); the rounding of the
-softmax weights to fp8 inside the fused loop is "parity unpinned": the page
-names that step but not its arithmetic.
+softmax weights to fp8 inside the fused loop is a reading ("parity
+unpinned" by the page, which names that step but not its arithmetic); the
+oracle's arithmetic for that reading is pinned by the tests against a
+full-row computation and the closed form of the online recurrence.
 """
 from __future__ import annotations
 

@@ -37,8 +37,9 @@
  *  7. P.V: the weight enters the product as e4m3(448 w_j) (its fp8 code,
  *     decoded exactly) times the decoded V code; l sums the unquantised w_j.
  *     (quant_p = 0 skips the rounding of w: used to pin the rest against the
- *     plain attention oracle.)  Parity of this rounding step is unpinned by
- *     the page, which names the fused steps but not their arithmetic.
+ *     plain attention oracle.)  Where this rounding happens is a reading:
+ *     parity unpinned by the page, which names the fused steps but not
+ *     their arithmetic.
  *  8. out = O * s_v / (448 l)  (or O * s_v / l when quant_p = 0), fp64.
  * Causal (square self-attention, n = N): query i sees keys [0, i].
  */

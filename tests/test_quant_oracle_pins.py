@@ -13,11 +13,15 @@ fused_mainloop_phases).  These tests tie it to things other than itself:
 * the whole pipeline, with the fp8 rounding of the weights switched off,
   against the plain attention oracle on inputs every quantiser represents
   exactly;
-* with the weight rounding on, against a full-row numpy computation that uses
-  torch's fp8 conversion, on rows whose maximum sits in the first key tile
-  (so the running maximum never moves);
+* with the weight rounding on, against a full-row numpy computation on rows
+  whose maximum sits in the first key tile (so the running maximum never
+  moves), and against the closed form of the online recurrence on rows whose
+  running maximum moves from tile to tile (weights rounded to e4m3 by a
+  nearest-value search over the decoded code grid);
 * closed forms: a single visible key gives its dequantised V row exactly.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -216,10 +220,95 @@ def test_weight_rounding_matches_full_row_numpy_when_max_is_in_first_tile():
     s = (qi @ ki.T).astype(np.float64) * sq[:, None] * sk[None, :] * scale
     assert np.all(np.argmax(s, axis=1) < 64)
     w = np.exp(s - s.max(axis=1, keepdims=True))
-    wq = torch.from_numpy(448.0 * w).to(torch.float8_e4m3fn).double().numpy()
+    wq = _e4m3_nearest(448.0 * w)
     vdec = torch.from_numpy(p["vq"][0, 0]).view(torch.float8_e4m3fn).double().numpy()  # [D, N]
     ref = (wq @ vdec.T) * p["sv"][0, 0].astype(np.float64)[None, :] / (448.0 * w.sum(axis=1, keepdims=True))
     assert np.abs(got[0, :, 0, :] - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def _e4m3_nearest(x):
+    """Round non-negative doubles to the nearest e4m3 value (ties to the even
+    code), by search over the grid of every positive code as torch decodes it.
+    Direct from the double: torch's own conversion of a double goes through
+    float first, and that double rounding can move a value that lies just off
+    a tie onto it."""
+    codes = np.arange(0, 0x7F)
+    grid = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    x = np.minimum(np.asarray(x, dtype=np.float64), 448.0)
+    hi = np.clip(np.searchsorted(grid, x, side="left"), 1, len(grid) - 1)
+    lo = hi - 1
+    dl, dh = x - grid[lo], grid[hi] - x
+    pick = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(codes[lo] % 2 == 0, lo, hi)))
+    return grid[pick]
+
+
+def _moving_max_closed_form(p, scale, causal, b=0, h=0, tile=64, final_max_only=False):
+    """The online recurrence of the fused loop written in closed form.
+
+    Keys are taken in ascending 64-key tiles.  With m_t the running maximum
+    after tile t (the cumulative maximum of the per-tile maxima over the
+    row's visible keys) and m_T its final value, the recurrence (rescale O
+    and l by exp(m_old - m_new), add e4m3(448 exp(s - m_t)) V and
+    exp(s - m_t)) sums to
+        O = sum_t exp(m_t - m_T) sum_{j in t} dec(e4m3(448 exp(s_j - m_t))) V_j
+        l = sum_j exp(s_j - m_T),   out = O s_v / (448 l).
+    No rescaling happens here, so a wrong rescale factor, an l that sums the
+    rounded weights or a non-cumulative maximum in the oracle shows.
+    final_max_only rounds every weight against m_T instead (the schedule
+    without an online maximum), to show that the pin sees the difference."""
+    # the C library's exp (as the oracle uses), elementwise: numpy's own
+    # vectorised exp differs from it in the last bit for a few percent of
+    # arguments, which can move a weight across an e4m3 rounding boundary
+    cexp = np.frompyfunc(math.exp, 1, 1)
+    N = p["qi"].shape[1]
+    qi = p["qi"][b, :, h, :].astype(np.int64)
+    ki = p["ki"][b, :, h, :].astype(np.int64)
+    sq = np.repeat(p["sq"][b, h].astype(np.float64), 64)[:N]
+    sk = np.repeat(p["sk"][b, h].astype(np.float64), 64)[:N]
+    s = (qi @ ki.T).astype(np.float64) * sq[:, None] * sk[None, :] * scale
+    vdec = torch.from_numpy(p["vq"][b, h]).view(torch.float8_e4m3fn).double().numpy()[:, :N]  # [D, N]
+    out = np.zeros((N, vdec.shape[0]))
+    moves = np.zeros(N, dtype=np.int64)
+    for i in range(N):
+        vis = i + 1 if causal else N
+        row = s[i, :vis]
+        ntile = (vis + tile - 1) // tile
+        tmax = np.array([row[t * tile:(t + 1) * tile].max() for t in range(ntile)])
+        m = np.maximum.accumulate(tmax)
+        moves[i] = len(np.unique(m)) - 1
+        mT = m[-1]
+        o = np.zeros(vdec.shape[0])
+        for t in range(ntile):
+            mt = mT if final_max_only else m[t]
+            w = cexp(row[t * tile:(t + 1) * tile] - mt).astype(np.float64)
+            wq = _e4m3_nearest(448.0 * w)
+            o += math.exp(mt - mT) * (vdec[:, t * tile:t * tile + len(w)] @ wq)
+        l = cexp(row - mT).astype(np.float64).sum()
+        out[i] = o * p["sv"][b, h].astype(np.float64) / (448.0 * l)
+    return out, moves
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_weight_rounding_with_moving_max_matches_closed_form(causal):
+    N, H, D = 300, 2, 128                  # five key tiles, the last one ragged (44 keys)
+    g = torch.Generator().manual_seed(21)
+    q = (torch.randn(1, N, H, D, generator=g).abs() + 0.5).to(torch.bfloat16)
+    k = torch.randn(1, N, H, D, generator=g)
+    for t in range(5):                     # one key per tile scores higher the later its tile
+        k[0, 64 * t + 7] += 0.5 * (t + 1)
+    k = k.to(torch.bfloat16)
+    v = _rand_bf16((1, N, H, D), 22)
+    p = oracle.quant_prep(q, k, v)
+    scale = 0.05
+    got = oracle.quant_attn(p, scale, causal=causal, quant_p=True)
+    for h in range(H):
+        ref, moves = _moving_max_closed_form(p, scale, causal, h=h)
+        assert (moves >= 2).mean() > 0.5     # the running maximum moves on most rows
+        assert np.abs(got[0, :, h, :] - ref).max() <= 1e-12 * np.abs(ref).max()
+        # rounding every weight against the final maximum is a different
+        # result, far outside the comparison above
+        alt, _ = _moving_max_closed_form(p, scale, causal, h=h, final_max_only=True)
+        assert np.abs(alt - ref).max() > 1e-6 * np.abs(ref).max()
 
 
 def test_single_visible_key_gives_dequantised_v_row():
