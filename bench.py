@@ -714,7 +714,8 @@ def main():
         # stream over as many bytes as one step moves, right after the
         # primary line (the same state of the chip)
         ceiling = stream_read_ceiling(prim["bytes"])
-        ceiling["kernel_frac"] = round(s["main_kernel_GBps"] / ceiling["GBps"], 4)
+        if "main_kernel_GBps" in s:   # split-decode lines (the tiny call runs the prefill kernel)
+            ceiling["kernel_frac"] = round(s["main_kernel_GBps"] / ceiling["GBps"], 4)
         ceiling["step_frac"] = round(s["value"] / ceiling["GBps"], 4)
         log("[bench] read ceiling %s" % json.dumps(ceiling))
     cpu = None
