@@ -18,15 +18,18 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     const int i = blockIdx.y;
     const int b = blockIdx.z;
     if (h >= a.hq) return;
+    // The row's metadata loads are independent of each other: issued together.
     const int q0 = a.cu_q[b];
-    int n = a.cu_q[b + 1] - q0;
+    const int q1 = a.cu_q[b + 1];
+    const int pieces = a.seg_splits ? a.seg_splits[b] : 0;
+    int n = q1 - q0;
     if (n > a.max_q) n = a.max_q;
     if (i >= n) return;
     int ns;
     if (a.seg_splits) {
         // balanced split path: a sequence in one piece was written directly;
         // one with no page (L = 0) is written as zeros below
-        ns = a.seg_splits[b];
+        ns = pieces;
         if (ns == 1) return;
     } else {
         const int L = a.seq_lens[b];
@@ -36,8 +39,15 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     const int64_t t = q0 + i;
     const int64_t base = (((int64_t)b * a.max_q + i) * a.hq + h) * a.max_splits;
 
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, a.part_ml[(base + s) * 2]);
+    // Lane s keeps split s's (m, l) for the first 64 splits, so the merge
+    // below takes them from a register instead of a second global round trip.
+    float m_l = -INFINITY, l_l = 0.f;
+    if (lane < ns) {
+        m_l = a.part_ml[(base + lane) * 2];
+        l_l = a.part_ml[(base + lane) * 2 + 1];
+    }
+    float M = m_l;
+    for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, a.part_ml[(base + s) * 2]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     // the row's sink logit (log2 units) joins the normaliser, with no value row
@@ -49,10 +59,37 @@ __global__ __launch_bounds__(kThreads) void paged_combine_kernel(const CombineAr
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float lsum = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ms = a.part_ml[(base + s) * 2];
-            const float ls = a.part_ml[(base + s) * 2 + 1];
-            const float wgt = exp2_fast(ms - M);   // ms = -inf gives 0
+        // Splits in order, each with the same arithmetic as before (the
+        // single-launch merge uses it too, so both forms stay bitwise
+        // equal); four splits' O loads are issued before their products.
+        const int ns64 = ns < 64 ? ns : 64;
+        int s = 0;
+        for (; s + 4 <= ns64; s += 4) {
+            float po4[4][PER];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < PER; ++e) po4[u][e] = a.part_o[(base + s + u) * D + lane + 64 * e];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float ms = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_l), s + u));
+                const float ls = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_l), s + u));
+                const float wgt = exp2_fast(ms - M);   // ms = -inf gives 0
+                lsum += wgt * ls;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += wgt * po4[u][e];
+            }
+        }
+        for (; s < ns; ++s) {
+            float ms, ls;
+            if (s < 64) {
+                ms = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_l), s));
+                ls = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_l), s));
+            } else {
+                ms = a.part_ml[(base + s) * 2];
+                ls = a.part_ml[(base + s) * 2 + 1];
+            }
+            const float wgt = exp2_fast(ms - M);
             lsum += wgt * ls;
             const float *po = a.part_o + (base + s) * D;
 #pragma unroll
