@@ -817,16 +817,28 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         // v_scale: V = v_scale * e4m3(code) over an fp8 cache (1 for bf16)
         const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
         uint16_t *op = a.out + (int64_t)(q0 + qi_[rb]) * a.o_st + (int64_t)h_[rb] * a.o_sh;
+        // Lanes l and l + 32 hold the low and high four values of each
+        // group of eight d.  One permlane32 swap per pair of groups gives
+        // lane l both halves of the even group and lane l + 32 both halves
+        // of the odd one, so every lane stores 16 contiguous bytes (half as
+        // many stores, 32-byte runs per row).
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
+            uint32_t w[4][2];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4) {
-                u32x2 pk;
-                pk[0] = (uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 0] * inv) |
-                        ((uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 1] * inv) << 16);
-                pk[1] = (uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 2] * inv) |
-                        ((uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 3] * inv) << 16);
-                *reinterpret_cast<u32x2 *>(op + 32 * db + 8 * c4 + 4 * hi) = pk;
+                w[c4][0] = (uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 0] * inv) |
+                           ((uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 1] * inv) << 16);
+                w[c4][1] = (uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 2] * inv) |
+                           ((uint32_t)f32_to_bf16_bits(oacc[rb][db][4 * c4 + 3] * inv) << 16);
+            }
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                // upper lanes of the first operand <-> lower lanes of the second
+                const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * cp][0], w[2 * cp + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * cp][1], w[2 * cp + 1][1], false, false);
+                *reinterpret_cast<u32x4 *>(op + 32 * db + 16 * cp + 8 * hi) =
+                    u32x4{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
             }
         }
     }
