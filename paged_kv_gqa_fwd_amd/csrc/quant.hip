@@ -399,18 +399,27 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const float *svp = a.sv + ((int64_t)b * a.h + h) * D;
     uint16_t *op = a.out + (int64_t)b * a.o_sb + (int64_t)row * a.o_st + (int64_t)h * a.o_sh;
+    // lanes l and l + 32 hold the low and high four values of each group of
+    // eight d: one permlane32 swap per pair of groups lets every lane store
+    // 16 contiguous bytes (as in the prefill kernel's epilogue)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
+        uint32_t w[4][2];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int d0 = 32 * db + 8 * c4 + 4 * hi;
             const f32x4 s4 = *reinterpret_cast<const f32x4 *>(svp + d0);
-            u32x2 pk;
-            pk[0] = (uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 0] * s4[0] * inv) |
-                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 1] * s4[1] * inv) << 16);
-            pk[1] = (uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 2] * s4[2] * inv) |
-                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 3] * s4[3] * inv) << 16);
-            *reinterpret_cast<u32x2 *>(op + d0) = pk;
+            w[c4][0] = (uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 0] * s4[0] * inv) |
+                       ((uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 1] * s4[1] * inv) << 16);
+            w[c4][1] = (uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 2] * s4[2] * inv) |
+                       ((uint32_t)f32_to_bf16_bits(oacc[db][4 * c4 + 3] * s4[3] * inv) << 16);
+        }
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(w[2 * cp][0], w[2 * cp + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(w[2 * cp][1], w[2 * cp + 1][1], false, false);
+            *reinterpret_cast<u32x4 *>(op + 32 * db + 16 * cp + 8 * hi) =
+                u32x4{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
         }
     }
 }
