@@ -159,8 +159,8 @@ def _kernel_times(fn, steps):
         fn()
     torch.cuda.synchronize()
     pa.kernel_timing_enable(False)
-    mm, mn, cm, cn, pm, pn = pa.kernel_timing_read()
-    return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0)
+    mm, mn, cm, cn, pm, pn, wm, wn = pa.kernel_timing_read()
+    return mm / max(mn, 1), (cm / cn if cn else 0.0), (pm / pn if pn else 0.0), (wm / wn if wn else 0.0)
 
 
 def _warm(fn, min_steps, min_seconds=0.3):
@@ -223,7 +223,7 @@ def run_workload(name, steps, warmup, pps=0, path=0, window=0, fp8=False, layout
         for _ in range(warmup):
             step()
     step_ms = _time_steps(step, steps)
-    main_ms, comb_ms, _ = _kernel_times(step, steps)
+    main_ms, comb_ms, _, _ = _kernel_times(step, steps)
     dist = _step_distribution(step, steps)
     suffix = ("+window%d" % window if window else "") + ("+fp8" if fp8 else "") + ("+%s" % layout if layout else "") + tag
     res = {
@@ -264,10 +264,10 @@ def run_write(name, steps, warmup):
 
     steps = _secondary_steps(_warm(step, warmup), steps)
     step_ms = _time_steps(step, steps)
-    main_ms, comb_ms, write_ms = _kernel_times(step, steps)
+    main_ms, comb_ms, _, write_ms = _kernel_times(step, steps)
     _warm(two_launch, warmup, 0.1)
     two_ms = _time_steps(two_launch, steps)
-    _, _, write_alone_ms = _kernel_times(two_launch, steps)
+    _, _, _, write_alone_ms = _kernel_times(two_launch, steps)
     written = sum(min(n, L) for n, L in zip(case.q_lens, case.kv_lens))
     wbytes = 2 * written * case.num_kv_heads * 2 * case.head_dim * 2
     abytes = algorithmic_bytes(case)
@@ -309,7 +309,7 @@ def run_quant(steps, warmup, cpu_seconds=0.0):
 
     steps = _secondary_steps(_warm(step, warmup), steps)
     step_ms = _time_steps(step, steps)
-    main_ms, _, prep_ms = _kernel_times(step, steps)
+    main_ms, _, prep_ms, _ = _kernel_times(step, steps)
     dist = _step_distribution(step, steps)
     flops = algorithmic_flops(case)
     tops = flops / (step_ms * 1e-3) / 1e12

@@ -447,16 +447,19 @@ int attn_quant_fwd(void *out, const void *q, const void *k, const void *v,
  * Kernel timing (instrumentation for benchmarks).  While enabled, every
  * launch is bracketed by HIP events recorded on the launch stream; elapsed
  * times are summed per kind: the main attention kernel (split-KV partials,
- * prefill or the quantised loop), the split-KV combine kernel, and the work
- * before the main kernel (the quantised path's preparation kernels, the
- * KV-cache write).  attn_kernel_timing_read
+ * prefill or the quantised loop), the split-KV combine kernel, the other
+ * work before the main kernel (the quantised path's preparation kernels,
+ * the prefill launch-order sort, the fp8 page staging) and the KV-cache
+ * write kernel (none when the write runs inside the split-decode launch).
+ * attn_kernel_timing_read
  * synchronises on the recorded events, returns the totals (milliseconds)
  * and launch counts (any pointer may be NULL), and resets them.  Returns
  * ATTN_ERR_HIP if an event call fails.
  */
 int attn_kernel_timing_enable(int32_t enable);
 int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
-                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches);
+                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches,
+                            double *write_ms, int32_t *write_launches);
 
 /*
  * attn_stream_read -- measurement utility: read `bytes` of device memory at

@@ -157,7 +157,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_kernel_timing_enable.argtypes = [i32]
     lib.attn_kernel_timing_enable.restype = ctypes.c_int
     dp, ip = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)
-    lib.attn_kernel_timing_read.argtypes = [dp, ip, dp, ip, dp, ip]
+    lib.attn_kernel_timing_read.argtypes = [dp, ip, dp, ip, dp, ip, dp, ip]
     lib.attn_kernel_timing_read.restype = ctypes.c_int
     lib.attn_stream_read.argtypes = [p, sz, p, i32, i32, p]
     lib.attn_stream_read.restype = ctypes.c_int
@@ -481,10 +481,10 @@ def kernel_timing_enable(on: bool) -> None:
 
 def kernel_timing_read():
     """(main_ms_total, main_launches, combine_ms_total, combine_launches,
-    prep_ms_total, prep_launches)."""
+    prep_ms_total, prep_launches, write_ms_total, write_launches)."""
     lib = load_library()
     v = [ctypes.c_double(), ctypes.c_int32(), ctypes.c_double(), ctypes.c_int32(),
-         ctypes.c_double(), ctypes.c_int32()]
+         ctypes.c_double(), ctypes.c_int32(), ctypes.c_double(), ctypes.c_int32()]
     rc = lib.attn_kernel_timing_read(*[ctypes.byref(x) for x in v])
     if rc != ATTN_OK:
         raise AttnError(rc)

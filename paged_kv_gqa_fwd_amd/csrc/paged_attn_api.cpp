@@ -269,7 +269,7 @@ int make_plan(const attn_paged_dims *d, int32_t n_seqs, int32_t max_q, int32_t p
 }
 
 // ---- kernel timing instrumentation ---------------------------------------
-enum TimedKind { kTimedMain = 0, kTimedCombine = 1, kTimedPrep = 2 };
+enum TimedKind { kTimedMain = 0, kTimedCombine = 1, kTimedPrep = 2, kTimedWrite = 3 };
 struct TimedLaunch {
     hipEvent_t start, stop;
     int kind;
@@ -554,7 +554,7 @@ int kv_write_launch(const pa::KvWriteArgs &w, hipStream_t st) {
     if (pa::launch_kv_write(w, st) != hipSuccess) return ATTN_ERR_HIP;
     if (timing) {
         if (record_event(&tl.stop, st) != ATTN_OK) return ATTN_ERR_HIP;
-        tl.kind = kTimedPrep;
+        tl.kind = kTimedWrite;
         timing_push(tl);
     }
     return ATTN_OK;
@@ -934,14 +934,15 @@ int attn_kernel_timing_enable(int32_t enable) {
 }
 
 int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *combine_ms,
-                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches) {
+                            int32_t *combine_launches, double *prep_ms, int32_t *prep_launches,
+                            double *write_ms, int32_t *write_launches) {
     std::vector<TimedLaunch> v;
     {
         std::lock_guard<std::mutex> lk(g_timing_mu);
         v.swap(g_timed);
     }
-    double tms[3] = {0, 0, 0};
-    int32_t cnt[3] = {0, 0, 0};
+    double tms[4] = {0, 0, 0, 0};
+    int32_t cnt[4] = {0, 0, 0, 0};
     int rc = ATTN_OK;
     for (auto &t : v) {
         float ms = 0.f;
@@ -959,6 +960,8 @@ int attn_kernel_timing_read(double *main_ms, int32_t *main_launches, double *com
     if (combine_launches) *combine_launches = cnt[kTimedCombine];
     if (prep_ms) *prep_ms = tms[kTimedPrep];
     if (prep_launches) *prep_launches = cnt[kTimedPrep];
+    if (write_ms) *write_ms = tms[kTimedWrite];
+    if (write_launches) *write_launches = cnt[kTimedWrite];
     return rc;
 }
 

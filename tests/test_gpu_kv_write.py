@@ -120,8 +120,8 @@ def _launches(fn):
     res = fn()
     torch.cuda.synchronize()
     pa.kernel_timing_enable(False)
-    _, main_n, _, _, _, prep_n = pa.kernel_timing_read()
-    return res, main_n, prep_n
+    _, main_n, _, _, _, _, _, write_n = pa.kernel_timing_read()
+    return res, main_n, write_n
 
 
 FUSED = [
