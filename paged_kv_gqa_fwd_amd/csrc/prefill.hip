@@ -70,6 +70,9 @@ namespace pa {
 #ifndef PA_PF_Q_AGPR
 #define PA_PF_Q_AGPR 1
 #endif
+#ifndef PA_PF_XCD_CHUNK   // grid-order launches: runs of 32 items per XCD
+#define PA_PF_XCD_CHUNK 1
+#endif
 #ifndef PA_PF_TILE_PAGES128
 #define PA_PF_TILE_PAGES128 2
 #endif
@@ -225,13 +228,32 @@ __global__ __launch_bounds__(PfCfg<D>::THREADS, 1) void paged_prefill_kernel(con
         g = hb % (int)gridDim.y;
         b = hb / (int)gridDim.y;
     } else {
-        g = blockIdx.y;
-        b = blockIdx.z;
+        int x = blockIdx.x, y = blockIdx.y, z = blockIdx.z;
+#if PA_PF_XCD_CHUNK
+        {
+            // Workgroups are dealt to the 8 XCDs in turn by linear id.  In
+            // each full run of 256 ids, XCD c takes grid items 32c .. 32c + 31
+            // (consecutive tiles, mostly of one head), so an XCD's L2 serves
+            // one head's pages at a time.
+            const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+            const int n = gx * gy * (int)gridDim.z;
+            const int lin = x + gx * (y + gy * z);
+            if (lin < n - n % 256) {
+                const int w8 = lin % 256;
+                const int item = lin - w8 + (w8 % 8) * 32 + w8 / 8;
+                x = item % gx;
+                y = (item / gx) % gy;
+                z = item / (gx * gy);
+            }
+        }
+#endif
+        g = y;
+        b = z;
         // Later query tiles see more keys under a causal mask: launch them
         // first.  Split-key launch: x = split * tiles + (reversed) tile.
         const int tiles = (int)gridDim.x / (a.pf_splits > 1 ? a.pf_splits : 1);
-        split = (int)blockIdx.x / tiles;
-        tile = tiles - 1 - ((int)blockIdx.x - split * tiles);
+        split = x / tiles;
+        tile = tiles - 1 - (x - split * tiles);
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
