@@ -210,6 +210,7 @@ __device__ __forceinline__ float load_scalar_f32(const float *p) {
 
 constexpr int kQStages = 3;
 constexpr int kQRows = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int kQXcdRun = 64;  // consecutive grid items per XCD (its resident workgroups)
 
 __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
     constexpr int D = kQuantD;
@@ -217,8 +218,23 @@ __global__ __launch_bounds__(256, 2) void quant_attn_kernel(const QuantArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t sk[kQStages][TB];
     __shared__ __attribute__((aligned(1024))) uint8_t sv[kQStages][TB];
 
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int qt = gridDim.x - 1 - blockIdx.x;   // later query tiles first (longer under causal)
+    int bx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    {
+        // Workgroups are dealt to the 8 XCDs in turn by linear id; in each
+        // full run of 8 QXCD ids, XCD c takes QXCD consecutive grid items
+        // (query tiles of one head), so an XCD's L2 serves one head at a time.
+        const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+        const int n = gx * gy * (int)gridDim.z;
+        const int lin = (int)blockIdx.x + gx * ((int)blockIdx.y + gy * (int)blockIdx.z);
+        if (lin < n - n % (8 * kQXcdRun)) {
+            const int w8 = lin % (8 * kQXcdRun);
+            const int item = lin - w8 + (w8 % 8) * kQXcdRun + w8 / 8;
+            bx = item % gx;
+            h = (item / gx) % gy;
+            b = item / (gx * gy);
+        }
+    }
+    const int qt = gridDim.x - 1 - bx;   // later query tiles first (longer under causal)
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5;
